@@ -1,0 +1,89 @@
+"""QLoRA linear layer oracle (CPU, NumPy, float64). Test infrastructure only.
+
+Sources (the QLoRA pages):
+
+* forward: Y = X W + s X L1 L2 with L1 in R^{h x r}, L2 in R^{r x o}
+  (diycv.top "QLoRA 论文解读", section 问题背景, LoRA equation); with the
+  base weight replaced by doubleDequant(c1, c2, W_NF4) in BF16 (section
+  关键公式, equation for Y^BF16). The scale s is kept as in the LoRA
+  equation (the 关键公式 rendering omits it).
+* backward: gradients flow through the dequantised BF16 base weight to the
+  layer input, and only the adapters get parameter gradients; there is no
+  weight gradient (section 关键公式, text after the dtype table; training
+  steps 4-5; neura.market analysis, "How It Works").
+
+Layout used here and by the library: the base weight is stored as
+Wt[N][K] (out_features x in_features), the transpose of the pages' W; so
+Y = X Wt^T + s (X L1) L2 and dX = dY Wt + s (dY L2^T) L1^T.
+
+Inputs arrive as bf16 bit patterns (uint16) and are widened exactly; every
+product and sum is then taken in float64 with library matmuls, so the result
+is the exact layer up to float64 rounding. No dropout (reading: the pages'
+LoRA dropout is a training-recipe setting, not part of the layer).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .nf4 import bf16_bits_to_f32
+
+_F64 = np.float64
+
+
+def widen(bits_or_array) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64 exactly; float arrays pass through."""
+    a = np.asarray(bits_or_array)
+    if a.dtype == np.uint16:
+        return bf16_bits_to_f32(a).astype(_F64)
+    return a.astype(_F64)
+
+
+def linear_fwd(X, Wt, L1, L2, s: float):
+    """Y = X Wt^T + s (X L1) L2 in float64. Returns (Y, T) with T = X L1."""
+    X, Wt, L1, L2 = widen(X), widen(Wt), widen(L1), widen(L2)
+    T = X @ L1
+    Y = X @ Wt.T + float(s) * (T @ L2)
+    return Y, T
+
+
+def linear_bwd(X, Wt, L1, L2, s: float, dY):
+    """Gradients of the layer for upstream gradient dY, float64.
+
+    dX  = dY Wt + s (dY L2^T) L1^T      (through the frozen base and the adapter)
+    dL1 = s X^T (dY L2^T)
+    dL2 = s (X L1)^T dY
+    There is no gradient for the frozen base weight.
+    """
+    X, Wt, L1, L2, dY = widen(X), widen(Wt), widen(L1), widen(L2), widen(dY)
+    s = float(s)
+    U = dY @ L2.T
+    T = X @ L1
+    dX = dY @ Wt + s * (U @ L1.T)
+    dL1 = s * (X.T @ U)
+    dL2 = s * (T.T @ dY)
+    return dX, dL1, dL2
+
+
+def linear_fwd_rows(X, Wt, L1, L2, s: float, rows):
+    """Selected rows of Y (for sampled checks at full size)."""
+    X = widen(np.asarray(X)[rows])
+    Y, _ = linear_fwd(X, Wt, L1, L2, s)
+    return Y
+
+
+def linear_bwd_dx_rows(Wt, L1, L2, s: float, dY, rows):
+    """Selected rows of dX (row m of dX depends on row m of dY only)."""
+    dY = widen(np.asarray(dY)[rows])
+    Wt, L1, L2 = widen(Wt), widen(L1), widen(L2)
+    return dY @ Wt + float(s) * ((dY @ L2.T) @ L1.T)
+
+
+def rel_err(G, R) -> float:
+    """max |G - R| / RMS(R), G widened to float64; R the oracle result."""
+    G = widen(G)
+    R = np.asarray(R, dtype=_F64)
+    rms = float(np.sqrt(np.mean(R * R)))
+    if rms == 0.0:
+        return float(np.max(np.abs(G - R))) if G.size else 0.0
+    return float(np.max(np.abs(G - R))) / rms
