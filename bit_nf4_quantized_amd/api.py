@@ -1,0 +1,354 @@
+"""Thin ctypes binding of libqlora_nf4.so (argument marshalling only).
+
+Every function here has the name of the C entry point it calls. torch is
+used for device memory, shapes and the current HIP stream; all arithmetic
+happens in the library's HIP kernels. If the library has not been built the
+first call raises (there is no fallback path).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqlora_nf4.so")
+
+QLORA_OK = 0
+QLORA_ERR_ARG = -1
+QLORA_ERR_SHAPE = -2
+QLORA_ERR_ALIGN = -3
+QLORA_ERR_WORKSPACE = -4
+QLORA_ERR_HIP = -5
+QLORA_F32 = 0
+QLORA_BF16 = 1
+QLORA_BLOCK = 64
+QLORA_DQ_BLOCK = 256
+QLORA_MAX_RANK = 256
+
+# every symbol declared in include/qlora_nf4.h
+EXPORTS = (
+    "qlora_status_str", "qlora_last_error", "qlora_nf4_codebook", "qlora_quant_sizes",
+    "qlora_quantize", "qlora_dequantize", "qlora_linear_workspace", "qlora_linear_fwd",
+    "qlora_linear_bwd", "qlora_set_timing",
+)
+QLORA_TIMING_FWD_GEMM = 0
+QLORA_TIMING_DX_GEMM = 1
+QLORA_TIMING_GEMV = 2
+QLORA_TIMING_QUANT = 3
+QLORA_TIMING_DEQUANT = 4
+
+
+class QNF4(ctypes.Structure):
+    """Mirror of the C struct qlora_nf4 (host struct of device pointers)."""
+
+    _fields_ = [
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+        ("codes", ctypes.c_void_p),
+        ("absmax8", ctypes.c_void_p),
+        ("scale2", ctypes.c_void_p),
+        ("mean", ctypes.c_void_p),
+    ]
+
+
+class QLoRAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = _load()
+        msg = lib.qlora_status_str(status).decode()
+        extra = lib.qlora_last_error().decode() if status == QLORA_ERR_HIP else ""
+        super().__init__(f"{where}: {msg}" + (f" ({extra})" if extra else ""))
+        self.status = status
+
+
+_LIB = None
+
+
+def _load():
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python {os.path.join(HERE, 'build.py')}`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    P = ctypes.POINTER
+    lib.qlora_status_str.argtypes = [ctypes.c_int]
+    lib.qlora_status_str.restype = ctypes.c_char_p
+    lib.qlora_last_error.argtypes = []
+    lib.qlora_last_error.restype = ctypes.c_char_p
+    lib.qlora_nf4_codebook.argtypes = [P(ctypes.c_float)]
+    lib.qlora_nf4_codebook.restype = ctypes.c_int
+    lib.qlora_quant_sizes.argtypes = [i64, i64, P(sz), P(sz), P(sz), P(sz)]
+    lib.qlora_quant_sizes.restype = ctypes.c_int
+    lib.qlora_quantize.argtypes = [vp, ctypes.c_int, P(QNF4), vp, sz, vp]
+    lib.qlora_quantize.restype = ctypes.c_int
+    lib.qlora_dequantize.argtypes = [P(QNF4), vp, vp]
+    lib.qlora_dequantize.restype = ctypes.c_int
+    lib.qlora_linear_workspace.argtypes = [i64, i64, i64, ctypes.c_int, P(sz)]
+    lib.qlora_linear_workspace.restype = ctypes.c_int
+    lib.qlora_linear_fwd.argtypes = [P(QNF4), vp, i64, vp, vp, ctypes.c_int, ctypes.c_float, vp, vp, vp, sz, vp]
+    lib.qlora_linear_fwd.restype = ctypes.c_int
+    lib.qlora_linear_bwd.argtypes = [P(QNF4), vp, vp, i64, vp, vp, ctypes.c_int, ctypes.c_float, vp, vp, vp, vp,
+                                     ctypes.c_int, vp, sz, vp]
+    lib.qlora_linear_bwd.restype = ctypes.c_int
+    lib.qlora_set_timing.argtypes = [ctypes.c_int, vp, vp, ctypes.c_int, P(ctypes.c_int)]
+    lib.qlora_set_timing.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes library (raises if it is not built)."""
+    return _load()
+
+
+def _check(status: int, where: str):
+    if status != QLORA_OK:
+        raise QLoRAError(status, where)
+
+
+def _stream(stream=None):
+    import torch
+
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, dtype, shape, name):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ---- host-only queries ------------------------------------------------------------
+
+def qlora_nf4_codebook() -> np.ndarray:
+    out = (ctypes.c_float * 16)()
+    _check(_load().qlora_nf4_codebook(out), "qlora_nf4_codebook")
+    return np.frombuffer(bytes(out), dtype=np.float32).copy()
+
+
+def qlora_quant_sizes(rows: int, cols: int) -> dict:
+    a, b, c, d = (ctypes.c_size_t() for _ in range(4))
+    _check(_load().qlora_quant_sizes(rows, cols, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
+                                     ctypes.byref(d)), "qlora_quant_sizes")
+    return {"codes": a.value, "absmax8": b.value, "scale2": c.value, "workspace": d.value}
+
+
+def qlora_linear_workspace(M: int, K: int, N: int, r: int) -> int:
+    out = ctypes.c_size_t()
+    _check(_load().qlora_linear_workspace(M, K, N, r, ctypes.byref(out)), "qlora_linear_workspace")
+    return out.value
+
+
+class KernelTimer:
+    """Event brackets around every launch of one kernel class (qlora_set_timing).
+
+    Use as a context manager around the calls to measure; ``durations_ms()``
+    then gives the per-launch times from the HIP events on the library's
+    stream. Events are created through torch (plumbing only).
+    """
+
+    def __init__(self, kernel: int, capacity: int = 4096):
+        import torch
+
+        self.kernel = kernel
+        self.events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(capacity)]
+        self._start = (ctypes.c_void_p * capacity)(*[e[0].cuda_event for e in self.events])
+        self._stop = (ctypes.c_void_p * capacity)(*[e[1].cuda_event for e in self.events])
+        self._count = ctypes.c_int(0)
+        self.capacity = capacity
+
+    def __enter__(self):
+        self._count.value = 0
+        _check(_load().qlora_set_timing(self.kernel, self._start, self._stop, self.capacity,
+                                        ctypes.byref(self._count)), "qlora_set_timing")
+        return self
+
+    def __exit__(self, *exc):
+        _load().qlora_set_timing(self.kernel, None, None, 0, None)
+        return False
+
+    @property
+    def count(self) -> int:
+        return self._count.value
+
+    def durations_ms(self) -> list:
+        import torch
+
+        torch.cuda.synchronize()
+        return [self.events[i][0].elapsed_time(self.events[i][1]) for i in range(self.count)]
+
+
+def qlora_status_str(status: int) -> str:
+    return _load().qlora_status_str(status).decode()
+
+
+# ---- quantised tensor ----------------------------------------------------------------
+
+@dataclass
+class NF4Tensor:
+    """A quantised weight [rows][cols]: the device buffers of qlora_nf4."""
+
+    rows: int
+    cols: int
+    codes: "torch.Tensor"     # uint8 [ceil(rows*cols/2)]
+    absmax8: "torch.Tensor"   # uint8 [nb]
+    scale2: "torch.Tensor"    # float32 [ng]
+    mean: "torch.Tensor"      # float32 [1]
+
+    def struct(self) -> QNF4:
+        return QNF4(self.rows, self.cols, self.codes.data_ptr(), self.absmax8.data_ptr(),
+                    self.scale2.data_ptr(), self.mean.data_ptr())
+
+    @staticmethod
+    def empty(rows: int, cols: int, device="cuda") -> "NF4Tensor":
+        import torch
+
+        s = qlora_quant_sizes(rows, cols)
+        return NF4Tensor(rows, cols,
+                         torch.empty(max(s["codes"], 1), dtype=torch.uint8, device=device),
+                         torch.empty(max(s["absmax8"], 1), dtype=torch.uint8, device=device),
+                         torch.empty(max(s["scale2"] // 4, 1), dtype=torch.float32, device=device),
+                         torch.empty(1, dtype=torch.float32, device=device))
+
+
+def _workspace(nbytes: int, device, ws=None):
+    import torch
+
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def qlora_quantize(W, out: NF4Tensor | None = None, workspace=None, stream=None) -> NF4Tensor:
+    """NF4 + DQ quantisation of a [rows][cols] fp32 or bf16 device tensor."""
+    import torch
+
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [rows][cols]")
+    rows, cols = W.shape
+    if W.dtype == torch.float32:
+        dt = QLORA_F32
+    elif W.dtype == torch.bfloat16:
+        dt = QLORA_BF16
+    else:
+        raise TypeError("W must be float32 or bfloat16")
+    _need(W, W.dtype, (rows, cols), "W")
+    q = out if out is not None else NF4Tensor.empty(rows, cols, W.device)
+    sizes = qlora_quant_sizes(rows, cols)
+    ws = _workspace(sizes["workspace"], W.device, workspace)
+    st = q.struct()
+    _check(_load().qlora_quantize(_ptr(W), dt, ctypes.byref(st), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream)), "qlora_quantize")
+    return q
+
+
+def qlora_dequantize(q: NF4Tensor, out=None, stream=None):
+    """doubleDequant to a bf16 [rows][cols] device tensor."""
+    import torch
+
+    y = out if out is not None else torch.empty((q.rows, q.cols), dtype=torch.bfloat16, device=q.codes.device)
+    _need(y, torch.bfloat16, (q.rows, q.cols), "out")
+    st = q.struct()
+    _check(_load().qlora_dequantize(ctypes.byref(st), _ptr(y), _stream(stream)), "qlora_dequantize")
+    return y
+
+
+def qlora_linear_fwd(q: NF4Tensor, X, L1, L2, scale: float, want_T: bool = False, Y=None, T_out=None,
+                     workspace=None, stream=None):
+    """Y = X dequant(Wt)^T + s (X L1) L2; returns (Y, T) with T = bf16(X L1) or None."""
+    import torch
+
+    M, K = X.shape
+    N = q.rows
+    r = L1.shape[1]
+    if K != q.cols:
+        raise ValueError("X columns must equal the weight's in_features")
+    _need(X, torch.bfloat16, (M, K), "X")
+    _need(L1, torch.bfloat16, (K, r), "L1")
+    _need(L2, torch.bfloat16, (r, N), "L2")
+    Y = Y if Y is not None else torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    _need(Y, torch.bfloat16, (M, N), "Y")
+    if want_T and T_out is None:
+        T_out = torch.empty((M, r), dtype=torch.bfloat16, device=X.device)
+    if T_out is not None:
+        _need(T_out, torch.bfloat16, (M, r), "T_out")
+    ws = _workspace(qlora_linear_workspace(M, K, N, r), X.device, workspace)
+    st = q.struct()
+    _check(_load().qlora_linear_fwd(ctypes.byref(st), _ptr(X), M, _ptr(L1), _ptr(L2), r, float(scale), _ptr(Y),
+                                    _ptr(T_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "qlora_linear_fwd")
+    return Y, T_out
+
+
+def qlora_linear_bwd(q: NF4Tensor, X, dY, L1, L2, scale: float, T=None, need_dX: bool = True,
+                     grad_dtype=None, dX=None, dL1=None, dL2=None, workspace=None, stream=None):
+    """Returns (dX or None, dL1, dL2) of the QLoRA linear for upstream gradient dY."""
+    import torch
+
+    grad_dtype = torch.float32 if grad_dtype is None else grad_dtype
+    if grad_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("grad_dtype must be float32 or bfloat16")
+    M, K = X.shape
+    N = q.rows
+    r = L1.shape[1]
+    _need(X, torch.bfloat16, (M, K), "X")
+    _need(dY, torch.bfloat16, (M, N), "dY")
+    _need(L1, torch.bfloat16, (K, r), "L1")
+    _need(L2, torch.bfloat16, (r, N), "L2")
+    if T is not None:
+        _need(T, torch.bfloat16, (M, r), "T")
+    if need_dX:
+        dX = dX if dX is not None else torch.empty((M, K), dtype=torch.bfloat16, device=X.device)
+        _need(dX, torch.bfloat16, (M, K), "dX")
+    else:
+        dX = None
+    dL1 = dL1 if dL1 is not None else torch.empty((K, r), dtype=grad_dtype, device=X.device)
+    dL2 = dL2 if dL2 is not None else torch.empty((r, N), dtype=grad_dtype, device=X.device)
+    _need(dL1, grad_dtype, (K, r), "dL1")
+    _need(dL2, grad_dtype, (r, N), "dL2")
+    ws = _workspace(qlora_linear_workspace(M, K, N, r), X.device, workspace)
+    st = q.struct()
+    gd = QLORA_F32 if grad_dtype == torch.float32 else QLORA_BF16
+    _check(_load().qlora_linear_bwd(ctypes.byref(st), _ptr(X), _ptr(dY), M, _ptr(L1), _ptr(L2), r, float(scale),
+                                    _ptr(T), _ptr(dX), _ptr(dL1), _ptr(dL2), gd, _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream)), "qlora_linear_bwd")
+    return dX, dL1, dL2
+
+
+# ---- helpers for moving numpy data (bf16 as uint16 bits) ------------------------------
+
+def to_device_bf16(bits: np.ndarray, device="cuda"):
+    """uint16 bf16 bit patterns (host) -> bf16 device tensor, same bytes."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
+def to_host_bits(t) -> np.ndarray:
+    """bf16 device tensor -> uint16 bit patterns on the host."""
+    import torch
+
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

@@ -1,0 +1,248 @@
+// C ABI of the QLoRA NF4 library: host-side validation, sizes, the NF4
+// codebook, and stream-ordered kernel launches. See include/qlora_nf4.h.
+#include "qlora_nf4.h"
+
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "launch.h"
+
+using qlora::LinearWorkspace;
+using qlora::NF4Table;
+using qlora::NF4Thresholds;
+using qlora::NF4View;
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int hip_fail(hipError_t e) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+  return QLORA_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// N(0,1) quantile by bisection on the CDF 1/2 erfc(-x / sqrt 2), to full
+// double precision.
+double normal_quantile(double p) {
+  double lo = -40.0, hi = 40.0;
+  for (int i = 0; i < 400; ++i) {
+    const double mid = 0.5 * (lo + hi);
+    if (mid == lo || mid == hi) break;
+    if (0.5 * erfc(-mid / sqrt(2.0)) < p)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+// S_c = { 1/2 [Q(i/(c+2)) + Q((i+1)/(c+2))] : i = 1..c } for odd c (QLoRA
+// pages, diycv.top, section 方法总览 item 2, with c = 15 giving the
+// denominator 2^4 + 1); its middle element is exactly 0.
+void quantile_set(int c, double* out) {
+  const double d = (double)(c + 2);
+  for (int i = 1; i <= c; ++i) out[i - 1] = 0.5 * (normal_quantile(i / d) + normal_quantile((i + 1) / d));
+  out[c / 2] = 0.0;
+}
+
+struct Tables {
+  NF4Table tab;
+  NF4Thresholds th;
+};
+
+// The NF4 codebook: 7 negative members of S_15 over |min S_15|, an exact 0,
+// and 8 positive members of S_17 over max S_17 (one fp32 rounding each),
+// ascending; plus the decision thresholds between neighbouring codes.
+Tables build_tables() {
+  double s15[15], s17[17];
+  quantile_set(15, s15);
+  quantile_set(17, s17);
+  double v[16];
+  int n = 0;
+  for (int i = 0; i < 7; ++i) v[n++] = s15[i] / (-s15[0]);
+  v[n++] = 0.0;
+  for (int i = 9; i < 17; ++i) v[n++] = s17[i] / s17[16];
+  Tables T;
+  for (int i = 0; i < 16; ++i) T.tab.q[i] = (float)v[i];
+  T.tab.q[0] = -1.0f;
+  T.tab.q[15] = 1.0f;
+  for (int j = 0; j < 15; ++j) {
+    // exact midpoint of two fp32 values, then the smallest fp32 strictly above it
+    const double m = 0.5 * ((double)T.tab.q[j] + (double)T.tab.q[j + 1]);
+    float f = (float)m;
+    if (!((double)f > m)) f = nextafterf(f, INFINITY);
+    T.th.t[j] = f;
+  }
+  return T;
+}
+
+const Tables& tables() {
+  static const Tables T = build_tables();  // thread-safe one-time init
+  return T;
+}
+
+bool valid_nf4(const qlora_nf4* q) {
+  return q && q->codes && q->absmax8 && q->scale2 && q->mean;
+}
+
+NF4View view_of(const qlora_nf4* q) {
+  NF4View v;
+  v.codes = q->codes;
+  v.absmax8 = q->absmax8;
+  v.scale2 = q->scale2;
+  v.mean = q->mean;
+  v.rows = q->rows;
+  v.cols = q->cols;
+  return v;
+}
+
+// Shape rules shared by the linear entry points.
+int check_linear(const qlora_nf4* W, int64_t M, int r, float scale) {
+  if (!valid_nf4(W)) return QLORA_ERR_ARG;
+  if (!isfinite(scale)) return QLORA_ERR_ARG;
+  if (r < 8 || r > QLORA_MAX_RANK || (r % 8) != 0) return QLORA_ERR_ARG;
+  if (M < 0 || W->rows <= 0 || W->cols <= 0) return QLORA_ERR_SHAPE;
+  if ((W->cols % QLORA_BLOCK) != 0 || (W->rows % 8) != 0) return QLORA_ERR_SHAPE;
+  if (M > (int64_t)1 << 31 || W->rows > (int64_t)1 << 31 || W->cols > (int64_t)1 << 31) return QLORA_ERR_SHAPE;
+  if (!aligned16(W->codes)) return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qlora_status_str(int status) {
+  switch (status) {
+    case QLORA_OK: return "QLORA_OK";
+    case QLORA_ERR_ARG: return "QLORA_ERR_ARG: invalid argument";
+    case QLORA_ERR_SHAPE: return "QLORA_ERR_SHAPE: unsupported or inconsistent shape";
+    case QLORA_ERR_ALIGN: return "QLORA_ERR_ALIGN: device pointer not 16-byte aligned";
+    case QLORA_ERR_WORKSPACE: return "QLORA_ERR_WORKSPACE: workspace missing or too small";
+    case QLORA_ERR_HIP: return "QLORA_ERR_HIP: HIP runtime or launch failure";
+    default: return "unknown qlora status";
+  }
+}
+
+const char* qlora_last_error(void) { return g_last_error; }
+
+int qlora_nf4_codebook(float* out16) {
+  if (!out16) return QLORA_ERR_ARG;
+  memcpy(out16, tables().tab.q, sizeof(float) * 16);
+  return QLORA_OK;
+}
+
+int qlora_quant_sizes(int64_t rows, int64_t cols, size_t* codes_bytes, size_t* absmax8_bytes,
+                      size_t* scale2_bytes, size_t* workspace_bytes) {
+  if (rows < 0 || cols < 0) return QLORA_ERR_SHAPE;
+  if (cols > 0 && rows > INT64_MAX / 2 / cols) return QLORA_ERR_SHAPE;
+  const int64_t numel = rows * cols;
+  const int64_t nb = (numel + QLORA_BLOCK - 1) / QLORA_BLOCK;
+  const int64_t ng = (nb + QLORA_DQ_BLOCK - 1) / QLORA_DQ_BLOCK;
+  if (codes_bytes) *codes_bytes = (size_t)((numel + 1) / 2);
+  if (absmax8_bytes) *absmax8_bytes = (size_t)nb;
+  if (scale2_bytes) *scale2_bytes = (size_t)ng * sizeof(float);
+  if (workspace_bytes) *workspace_bytes = qlora::quant_workspace_layout(numel).total;
+  return QLORA_OK;
+}
+
+int qlora_quantize(const void* W, qlora_dtype in_dtype, const qlora_nf4* q, void* ws, size_t ws_bytes,
+                   hipStream_t stream) {
+  if (!q) return QLORA_ERR_ARG;
+  if (in_dtype != QLORA_F32 && in_dtype != QLORA_BF16) return QLORA_ERR_ARG;
+  if (q->rows < 0 || q->cols < 0) return QLORA_ERR_SHAPE;
+  if (q->cols > 0 && q->rows > INT64_MAX / 2 / q->cols) return QLORA_ERR_SHAPE;
+  const int64_t numel = q->rows * q->cols;
+  if (numel == 0) return QLORA_OK;
+  if ((numel + QLORA_BLOCK * QLORA_DQ_BLOCK - 1) / (QLORA_BLOCK * QLORA_DQ_BLOCK) > 0x7FFFFFFF)
+    return QLORA_ERR_SHAPE;
+  if (!W || !valid_nf4(q) || !ws) return QLORA_ERR_ARG;
+  if (!aligned16(W) || !aligned16(q->codes) || !aligned16(ws)) return QLORA_ERR_ALIGN;
+  if (ws_bytes < qlora::quant_workspace_layout(numel).total) return QLORA_ERR_WORKSPACE;
+  const hipError_t e = qlora::launch_quantize(W, in_dtype == QLORA_BF16, numel, tables().th, q->codes,
+                                              q->absmax8, q->scale2, q->mean, ws, stream);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
+
+int qlora_dequantize(const qlora_nf4* q, uint16_t* out, hipStream_t stream) {
+  if (!q) return QLORA_ERR_ARG;
+  if (q->rows < 0 || q->cols < 0) return QLORA_ERR_SHAPE;
+  if (q->cols > 0 && q->rows > INT64_MAX / 2 / q->cols) return QLORA_ERR_SHAPE;
+  const int64_t numel = q->rows * q->cols;
+  if (numel == 0) return QLORA_OK;
+  if (!valid_nf4(q) || !out) return QLORA_ERR_ARG;
+  if (!aligned16(q->codes) || !aligned16(out)) return QLORA_ERR_ALIGN;
+  const hipError_t e =
+      qlora::launch_dequantize(q->codes, q->absmax8, q->scale2, q->mean, tables().tab, numel, out, stream);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
+
+int qlora_linear_workspace(int64_t M, int64_t K, int64_t N, int r, size_t* bytes) {
+  if (!bytes) return QLORA_ERR_ARG;
+  if (r < 8 || r > QLORA_MAX_RANK || (r % 8) != 0) return QLORA_ERR_ARG;
+  if (M < 0 || K <= 0 || N <= 0 || (K % QLORA_BLOCK) != 0 || (N % 8) != 0) return QLORA_ERR_SHAPE;
+  if (M > (int64_t)1 << 31 || N > (int64_t)1 << 31 || K > (int64_t)1 << 31) return QLORA_ERR_SHAPE;
+  *bytes = qlora::linear_workspace_layout(M, K, N, r).total;
+  return QLORA_OK;
+}
+
+int qlora_linear_fwd(const qlora_nf4* W, const uint16_t* X, int64_t M, const uint16_t* L1, const uint16_t* L2,
+                     int r, float scale, uint16_t* Y, uint16_t* T_out, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  int st = check_linear(W, M, r, scale);
+  if (st != QLORA_OK) return st;
+  if (!L1 || !L2) return QLORA_ERR_ARG;
+  if (M > 0 && (!X || !Y)) return QLORA_ERR_ARG;
+  if (!ws) return QLORA_ERR_WORKSPACE;
+  if (!aligned16(X) || !aligned16(L1) || !aligned16(L2) || !aligned16(Y) || !aligned16(T_out) || !aligned16(ws))
+    return QLORA_ERR_ALIGN;
+  if (ws_bytes < qlora::linear_workspace_layout(M, W->cols, W->rows, r).total) return QLORA_ERR_WORKSPACE;
+  const hipError_t e = qlora::linear_forward(view_of(W), tables().tab, X, M, L1, L2, r, scale, Y, T_out, ws, stream);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
+
+int qlora_linear_bwd(const qlora_nf4* W, const uint16_t* X, const uint16_t* dY, int64_t M, const uint16_t* L1,
+                     const uint16_t* L2, int r, float scale, const uint16_t* T, uint16_t* dX, void* dL1,
+                     void* dL2, qlora_dtype grad_dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_linear(W, M, r, scale);
+  if (st != QLORA_OK) return st;
+  if (grad_dtype != QLORA_F32 && grad_dtype != QLORA_BF16) return QLORA_ERR_ARG;
+  if (!L1 || !L2 || !dL1 || !dL2) return QLORA_ERR_ARG;
+  if (M > 0 && (!X || !dY)) return QLORA_ERR_ARG;
+  if (!ws) return QLORA_ERR_WORKSPACE;
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(L1) || !aligned16(L2) || !aligned16(T) || !aligned16(dX) ||
+      !aligned16(dL1) || !aligned16(dL2) || !aligned16(ws))
+    return QLORA_ERR_ALIGN;
+  if (ws_bytes < qlora::linear_workspace_layout(M, W->cols, W->rows, r).total) return QLORA_ERR_WORKSPACE;
+  const hipError_t e = qlora::linear_backward(view_of(W), tables().tab, X, dY, M, L1, L2, r, scale, T, dX, dL1,
+                                              dL2, grad_dtype == QLORA_BF16, ws, stream);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
+
+int qlora_set_timing(int kernel, hipEvent_t* start, hipEvent_t* stop, int n, int* count) {
+  if (kernel < 0 || kernel >= QLORA_TIMING_CLASSES || n < 0) return QLORA_ERR_ARG;
+  qlora::TimingSlot& t = qlora::timing_slots()[kernel];
+  if (n == 0 || !start || !stop || !count) {
+    t = qlora::TimingSlot();
+    return QLORA_OK;
+  }
+  t.start = start;
+  t.stop = stop;
+  t.n = n;
+  t.count = count;
+  return QLORA_OK;
+}
+
+}  // extern "C"
+
+namespace qlora {
+TimingSlot* timing_slots() {
+  static thread_local TimingSlot slots[kTimeClasses];
+  return slots;
+}
+}  // namespace qlora

@@ -1,0 +1,104 @@
+// Internal (C++) interface between the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace qlora {
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Optional per-thread event brackets around one kernel class (measurement
+// only; see qlora_set_timing). Classes match the QLORA_TIMING_* constants.
+enum TimingClass { kTimeFwdGemm = 0, kTimeDxGemm = 1, kTimeGemv = 2, kTimeQuant = 3, kTimeDequant = 4,
+                   kTimeClasses = 5 };
+
+struct TimingSlot {
+  hipEvent_t* start = nullptr;
+  hipEvent_t* stop = nullptr;
+  int n = 0;
+  int* count = nullptr;
+};
+
+TimingSlot* timing_slots();  // thread-local array of kTimeClasses slots
+
+// Records start before and stop after `launch()` when the class is being timed.
+template <typename F>
+hipError_t timed(int cls, hipStream_t stream, F&& launch) {
+  TimingSlot& t = timing_slots()[cls];
+  const bool on = t.n > 0 && t.count && *t.count < t.n;
+  if (on) {
+    hipError_t e = hipEventRecord(t.start[*t.count], stream);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch();
+  if (e != hipSuccess) return e;
+  if (on) {
+    e = hipEventRecord(t.stop[*t.count], stream);
+    if (e != hipSuccess) return e;
+    ++*t.count;
+  }
+  return hipSuccess;
+}
+
+// Scratch of qlora_quantize: fp32 block absmax values and two float64 arrays
+// for the per-group tree sums and their fold.
+struct QuantWorkspace {
+  size_t absmax_off, sum_a_off, sum_b_off, total;
+};
+
+inline QuantWorkspace quant_workspace_layout(int64_t numel) {
+  const size_t nb = (size_t)((numel + kBlock - 1) / kBlock);
+  const size_t ng = (nb + kDqBlock - 1) / kDqBlock;
+  QuantWorkspace L;
+  L.absmax_off = 0;
+  L.sum_a_off = align_up(nb * sizeof(float), 256);
+  L.sum_b_off = L.sum_a_off + align_up(ng * sizeof(double), 256);
+  L.total = L.sum_b_off + align_up(ng * sizeof(double), 256);
+  if (L.total == 0) L.total = 256;
+  return L;
+}
+
+hipError_t launch_quantize(const void* w, bool bf16_in, int64_t numel, const NF4Thresholds& th,
+                           uint8_t* codes, uint8_t* absmax8, float* scale2, float* mean, void* ws,
+                           hipStream_t stream);
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* absmax8, const float* scale2,
+                             const float* mean, const NF4Table& tab, int64_t numel, uint16_t* out,
+                             hipStream_t stream);
+
+// Views of a quantised weight for the GEMM kernels.
+struct NF4View {
+  const uint8_t* codes;
+  const uint8_t* absmax8;
+  const float* scale2;
+  const float* mean;
+  int64_t rows, cols;  // stored [rows][cols]
+};
+
+// Workspace of the linear layer (shared by forward and backward).
+struct LinearWorkspace {
+  size_t l2t_off;    // bf16 [N][r]   L2 transposed
+  size_t st_off;     // bf16 [M][r]   s * (X L1)
+  size_t t_off;      // bf16 [M][r]   X L1 (when the caller gives no T)
+  size_t su_off;     // bf16 [M][r]   s * (dY L2^T)
+  size_t part_off;   // fp32 split-K partials
+  size_t part_bytes;
+  size_t total;
+};
+
+LinearWorkspace linear_workspace_layout(int64_t M, int64_t K, int64_t N, int r);
+
+hipError_t linear_forward(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M,
+                          const uint16_t* L1, const uint16_t* L2, int r, float s, uint16_t* Y,
+                          uint16_t* T_out, void* ws, hipStream_t stream);
+
+hipError_t linear_backward(const NF4View& W, const NF4Table& tab, const uint16_t* X, const uint16_t* dY,
+                           int64_t M, const uint16_t* L1, const uint16_t* L2, int r, float s,
+                           const uint16_t* T, uint16_t* dX, void* dL1, void* dL2, bool grad_bf16,
+                           void* ws, hipStream_t stream);
+
+}  // namespace qlora

@@ -1,0 +1,270 @@
+// NF4 blockwise quantisation with double quantisation, and the standalone
+// doubleDequant to bf16, for gfx950.
+//
+// Method (QLoRA pages, diycv.top "QLoRA 论文解读", section 方法总览 items
+// 1-3; neura.market "How It Works"): flatten the weight, cut it into
+// contiguous 64-blocks, scale each block by its absmax into [-1, 1] and store
+// the nearest NF4 code; then quantise the block absmax values, minus their
+// mean, to an 8-bit float in groups of 256 with one fp32 scale per group.
+//
+// Kernels (all HBM-bound; see the launchers at the bottom):
+//   quant_blocks_kernel   one workgroup per DQ group of 256 blocks
+//                         (16384 weights): coalesced loads, absmax by
+//                         cross-lane max over the 8 lanes of a block, codes,
+//                         nibble packing, and the float64 adjacent-pair tree
+//                         sum of the group's 256 absmax values in LDS.
+//   tree_fold_kernel      one workgroup folds the per-group sums with the
+//                         same adjacent-pair rule and writes the fp32 mean.
+//   dq_encode_kernel      one workgroup per group: a - mean, group absmax,
+//                         fp32 scale, E4M3 codes.
+//   dequant_kernel        16 weights per thread: codes + E4M3 constants ->
+//                         bf16, 2 x 16-byte stores.
+#include "common.h"
+#include "launch.h"
+
+namespace qlora {
+
+namespace {
+
+constexpr int kGroupWeights = kBlock * kDqBlock;  // 16384
+constexpr int kQuantThreads = 256;                // 8 lanes per 64-block
+
+template <typename InT>
+__device__ __forceinline__ void load8(const InT* __restrict__ w, int64_t e0, int64_t numel, float v[8]);
+
+template <>
+__device__ __forceinline__ void load8<float>(const float* __restrict__ w, int64_t e0, int64_t numel,
+                                             float v[8]) {
+  if (e0 + 8 <= numel) {
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(w + e0);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(w + e0 + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (e0 + i < numel) ? w[e0 + i] : 0.0f;
+  }
+}
+
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* __restrict__ w, int64_t e0,
+                                                int64_t numel, float v[8]) {
+  if (e0 + 8 <= numel) {
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(w + e0);
+    v[0] = __uint_as_float(a.x << 16); v[1] = __uint_as_float(a.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(a.y << 16); v[3] = __uint_as_float(a.y & 0xFFFF0000u);
+    v[4] = __uint_as_float(a.z << 16); v[5] = __uint_as_float(a.z & 0xFFFF0000u);
+    v[6] = __uint_as_float(a.w << 16); v[7] = __uint_as_float(a.w & 0xFFFF0000u);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (e0 + i < numel) ? bf16_to_f32(w[e0 + i]) : 0.0f;
+  }
+}
+
+// Nearest-code index of a normalised value: number of thresholds <= x.
+__device__ __forceinline__ uint32_t nearest_code(float x, const NF4Thresholds& th) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < 15; ++j) c += (x >= th.t[j]) ? 1u : 0u;
+  return c;
+}
+
+template <typename InT>
+__global__ __launch_bounds__(kQuantThreads) void quant_blocks_kernel(
+    const InT* __restrict__ w, int64_t numel, int64_t nb, NF4Thresholds th,
+    uint8_t* __restrict__ codes, float* __restrict__ absmax, double* __restrict__ gsum) {
+  __shared__ float s_a[kDqBlock];
+  __shared__ double s_t[2][kDqBlock];
+  const int t = threadIdx.x;
+  const int64_t g = blockIdx.x;
+  const int64_t gbase = g * kGroupWeights;
+
+  for (int it = 0; it < kGroupWeights / (kQuantThreads * 8); ++it) {
+    const int local = it * (kQuantThreads * 8) + t * 8;  // element offset in the group
+    const int64_t e0 = gbase + local;
+    float v[8];
+    if (e0 < numel) {
+      load8<InT>(w, e0, numel, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[i]));
+    float a = wave_max(m, 8);                 // max over the 8 lanes of this block
+    const bool zero_block = !(a >= 0x1p-126f);
+    if (zero_block) a = 0.0f;
+    const float r = zero_block ? 0.0f : 1.0f / a;  // correctly rounded RN32(1/a)
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float x = v[i] * r;
+      uint32_t c = zero_block ? 7u : nearest_code(x, th);
+      if (e0 + i >= numel) c = 0u;            // padding beyond the tensor
+      packed |= c << (4 * i);
+    }
+    if (e0 < numel) {
+      const int64_t byte0 = e0 >> 1;
+      if (e0 + 8 <= numel) {
+        *reinterpret_cast<uint32_t*>(codes + byte0) = packed;
+      } else {
+        const int64_t nbytes = ((numel - e0) + 1) >> 1;
+        for (int64_t b = 0; b < nbytes; ++b) codes[byte0 + b] = (uint8_t)(packed >> (8 * b));
+      }
+    }
+    if ((t & 7) == 0) {
+      const int lb = local / kBlock;
+      s_a[lb] = a;
+      const int64_t blk = e0 / kBlock;
+      if (blk < nb) absmax[blk] = a;
+    }
+  }
+  __syncthreads();
+
+  // float64 adjacent-pair tree over the group's valid block constants
+  int n = (int)((nb - g * kDqBlock) < kDqBlock ? (nb - g * kDqBlock) : kDqBlock);
+  s_t[0][t] = (t < n) ? (double)s_a[t] : 0.0;
+  __syncthreads();
+  int src = 0;
+  while (n > 1) {
+    const int half = n >> 1;
+    if (t < half) s_t[src ^ 1][t] = s_t[src][2 * t] + s_t[src][2 * t + 1];
+    if ((n & 1) && t == half) s_t[src ^ 1][t] = s_t[src][n - 1];
+    __syncthreads();
+    src ^= 1;
+    n = (n + 1) >> 1;
+  }
+  if (t == 0) gsum[g] = s_t[src][0];
+}
+
+// Folds buf[0..n) with the adjacent-pair rule, level by level, in place
+// across two halves of the workspace, then writes mean = RN32(S / nb).
+__global__ __launch_bounds__(1024) void tree_fold_kernel(double* __restrict__ a, double* __restrict__ b,
+                                                         int64_t n, int64_t nb, float* __restrict__ mean) {
+  double* src = a;
+  double* dst = b;
+  while (n > 1) {
+    const int64_t half = n >> 1;
+    for (int64_t i = threadIdx.x; i < half; i += blockDim.x) dst[i] = src[2 * i] + src[2 * i + 1];
+    if ((n & 1) && threadIdx.x == 0) dst[half] = src[n - 1];
+    __syncthreads();
+    double* tmp = src;
+    src = dst;
+    dst = tmp;
+    n = (n + 1) >> 1;
+  }
+  if (threadIdx.x == 0) {
+    const double S = (n == 1) ? src[0] : 0.0;
+    mean[0] = nb > 0 ? (float)(S / (double)nb) : 0.0f;
+  }
+}
+
+__global__ __launch_bounds__(kDqBlock) void dq_encode_kernel(const float* __restrict__ absmax, int64_t nb,
+                                                             const float* __restrict__ mean,
+                                                             uint8_t* __restrict__ absmax8,
+                                                             float* __restrict__ scale2) {
+  __shared__ float s_max[kDqBlock / 64];
+  const int t = threadIdx.x;
+  const int64_t b = (int64_t)blockIdx.x * kDqBlock + t;
+  const float mu = mean[0];
+  const float d = (b < nb) ? absmax[b] - mu : 0.0f;  // RN32(a - mu)
+  float m = wave_max(__builtin_fabsf(d), 64);
+  if ((t & 63) == 0) s_max[t >> 6] = m;
+  __syncthreads();
+  float A = s_max[0];
+#pragma unroll
+  for (int i = 1; i < kDqBlock / 64; ++i) A = __builtin_fmaxf(A, s_max[i]);
+  float sigma = A / 448.0f;                            // RN32(A / 448)
+  if (!(sigma >= 0x1p-126f)) sigma = 0.0f;
+  if (b < nb) {
+    uint32_t c = 0;
+    if (sigma != 0.0f) c = f32_to_e4m3(d / sigma);     // RN32(d / sigma), then E4M3
+    absmax8[b] = (uint8_t)c;
+  }
+  if (t == 0) scale2[blockIdx.x] = sigma;
+}
+
+// 16 weights per thread: 8 code bytes in, 32 bytes of bf16 out.
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
+                                                      const uint8_t* __restrict__ absmax8,
+                                                      const float* __restrict__ scale2,
+                                                      const float* __restrict__ mean, NF4Table tab,
+                                                      int64_t numel, uint16_t* __restrict__ out) {
+  __shared__ float s_q[16];
+  if (threadIdx.x < 16) s_q[threadIdx.x] = tab.q[threadIdx.x];
+  __syncthreads();
+  const float mu = mean[0];
+  const int64_t nunits = (numel + 15) / 16;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < nunits;
+       u += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e0 = u * 16;
+    const int64_t blk = e0 / kBlock;
+    const float ap = block_scale(absmax8[blk], scale2[blk / kDqBlock], mu);
+    if (e0 + 16 <= numel) {
+      const u32x2_t c = *reinterpret_cast<const u32x2_t*>(codes + (e0 >> 1));
+      uint32_t o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t word = (i < 4) ? c.x : c.y;
+        const uint32_t byte = (word >> (8 * (i & 3))) & 0xFFu;
+        const float lo = s_q[byte & 15u] * ap;
+        const float hi = s_q[byte >> 4] * ap;
+        o[i] = pack_bf16x2(lo, hi);
+      }
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + e0);
+      dst[0] = u32x4_t{o[0], o[1], o[2], o[3]};
+      dst[1] = u32x4_t{o[4], o[5], o[6], o[7]};
+    } else {
+      for (int64_t e = e0; e < numel; ++e) {
+        const uint32_t byte = codes[e >> 1];
+        const uint32_t c = (e & 1) ? (byte >> 4) : (byte & 15u);
+        out[e] = f32_to_bf16(s_q[c] * ap);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* w, bool bf16_in, int64_t numel, const NF4Thresholds& th,
+                           uint8_t* codes, uint8_t* absmax8, float* scale2, float* mean, void* ws,
+                           hipStream_t stream) {
+  const int64_t nb = (numel + kBlock - 1) / kBlock;
+  const int64_t ng = (nb + kDqBlock - 1) / kDqBlock;
+  QuantWorkspace L = quant_workspace_layout(numel);
+  char* base = static_cast<char*>(ws);
+  float* absmax = reinterpret_cast<float*>(base + L.absmax_off);
+  double* sum_a = reinterpret_cast<double*>(base + L.sum_a_off);
+  double* sum_b = reinterpret_cast<double*>(base + L.sum_b_off);
+  hipError_t e = timed(kTimeQuant, stream, [&] {
+    if (bf16_in)
+      hipLaunchKernelGGL(quant_blocks_kernel<uint16_t>, dim3((unsigned)ng), dim3(kQuantThreads), 0, stream,
+                         static_cast<const uint16_t*>(w), numel, nb, th, codes, absmax, sum_a);
+    else
+      hipLaunchKernelGGL(quant_blocks_kernel<float>, dim3((unsigned)ng), dim3(kQuantThreads), 0, stream,
+                         static_cast<const float*>(w), numel, nb, th, codes, absmax, sum_a);
+    return hipGetLastError();
+  });
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(tree_fold_kernel, dim3(1), dim3(1024), 0, stream, sum_a, sum_b, ng, nb, mean);
+  hipLaunchKernelGGL(dq_encode_kernel, dim3((unsigned)ng), dim3(kDqBlock), 0, stream, absmax, nb, mean,
+                     absmax8, scale2);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* absmax8, const float* scale2,
+                             const float* mean, const NF4Table& tab, int64_t numel, uint16_t* out,
+                             hipStream_t stream) {
+  const int64_t nunits = (numel + 15) / 16;
+  int64_t blocks = (nunits + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  if (blocks < 1) blocks = 1;
+  return timed(kTimeDequant, stream, [&] {
+    hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, codes, absmax8, scale2,
+                       mean, tab, numel, out);
+    return hipGetLastError();
+  });
+}
+
+}  // namespace qlora

@@ -119,18 +119,24 @@ def tiny_512() -> LinearInputs:
                        cfg["w_kind"], cfg["w_std"])
 
 
-def layer_set(name: str, M: int | None = None, only: list[str] | None = None):
-    """Yield (shape, LinearInputs) for each linear of a 7-linear layer set,
-    in the fixed draw order. ``M`` may shrink the token count for tests;
-    ``only`` selects linears by name (the draws of skipped ones still happen,
-    so every linear sees the same bytes whichever subset is requested)."""
+def layer_linear(name: str, index: int, M: int | None = None, with_grad: bool = True):
+    """Inputs of linear ``index`` (0..6: q, k, v, o, gate, up, down) of a
+    7-linear layer set. Each linear has its own stream
+    default_rng([seed, index]), drawn in the order W, L1, L2, X, dY, so any
+    linear can be drawn alone. ``M`` may shrink the token count for tests."""
     cfg = WORKLOADS[name]
-    rng = np.random.default_rng(cfg["seed"])
+    shp = cfg["linears"][index]
+    rng = np.random.default_rng([cfg["seed"], index])
     M = cfg["M"] if M is None else M
-    for shp in cfg["linears"]:
-        inp = draw_linear(rng, shp, M, cfg["r"], cfg["s"], cfg["w_kind"], cfg["w_std"])
-        if only is None or shp.name in only:
-            yield shp, inp
+    return shp, draw_linear(rng, shp, M, cfg["r"], cfg["s"], cfg["w_kind"], cfg["w_std"], with_grad)
+
+
+def layer_weight(name: str, index: int) -> np.ndarray:
+    """Only the fp32 weight of linear ``index`` (the first draw of its stream)."""
+    cfg = WORKLOADS[name]
+    shp = cfg["linears"][index]
+    rng = np.random.default_rng([cfg["seed"], index])
+    return draw_weight(rng, shp.N, shp.K, cfg["w_kind"], cfg["w_std"])
 
 
 def gemv_inputs(K: int, N: int, M: int, seed: int = 3, r: int = 64, s: float = 0.25) -> LinearInputs:

@@ -1,0 +1,225 @@
+/*
+ * qlora_nf4.h -- C ABI of the MI355X (gfx950) QLoRA NF4 library.
+ *
+ * The library implements the data-parallel hot path of QLoRA as described
+ * on the QLoRA pages (page diycv.top "QLoRA 论文解读"; neura.market
+ * "QLoRA" analysis):
+ *
+ *   - NF4 blockwise quantisation of a frozen weight with block size 64,
+ *     and double quantisation (DQ) of the per-block absmax constants:
+ *     mean-subtracted, stored as 8-bit floats in groups of 256 blocks with
+ *     one fp32 scale per group (section 方法总览 items 1-3);
+ *   - doubleDequant(c1, c2, W) = dequant(dequant(c1, c2), W) to bf16
+ *     (section 关键公式);
+ *   - the QLoRA linear layer Y = X dequant(W) + s X L1 L2 (section
+ *     问题背景, LoRA equation; section 关键公式) and its backward pass,
+ *     which returns dX and the adapter gradients dL1, dL2 but no weight
+ *     gradient (section 关键公式, text after the dtype table).
+ *
+ * Conventions for every entry point
+ *   - Device pointers are HIP device addresses on the current device; host
+ *     pointers are marked "host". Matrices are dense row-major.
+ *   - The frozen weight is stored as Wt[N][K]: N = out_features (rows),
+ *     K = in_features (cols). Blocks of 64 run along the row-major
+ *     flattening; block b covers elements [64b, 64b+64), DQ group g covers
+ *     blocks [256g, 256g+256). The last block and group may be short.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Ownership: the caller allocates and frees every buffer, including
+ *     workspaces sized by the query functions. The library allocates no
+ *     memory and keeps no mutable state; all calls are reentrant.
+ *   - Asynchrony: work is enqueued on `stream` and the call returns without
+ *     synchronising. Errors found on the host (arguments, shapes,
+ *     alignment, workspace size) are returned before anything is enqueued.
+ *     A failed launch returns QLORA_ERR_HIP. Device faults surface at the
+ *     caller's next synchronisation.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - Inputs must be finite; results for NaN/Inf inputs are unspecified.
+ *   - Alignment: every device pointer must be 16-byte aligned unless noted.
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_ERR_ARG = -1,        /* null pointer, bad enum or scalar, r out of range */
+  QLORA_ERR_SHAPE = -2,      /* unsupported or inconsistent sizes */
+  QLORA_ERR_ALIGN = -3,      /* a device pointer is not 16-byte aligned */
+  QLORA_ERR_WORKSPACE = -4,  /* workspace missing or smaller than required */
+  QLORA_ERR_HIP = -5         /* a HIP launch or runtime call failed */
+} qlora_status;
+
+typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
+
+enum {
+  QLORA_BLOCK = 64,      /* weights per first-level absmax constant */
+  QLORA_DQ_BLOCK = 256,  /* first-level constants per second-level scale */
+  QLORA_MAX_RANK = 256   /* largest LoRA rank r accepted */
+};
+
+/*
+ * One NF4+DQ quantised tensor: the pages' (c1, c2, W^NF4) triple plus the
+ * DQ mean. The struct itself lives in host memory; its buffer pointers are
+ * device pointers owned by the caller. Sizes (nb = ceil(rows*cols/64),
+ * ng = ceil(nb/256)):
+ *   codes   [ceil(rows*cols/2)] u8   4-bit codes; element 2j is the low
+ *                                    nibble of byte j, element 2j+1 the high
+ *                                    nibble; an unused last high nibble is 0.
+ *   absmax8 [nb] u8                  E4M3 (OCP "E4M3FN") codes of
+ *                                    (absmax_b - mean) / scale2_g.
+ *   scale2  [ng] f32                 per-group second-level scale.
+ *   mean    [1]  f32                 per-tensor mean of the block absmax.
+ * `codes` must be 16-byte aligned; absmax8, scale2 and mean need only their
+ * natural alignment.
+ */
+typedef struct {
+  int64_t rows;
+  int64_t cols;
+  uint8_t *codes;
+  uint8_t *absmax8;
+  float *scale2;
+  float *mean;
+} qlora_nf4;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *qlora_status_str(int status);
+
+/* Message of the last HIP failure on the calling thread ("" if none). */
+const char *qlora_last_error(void);
+
+/*
+ * qlora_nf4_codebook: the library's 16 NF4 values (host, ascending).
+ * Built once on the host from N(0,1) quantile midpoints
+ * q_i = 1/2 [Q(i/(c+2)) + Q((i+1)/(c+2))], i = 1..c (diycv.top, section
+ * 方法总览 item 2, with c = 2^4 - 1 = 15 for the pages' denominator 17):
+ * the 7 negative members of the 15-value set divided by its largest
+ * magnitude, an exact 0, and the 8 positive members of the 17-value set
+ * divided by its maximum; rounded once to fp32. Index 0 = -1, 7 = 0,
+ * 15 = +1. out16: host array of 16 floats. Returns QLORA_ERR_ARG if NULL.
+ */
+int qlora_nf4_codebook(float *out16);
+
+/*
+ * qlora_quant_sizes: buffer sizes in bytes for a rows x cols tensor (host
+ * only, no device work). Any output pointer may be NULL. workspace_bytes is
+ * the scratch that qlora_quantize needs. rows, cols >= 0.
+ */
+int qlora_quant_sizes(int64_t rows, int64_t cols, size_t *codes_bytes, size_t *absmax8_bytes,
+                      size_t *scale2_bytes, size_t *workspace_bytes);
+
+/*
+ * qlora_quantize: NF4 + DQ quantisation of the weight W (diycv.top, section
+ * 方法总览 items 1-3; training step 1-2 of section 训练与推理流程).
+ *   W         device, rows*cols elements of in_dtype (QLORA_F32 or
+ *             QLORA_BF16), row-major [rows][cols].
+ *   q         host struct; q->rows, q->cols give the shape; its buffers
+ *             receive codes, absmax8, scale2 and mean.
+ *   ws        device scratch of at least qlora_quant_sizes(...).workspace
+ *             bytes, 16-byte aligned.
+ * Per block: a = max|w| (a below 2^-126 makes a zero block, codes 7);
+ * x = RN32(w * RN32(1/a)); code = nearest NF4 value, ties to the lower
+ * code. DQ: mean = RN32(S/nb) with S the float64 adjacent-pair tree sum of
+ * the block absmax values; per group sigma = RN32(max|a - mean| / 448);
+ * absmax8 = E4M3 round-to-nearest-even of RN32((a - mean)/sigma),
+ * saturating at +-448 (0 where sigma is 0). Results are bit-for-bit
+ * deterministic. Empty tensors enqueue nothing.
+ */
+int qlora_quantize(const void *W, qlora_dtype in_dtype, const qlora_nf4 *q, void *ws,
+                   size_t ws_bytes, hipStream_t stream);
+
+/*
+ * qlora_dequantize: doubleDequant to bf16 (diycv.top, section 关键公式):
+ *   a'_b = RN32(RN32(e4m3(absmax8_b) * scale2_g) + mean)
+ *   out_e = bf16_RNE(RN32(q[code_e] * a'_b))
+ *   out  device uint16_t[rows*cols] (bf16 bits), 16-byte aligned.
+ */
+int qlora_dequantize(const qlora_nf4 *q, uint16_t *out, hipStream_t stream);
+
+/*
+ * qlora_linear_workspace: bytes of device workspace that qlora_linear_fwd
+ * and qlora_linear_bwd need for M tokens, in_features K, out_features N and
+ * rank r (host only). One workspace of this size serves both calls.
+ */
+int qlora_linear_workspace(int64_t M, int64_t K, int64_t N, int r, size_t *bytes);
+
+/*
+ * qlora_linear_fwd: Y = X dequant(Wt)^T + s (X L1) L2, computed with bf16
+ * operands and fp32 accumulation, rounded once to bf16 (diycv.top, section
+ * 关键公式 and section 问题背景; dequant as in qlora_dequantize, done on
+ * the fly inside the kernels). The LoRA branch rounds s*(X L1) to bf16
+ * before its second product.
+ *   W      host struct of the NF4+DQ weight [N][K] (rows = N, cols = K).
+ *   X      device bf16 [M][K];  L1 device bf16 [K][r];  L2 device bf16 [r][N].
+ *   scale  the LoRA scale s (finite).
+ *   Y      device bf16 [M][N].
+ *   T_out  optional device bf16 [M][r] receiving bf16(X L1) for the
+ *          backward pass (NULL to skip).
+ *   ws     device workspace of qlora_linear_workspace(M, K, N, r) bytes.
+ * Shapes: M >= 0; K a positive multiple of 64; N a positive multiple of 8;
+ * r a multiple of 8 in [8, 256]. M <= 16 takes the bandwidth-bound GEMV
+ * kernel, larger M the MFMA GEMM; both return the same layer.
+ */
+int qlora_linear_fwd(const qlora_nf4 *W, const uint16_t *X, int64_t M, const uint16_t *L1,
+                     const uint16_t *L2, int r, float scale, uint16_t *Y, uint16_t *T_out,
+                     void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * qlora_linear_bwd: gradients of the layer for the upstream gradient dY
+ * (diycv.top, section 关键公式, text after the dtype table: gradients pass
+ * through the dequantised bf16 base to the input; only the adapters get
+ * parameter gradients):
+ *   dX  = dY dequant(Wt) + s (dY L2^T) L1^T      bf16 [M][K]
+ *   dL1 = s X^T (dY L2^T)                        [K][r] in grad_dtype
+ *   dL2 = s (X L1)^T dY                          [r][N] in grad_dtype
+ * No gradient of the frozen weight is formed.
+ *   T      optional device bf16 [M][r] = bf16(X L1) from qlora_linear_fwd's
+ *          T_out; NULL recomputes it.
+ *   dX     device bf16 [M][K], or NULL to skip the input gradient.
+ *   dL1, dL2  device buffers of grad_dtype (QLORA_F32 or QLORA_BF16).
+ * Other arguments and shape rules as for qlora_linear_fwd. dL1 and dL2 are
+ * reduced over M in a fixed order, so repeated calls are bit-identical.
+ */
+int qlora_linear_bwd(const qlora_nf4 *W, const uint16_t *X, const uint16_t *dY, int64_t M,
+                     const uint16_t *L1, const uint16_t *L2, int r, float scale,
+                     const uint16_t *T, uint16_t *dX, void *dL1, void *dL2,
+                     qlora_dtype grad_dtype, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * qlora_set_timing: measurement hook; it changes no result. While set on the
+ * calling thread for a kernel class, each launch of that class by the
+ * entry points above is bracketed by hipEventRecord(start[i]) and
+ * hipEventRecord(stop[i]) on the call's stream, for i = 0 .. n-1 in launch
+ * order; *count (host) receives the number of brackets recorded so far.
+ * Launches beyond n are not recorded. n = 0 (or NULL arrays) clears the
+ * hook for that class. The event arrays and count are host memory owned by
+ * the caller and must stay valid while the hook is set; the events must
+ * have been created by the caller (hipEventCreate).
+ *   kernel  QLORA_TIMING_FWD_GEMM  fused dequant-GEMM producing Y (M > 16)
+ *           QLORA_TIMING_DX_GEMM   fused transposed-dequant GEMM producing dX
+ *           QLORA_TIMING_GEMV      small-M dequant-GEMV producing Y (M <= 16)
+ *           QLORA_TIMING_QUANT     first quantisation pass (codes + absmax)
+ *           QLORA_TIMING_DEQUANT   standalone dequant kernel
+ * Returns QLORA_ERR_ARG for an unknown class or negative n.
+ */
+enum {
+  QLORA_TIMING_FWD_GEMM = 0,
+  QLORA_TIMING_DX_GEMM = 1,
+  QLORA_TIMING_GEMV = 2,
+  QLORA_TIMING_QUANT = 3,
+  QLORA_TIMING_DEQUANT = 4,
+  QLORA_TIMING_CLASSES = 5
+};
+int qlora_set_timing(int kernel, hipEvent_t *start, hipEvent_t *stop, int n, int *count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_NF4_H */

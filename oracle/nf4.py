@@ -126,17 +126,10 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(_F32)
 
 
-def bf16_rne(x: np.ndarray) -> np.ndarray:
-    """fp32 -> bf16 bit patterns, round to nearest, ties to even mantissa.
+CHUNK = 1 << 20   # elementwise passes run over slices of this many elements
 
-    Written as the definition: of the two bf16 neighbours of x (truncation
-    towards zero and one bf16 ulp further from zero) take the nearer, and on
-    a tie the one whose last mantissa bit is 0. Inputs must be finite and
-    must not round beyond the largest finite bf16 value.
-    """
-    x = np.ascontiguousarray(x, dtype=_F32)
-    if not np.all(np.isfinite(x)):
-        raise ValueError("bf16_rne: non-finite input")
+
+def _bf16_rne_slice(x: np.ndarray) -> np.ndarray:
     bits = x.view(np.uint32)
     lo = (bits >> np.uint32(16)).astype(np.uint32)           # toward zero
     hi = lo + np.uint32(1)                                   # away from zero
@@ -149,8 +142,26 @@ def bf16_rne(x: np.ndarray) -> np.ndarray:
     d_hi = np.abs(hi_v - xv)
     take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((lo & np.uint32(1)) == 1))
     # exact bf16 values (low 16 bits zero) have d_lo == 0 and keep lo
-    out = np.where(take_hi, hi, lo)
-    return out.astype(np.uint16).reshape(x.shape)
+    return np.where(take_hi, hi, lo).astype(np.uint16)
+
+
+def bf16_rne(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest, ties to even mantissa.
+
+    Written as the definition: of the two bf16 neighbours of x (truncation
+    towards zero and one bf16 ulp further from zero) take the nearer, and on
+    a tie the one whose last mantissa bit is 0. Inputs must be finite and
+    must not round beyond the largest finite bf16 value. Elementwise, so it
+    is evaluated slice by slice.
+    """
+    x = np.ascontiguousarray(x, dtype=_F32)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("bf16_rne: non-finite input")
+    flat = x.reshape(-1)
+    out = np.empty(flat.size, dtype=np.uint16)
+    for i in range(0, flat.size, CHUNK):
+        out[i:i + CHUNK] = _bf16_rne_slice(flat[i:i + CHUNK])
+    return out.reshape(x.shape)
 
 
 def e4m3_decode(c: np.ndarray) -> np.ndarray:
@@ -232,11 +243,16 @@ def nearest_codes(x: np.ndarray, q: np.ndarray) -> np.ndarray:
     """code(x) = number of midpoints m_j strictly below x, which is the index
     of the nearest codebook value with ties going to the lower index."""
     m = nf4_midpoints(q)
-    x64 = np.asarray(x, dtype=_F32).astype(_F64)
-    code = np.zeros(x64.shape, dtype=np.int64)
-    for mj in m:
-        code += (x64 > mj)
-    return code.astype(np.uint8)
+    xs = np.asarray(x, dtype=_F32)
+    flat = xs.reshape(-1)
+    out = np.empty(flat.size, dtype=np.uint8)
+    for i in range(0, flat.size, CHUNK):
+        x64 = flat[i:i + CHUNK].astype(_F64)
+        code = np.zeros(x64.shape, dtype=np.uint8)
+        for mj in m:
+            code += (x64 > mj)
+        out[i:i + CHUNK] = code
+    return out.reshape(xs.shape)
 
 
 def pack_nibbles(codes: np.ndarray) -> np.ndarray:
@@ -282,8 +298,12 @@ def quantize(w: np.ndarray, q: np.ndarray | None = None) -> dict:
     r = (_F32(1.0) / safe_a).astype(_F32)                 # RN32(1/a)
     pad = np.zeros(nb * BLOCK, dtype=_F32)
     pad[:numel] = flat
-    x = (pad.reshape(nb, BLOCK) * r[:, None]).astype(_F32)  # RN32(w * r)
-    codes4 = nearest_codes(x, q)
+    blocks = pad.reshape(nb, BLOCK)
+    codes4 = np.empty((nb, BLOCK), dtype=np.uint8)
+    step = CHUNK // BLOCK
+    for b0 in range(0, nb, step):
+        x = (blocks[b0:b0 + step] * r[b0:b0 + step, None]).astype(_F32)  # RN32(w * r)
+        codes4[b0:b0 + step] = nearest_codes(x, q)
     codes4[zero_block, :] = 7                              # exact zero code
     codes4 = codes4.reshape(-1)[:numel]
 
@@ -331,8 +351,12 @@ def dequantize_f32(qt: dict, q: np.ndarray | None = None) -> np.ndarray:
     numel = qt["numel"]
     codes4 = unpack_nibbles(qt["codes"], numel)
     ap = dequant_constants(qt["absmax8"], qt["scale2"], qt["mean"])
-    a_e = np.repeat(ap, BLOCK)[:numel]
-    return (q[codes4] * a_e).astype(_F32)
+    out = np.empty(numel, dtype=_F32)
+    for i in range(0, numel, CHUNK):               # CHUNK is a multiple of BLOCK
+        c = codes4[i:i + CHUNK]
+        a_e = np.repeat(ap[i // BLOCK:(i + c.size + BLOCK - 1) // BLOCK], BLOCK)[:c.size]
+        out[i:i + CHUNK] = (q[c] * a_e).astype(_F32)
+    return out
 
 
 def dequantize(qt: dict, shape=None, q: np.ndarray | None = None) -> np.ndarray:

@@ -1,0 +1,60 @@
+"""Shared helpers of the GPU parity tests (moving seeded inputs to the device,
+calling the library through its binding, and fetching results)."""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+
+def require_gpu():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from bit_nf4_quantized_amd import api
+
+    if not os.path.exists(api.LIB_PATH):
+        raise RuntimeError("libqlora_nf4.so is not built (run bit_nf4_quantized_amd/build.py)")
+    return api
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_quantize(api, W: np.ndarray, bf16: bool = False):
+    """Quantise a host weight on the GPU; returns (NF4Tensor, host dict)."""
+    import torch
+
+    if bf16:
+        t = api.to_device_bf16(W)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(W, np.float32)).cuda()
+    q = api.qlora_quantize(t)
+    torch.cuda.synchronize()
+    return q, nf4_host(q)
+
+
+def nf4_host(q):
+    import torch
+
+    torch.cuda.synchronize()
+    numel = q.rows * q.cols
+    nb = -(-numel // 64)
+    ng = -(-nb // 256)
+    return {
+        "codes": q.codes.cpu().numpy()[: (numel + 1) // 2],
+        "absmax8": q.absmax8.cpu().numpy()[:nb],
+        "scale2": q.scale2.cpu().numpy()[:ng],
+        "mean": q.mean.cpu().numpy(),
+    }
+
+
+def assert_quant_equal(got: dict, ref: dict):
+    np.testing.assert_array_equal(got["mean"].view(np.uint32), ref["mean"].view(np.uint32))
+    np.testing.assert_array_equal(got["scale2"].view(np.uint32), ref["scale2"].view(np.uint32))
+    np.testing.assert_array_equal(got["absmax8"], ref["absmax8"])
+    np.testing.assert_array_equal(got["codes"], ref["codes"])

@@ -1,0 +1,159 @@
+"""Host-side checks of the C-ABI library (CPU only, no device compute).
+
+The library must load, export every function that include/qlora_nf4.h
+declares, build the same NF4 codebook as the oracle, report the buffer sizes
+the format implies, and reject bad arguments on the host before anything is
+enqueued. Only error paths of the launching entry points are exercised here,
+so no HIP call is made.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from bit_nf4_quantized_amd import api
+from oracle import nf4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora_nf4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_ ]*[\s\*]+(qlora_[a-z0-9_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(api.LIB_PATH):
+        from bit_nf4_quantized_amd import build
+        build.build()
+    return api.library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) == 10, names
+    assert sorted(api.EXPORTS) == names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_codebook_matches_oracle_bit_exact(lib):
+    g = api.qlora_nf4_codebook()
+    o = nf4.nf4_codebook()
+    assert g.view(np.uint32).tolist() == o.view(np.uint32).tolist()
+    assert lib.qlora_nf4_codebook(None) == api.QLORA_ERR_ARG
+
+
+@pytest.mark.parametrize("rows,cols", [(0, 0), (1, 1), (3, 21), (512, 512), (4096, 11008), (11008, 4096),
+                                       (22016, 8192), (7, 64 * 256 + 3)])
+def test_quant_sizes_match_format(rows, cols):
+    s = api.qlora_quant_sizes(rows, cols)
+    numel = rows * cols
+    assert s["codes"] == (numel + 1) // 2
+    assert s["absmax8"] == nf4.n_blocks(numel)
+    assert s["scale2"] == 4 * nf4.n_groups(numel)
+    assert s["workspace"] >= 4 * nf4.n_blocks(numel)
+
+
+def test_quant_sizes_rejects_negative(lib):
+    assert lib.qlora_quant_sizes(-1, 4, None, None, None, None) == api.QLORA_ERR_SHAPE
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4, -5):
+        assert lib.qlora_status_str(st).decode().startswith("QLORA_")
+    assert lib.qlora_status_str(42).decode() == "unknown qlora status"
+
+
+def fake_nf4(rows, cols, base=0x10000000):
+    # never dereferenced: every call below fails validation first
+    return api.QNF4(rows, cols, base, base + 0x100000, base + 0x200000, base + 0x300000)
+
+
+def test_quantize_validation(lib):
+    q = fake_nf4(64, 64)
+    ok_ptr = ctypes.c_void_p(0x20000000)
+    ws = ctypes.c_void_p(0x30000000)
+    big = 1 << 30
+    assert lib.qlora_quantize(ok_ptr, 0, None, ws, big, None) == api.QLORA_ERR_ARG
+    assert lib.qlora_quantize(ok_ptr, 7, ctypes.byref(q), ws, big, None) == api.QLORA_ERR_ARG
+    assert lib.qlora_quantize(None, 0, ctypes.byref(q), ws, big, None) == api.QLORA_ERR_ARG
+    assert lib.qlora_quantize(ctypes.c_void_p(0x20000004), 0, ctypes.byref(q), ws, big, None) == api.QLORA_ERR_ALIGN
+    assert lib.qlora_quantize(ok_ptr, 0, ctypes.byref(q), ws, 16, None) == api.QLORA_ERR_WORKSPACE
+    neg = fake_nf4(-1, 4)
+    assert lib.qlora_quantize(ok_ptr, 0, ctypes.byref(neg), ws, big, None) == api.QLORA_ERR_SHAPE
+    empty = fake_nf4(0, 17)
+    assert lib.qlora_quantize(None, 0, ctypes.byref(empty), None, 0, None) == api.QLORA_OK  # nothing to do
+    nullbuf = api.QNF4(64, 64, 0x10000000, None, 0x10200000, 0x10300000)
+    assert lib.qlora_quantize(ok_ptr, 0, ctypes.byref(nullbuf), ws, big, None) == api.QLORA_ERR_ARG
+
+
+def test_dequantize_validation(lib):
+    q = fake_nf4(64, 64)
+    assert lib.qlora_dequantize(None, ctypes.c_void_p(0x20000000), None) == api.QLORA_ERR_ARG
+    assert lib.qlora_dequantize(ctypes.byref(q), None, None) == api.QLORA_ERR_ARG
+    assert lib.qlora_dequantize(ctypes.byref(q), ctypes.c_void_p(0x20000002), None) == api.QLORA_ERR_ALIGN
+    mis = api.QNF4(64, 64, 0x10000001, 0x10100000, 0x10200000, 0x10300000)
+    assert lib.qlora_dequantize(ctypes.byref(mis), ctypes.c_void_p(0x20000000), None) == api.QLORA_ERR_ALIGN
+
+
+def test_linear_workspace_rules():
+    assert api.qlora_linear_workspace(8192, 4096, 11008, 64) > 0
+    assert api.qlora_linear_workspace(0, 4096, 4096, 8) > 0
+    with pytest.raises(api.QLoRAError):
+        api.qlora_linear_workspace(64, 100, 64, 8)     # K not a multiple of 64
+    with pytest.raises(api.QLoRAError):
+        api.qlora_linear_workspace(64, 128, 20, 8)     # N not a multiple of 8
+    with pytest.raises(api.QLoRAError):
+        api.qlora_linear_workspace(64, 128, 64, 12)    # r not a multiple of 8
+    with pytest.raises(api.QLoRAError):
+        api.qlora_linear_workspace(64, 128, 64, 264)   # r above the maximum
+
+
+def test_linear_validation(lib):
+    W = fake_nf4(512, 512)
+    p = lambda a: ctypes.c_void_p(a)
+    X, L1, L2, Y, ws = p(0x21000000), p(0x22000000), p(0x23000000), p(0x24000000), p(0x25000000)
+    big = 1 << 34
+    f = lib.qlora_linear_fwd
+    assert f(None, X, 64, L1, L2, 8, 2.0, Y, None, ws, big, None) == api.QLORA_ERR_ARG
+    assert f(ctypes.byref(W), X, 64, L1, L2, 7, 2.0, Y, None, ws, big, None) == api.QLORA_ERR_ARG
+    assert f(ctypes.byref(W), X, 64, L1, L2, 8, float("nan"), Y, None, ws, big, None) == api.QLORA_ERR_ARG
+    assert f(ctypes.byref(W), X, -1, L1, L2, 8, 2.0, Y, None, ws, big, None) == api.QLORA_ERR_SHAPE
+    bad = fake_nf4(512, 500)
+    assert f(ctypes.byref(bad), X, 64, L1, L2, 8, 2.0, Y, None, ws, big, None) == api.QLORA_ERR_SHAPE
+    assert f(ctypes.byref(W), None, 64, L1, L2, 8, 2.0, Y, None, ws, big, None) == api.QLORA_ERR_ARG
+    assert f(ctypes.byref(W), p(0x21000008), 64, L1, L2, 8, 2.0, Y, None, ws, big, None) == api.QLORA_ERR_ALIGN
+    assert f(ctypes.byref(W), X, 64, L1, L2, 8, 2.0, Y, None, ws, 64, None) == api.QLORA_ERR_WORKSPACE
+    assert f(ctypes.byref(W), X, 64, L1, L2, 8, 2.0, Y, None, None, big, None) == api.QLORA_ERR_WORKSPACE
+    b = lib.qlora_linear_bwd
+    dY, dX, g1, g2 = p(0x26000000), p(0x27000000), p(0x28000000), p(0x29000000)
+    assert b(ctypes.byref(W), X, dY, 64, L1, L2, 8, 2.0, None, dX, g1, g2, 5, ws, big, None) == api.QLORA_ERR_ARG
+    assert b(ctypes.byref(W), X, dY, 64, L1, L2, 8, 2.0, None, dX, None, g2, 0, ws, big, None) == api.QLORA_ERR_ARG
+    assert b(ctypes.byref(W), X, None, 64, L1, L2, 8, 2.0, None, dX, g1, g2, 0, ws, big, None) == api.QLORA_ERR_ARG
+    assert b(ctypes.byref(W), X, dY, 64, L1, L2, 8, 2.0, None, p(0x27000004), g1, g2, 0, ws, big,
+             None) == api.QLORA_ERR_ALIGN
+    assert b(ctypes.byref(W), X, dY, 64, L1, L2, 8, 2.0, None, dX, g1, g2, 0, ws, 100, None) == api.QLORA_ERR_WORKSPACE
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+
+    W = torch.zeros(64, 64)
+    with pytest.raises(ValueError):
+        api.qlora_quantize(W)
+
+
+def test_set_timing_validation(lib):
+    cnt = ctypes.c_int(0)
+    assert lib.qlora_set_timing(-1, None, None, 0, None) == api.QLORA_ERR_ARG
+    assert lib.qlora_set_timing(5, None, None, 0, None) == api.QLORA_ERR_ARG
+    assert lib.qlora_set_timing(0, None, None, -2, ctypes.byref(cnt)) == api.QLORA_ERR_ARG
+    assert lib.qlora_set_timing(0, None, None, 0, None) == api.QLORA_OK       # clearing is always fine
