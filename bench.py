@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of the QLoRA NF4 hot path on one MI355X.
+
+Timed step: forward + backward of all 7 linears of a LLaMA-7B-shaped layer
+(q, k, v, o 4096x4096; gate, up 4096->11008; down 11008->4096) for 8192
+tokens with NF4 + DQ base weights (normal, 0.1 % outliers x10), LoRA rank 64
+on every linear, s = 0.25. Per linear: qlora_linear_fwd (Y and T) then
+qlora_linear_bwd (dX, dL1, dL2). The weights are quantised once before
+timing (the base is frozen, as in QLoRA training). Inputs are synthetic and
+already resident in HBM when timing starts.
+
+value = algorithmic fwd+bwd flops per step / time per step, with flops
+4 M K N + 6 M r (K + N) per linear (3 forward and 5 backward products, no
+weight gradient; dequantisation is not counted).
+
+The same run also measures:
+  * roofline of the dominant fused dequant-GEMM kernel, from HIP events that
+    the library records around each of its launches on the call's stream;
+  * the small-M dequant-GEMV (M in {1, 4, 16}; 4096->11008 and 11008->4096)
+    in GB/s against 8 TB/s, cycling >= 24 distinct weight copies (> 512 MB)
+    so the 256 MB last-level cache cannot serve the weights;
+  * NF4 + DQ quantisation throughput on a LLaMA-65B-shaped tensor;
+  * the CPU oracle on a bounded sample (all 7 linears, 512 of the 8192
+    tokens) as a baseline.
+Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def linear_flops(M, K, N, r):
+    return 4 * M * K * N + 6 * M * r * (K + N)
+
+
+def nf4_bytes(K, N):
+    numel = K * N
+    nb = -(-numel // 64)
+    ng = -(-nb // 256)
+    return numel // 2 + nb + 4 * ng + 4
+
+
+def setup_layer(api, workloads, name, M=None):
+    import torch
+
+    cfg = workloads.WORKLOADS[name]
+    layers = []
+    host = []
+    for idx, shp in enumerate(cfg["linears"]):
+        _, inp = workloads.layer_linear(name, idx, M=M)
+        W = torch.from_numpy(inp.W).cuda()
+        q = api.qlora_quantize(W)
+        torch.cuda.synchronize()
+        del W
+        Mx = inp.X.shape[0]
+        r = inp.L1.shape[1]
+        d = dict(shape=shp, q=q, s=inp.s, M=Mx, r=r,
+                 X=api.to_device_bf16(inp.X), dY=api.to_device_bf16(inp.dY),
+                 L1=api.to_device_bf16(inp.L1), L2=api.to_device_bf16(inp.L2))
+        d["Y"] = torch.empty((Mx, shp.N), dtype=torch.bfloat16, device="cuda")
+        d["T"] = torch.empty((Mx, r), dtype=torch.bfloat16, device="cuda")
+        d["dX"] = torch.empty((Mx, shp.K), dtype=torch.bfloat16, device="cuda")
+        d["dL1"] = torch.empty((shp.K, r), dtype=torch.float32, device="cuda")
+        d["dL2"] = torch.empty((r, shp.N), dtype=torch.float32, device="cuda")
+        layers.append(d)
+        host.append((shp, inp))
+        log(f"setup {shp.name} K={shp.K} N={shp.N} M={Mx}")
+    ws_bytes = max(api.qlora_linear_workspace(d["M"], d["shape"].K, d["shape"].N, d["r"]) for d in layers)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    return layers, host, ws
+
+
+def run_step(api, layers, ws):
+    for d in layers:
+        api.qlora_linear_fwd(d["q"], d["X"], d["L1"], d["L2"], d["s"], Y=d["Y"], T_out=d["T"], workspace=ws)
+        api.qlora_linear_bwd(d["q"], d["X"], d["dY"], d["L1"], d["L2"], d["s"], T=d["T"], dX=d["dX"],
+                             dL1=d["dL1"], dL2=d["dL2"], workspace=ws)
+
+
+def kernel_summary(durs_ms, flops):
+    tot_ms = sum(durs_ms)
+    tot_f = sum(flops)
+    return {"launches": len(durs_ms), "avg_ms": tot_ms / max(len(durs_ms), 1),
+            "tflops": tot_f / (tot_ms * 1e-3) / 1e12 if tot_ms > 0 else None, "total_ms": tot_ms}
+
+
+def bench_gemv(api, workloads, reps=4):
+    """Decode-style forward, M in {1, 4, 16}, weights cycled over distinct copies."""
+    import torch
+
+    out = []
+    for K, N in ((4096, 11008), (11008, 4096)):
+        inp = workloads.gemv_inputs(K, N, 16)
+        q0 = api.qlora_quantize(torch.from_numpy(inp.W).cuda())
+        wbytes = nf4_bytes(K, N)
+        copies = max(24, -(-600 * 2 ** 20 // wbytes))
+        qs = [api.NF4Tensor(q0.rows, q0.cols, q0.codes.clone(), q0.absmax8.clone(), q0.scale2.clone(),
+                            q0.mean.clone()) for _ in range(copies)]
+        Xall = api.to_device_bf16(inp.X)
+        L1, L2 = api.to_device_bf16(inp.L1), api.to_device_bf16(inp.L2)
+        r = L1.shape[1]
+        for M in (1, 4, 16):
+            X = Xall[:M].contiguous()
+            Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            ws = torch.empty(api.qlora_linear_workspace(M, K, N, r), dtype=torch.uint8, device="cuda")
+            for i in range(copies):   # warm-up pass over every copy
+                api.qlora_linear_fwd(qs[i], X, L1, L2, inp.s, Y=Y, workspace=ws)
+            n = copies * reps
+            timer = api.KernelTimer(api.QLORA_TIMING_GEMV, capacity=n)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            with timer:
+                e0.record()
+                for i in range(n):
+                    api.qlora_linear_fwd(qs[i % copies], X, L1, L2, inp.s, Y=Y, workspace=ws)
+                e1.record()
+            torch.cuda.synchronize()
+            durs = timer.durations_ms()
+            avg = sum(durs) / len(durs)
+            kbytes = wbytes + 2 * M * K + 2 * M * r + 2 * r * N + 2 * M * N   # kernel's own stream
+            cbytes = wbytes + 2 * r * (K + N) + 2 * M * K + 2 * M * N          # whole call
+            call_ms = e0.elapsed_time(e1) / n
+            out.append({"K": K, "N": N, "M": M, "kernel_us": avg * 1e3,
+                        "kernel_GBps": kbytes / (avg * 1e-3) / 1e9,
+                        "kernel_frac_of_hbm_peak": kbytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                        "call_us": call_ms * 1e3, "call_GBps": cbytes / (call_ms * 1e-3) / 1e9,
+                        "weight_copies": copies})
+            log(f"gemv K={K} N={N} M={M}: kernel {avg*1e3:.2f} us "
+                f"{out[-1]['kernel_GBps']:.0f} GB/s, call {call_ms*1e3:.2f} us")
+        del qs
+        torch.cuda.empty_cache()
+    return out
+
+
+def bench_quantize(api, workloads, reps=5):
+    """NF4 + DQ quantisation of a LLaMA-65B gate-shaped weight (22016 x 8192)."""
+    import torch
+
+    shp = workloads.LLAMA65B[4]
+    W32 = torch.from_numpy(workloads.quantize_weight(shp, 4, 4)).cuda()
+    res = {}
+    for dt, W in (("f32", W32), ("bf16", W32.to(torch.bfloat16))):
+        q = api.qlora_quantize(W)
+        ws = torch.empty(api.qlora_quant_sizes(shp.N, shp.K)["workspace"], dtype=torch.uint8, device="cuda")
+        timer = api.KernelTimer(api.QLORA_TIMING_QUANT, capacity=reps)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with timer:
+            e0.record()
+            for _ in range(reps):
+                api.qlora_quantize(W, out=q, workspace=ws)
+            e1.record()
+        torch.cuda.synchronize()
+        numel = shp.N * shp.K
+        nbytes = numel * (4 if dt == "f32" else 2) + nf4_bytes(shp.K, shp.N)
+        call_ms = e0.elapsed_time(e1) / reps
+        k_ms = sum(timer.durations_ms()) / reps
+        res[dt] = {"shape": [shp.N, shp.K], "call_ms": call_ms, "GBps": nbytes / (call_ms * 1e-3) / 1e9,
+                   "frac_of_hbm_peak": nbytes / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                   "pass1_kernel_ms": k_ms}
+        log(f"quantize {dt} {shp.N}x{shp.K}: {call_ms:.3f} ms, {res[dt]['GBps']:.0f} GB/s")
+    return res
+
+
+def cpu_baseline(host, tokens=512):
+    """The oracle (dequant + forward + backward) on all 7 linears for a sample
+    of the tokens, on the host cores; reported in the same unit."""
+    import numpy as np
+
+    from oracle import linear, nf4
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    qts = [(shp, inp, nf4.quantize(inp.W)) for shp, inp in host]   # outside the timed region
+    flops = 0
+    t0 = time.perf_counter()
+    for shp, inp, qt in qts:
+        Wd = nf4.dequantize(qt, inp.W.shape)
+        X, dY = inp.X[:tokens], inp.dY[:tokens]
+        linear.linear_fwd(X, Wd, inp.L1, inp.L2, inp.s)
+        linear.linear_bwd(X, Wd, inp.L1, inp.L2, inp.s, dY)
+        flops += linear_flops(tokens, shp.K, shp.N, inp.L1.shape[1])
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "seconds": dt,
+            "sample": f"all 7 linears, first {tokens} of 8192 tokens: float64 NumPy dequant + fwd + bwd "
+                      f"(BLAS threads = cores; elementwise steps single-threaded)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama7b-layer", choices=["llama7b-layer", "llama33b-layer"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the GEMV and quantize sections")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from bit_nf4_quantized_amd import api, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    api.library()
+    name = args.workload
+    layers, host, ws = setup_layer(api, workloads, name)
+    flops_step = sum(linear_flops(d["M"], d["shape"].K, d["shape"].N, d["r"]) for d in layers)
+    fwd_flops = [2 * d["M"] * d["shape"].K * d["shape"].N + 2 * d["M"] * d["r"] * d["shape"].N for d in layers]
+    dx_flops = [2 * d["M"] * d["shape"].K * d["shape"].N + 2 * d["M"] * d["r"] * d["shape"].K for d in layers]
+
+    for _ in range(args.warmup):
+        run_step(api, layers, ws)
+    torch.cuda.synchronize()
+    n_l = len(layers)
+    t_fwd = api.KernelTimer(api.QLORA_TIMING_FWD_GEMM, capacity=n_l * args.steps)
+    t_dx = api.KernelTimer(api.QLORA_TIMING_DX_GEMM, capacity=n_l * args.steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    with t_fwd, t_dx:
+        e0.record()
+        for _ in range(args.steps):
+            run_step(api, layers, ws)
+        e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    value = flops_step / (ms_step * 1e-3) / 1e12
+    log(f"step {ms_step:.3f} ms, {value:.1f} TFLOP/s (wall {wall / args.steps * 1e3:.3f} ms/step)")
+
+    kf = kernel_summary(t_fwd.durations_ms(), fwd_flops * args.steps)
+    kd = kernel_summary(t_dx.durations_ms(), dx_flops * args.steps)
+    dom_name, dom = ("fwd_gemm", kf) if kf["total_ms"] >= kd["total_ms"] else ("dx_gemm", kd)
+    log(f"fwd GEMM {kf['tflops']:.1f} TFLOP/s avg {kf['avg_ms']:.3f} ms; "
+        f"dX GEMM {kd['tflops']:.1f} TFLOP/s avg {kd['avg_ms']:.3f} ms")
+    roofline = {"bound": "mfma", "achieved": dom["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": dom["tflops"] / PEAK_BF16_TFLOPS, "traffic": None,
+                "kernel": {"fwd_gemm": "gemm_kernel<A_ROW,B_NF4,EPI_BF16,slab>",
+                           "dx_gemm": "gemm_kernel<A_ROW,B_NF4T,EPI_BF16,slab>"}[dom_name],
+                "avg_launch_ms": dom["avg_ms"], "launches": dom["launches"]}
+
+    shp_desc = ", ".join(f"{d['shape'].name} {d['shape'].K}->{d['shape'].N}" for d in layers)
+    result = {
+        "metric": "QLoRA NF4 linear fwd+bwd TFLOP/s; NF4 GEMV weight GB/s (% of peak)",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{name}: 7 linears ({shp_desc}), {layers[0]['M']} tokens, NF4+DQ base "
+                               f"(block 64, DQ block 256), LoRA r={layers[0]['r']} s={layers[0]['s']} on all 7, "
+                               f"fwd+bwd per step",
+                   "tokens": layers[0]["M"], "rank": layers[0]["r"], "lora_scale": layers[0]["s"],
+                   "flops_per_step": flops_step},
+        "roofline": roofline,
+        "kernels": {"fwd_gemm": kf, "dx_gemm": kd},
+    }
+    del layers, ws
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        result["gemv"] = bench_gemv(api, workloads)
+        result["quantize"] = bench_quantize(api, workloads)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(host)
+        log(f"cpu baseline {result['cpu_baseline']['value']:.4f} TFLOP/s in {result['cpu_baseline']['seconds']:.1f} s")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
