@@ -178,7 +178,7 @@ def bench_quantize(api, workloads, reps=5):
     return res
 
 
-def cpu_baseline(host, tokens=512):
+def cpu_baseline(host, tokens=2048):
     """The oracle (dequant + forward + backward) on all 7 linears for a sample
     of the tokens, on the host cores; reported in the same unit."""
     import numpy as np

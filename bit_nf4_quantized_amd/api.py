@@ -172,6 +172,13 @@ class KernelTimer:
         self.kernel = kernel
         self.events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                        for _ in range(capacity)]
+        # torch creates the underlying HIP event on its first record()
+        for a, b in self.events:
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
+        if any(not a.cuda_event or not b.cuda_event for a, b in self.events):
+            raise RuntimeError("KernelTimer: event creation failed")
         self._start = (ctypes.c_void_p * capacity)(*[e[0].cuda_event for e in self.events])
         self._stop = (ctypes.c_void_p * capacity)(*[e[1].cuda_event for e in self.events])
         self._count = ctypes.c_int(0)

@@ -164,6 +164,7 @@ int qlora_quantize(const void* W, qlora_dtype in_dtype, const qlora_nf4* q, void
   if (!W || !valid_nf4(q) || !ws) return QLORA_ERR_ARG;
   if (!aligned16(W) || !aligned16(q->codes) || !aligned16(ws)) return QLORA_ERR_ALIGN;
   if (ws_bytes < qlora::quant_workspace_layout(numel).total) return QLORA_ERR_WORKSPACE;
+  (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
   const hipError_t e = qlora::launch_quantize(W, in_dtype == QLORA_BF16, numel, tables().th, q->codes,
                                               q->absmax8, q->scale2, q->mean, ws, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
@@ -177,6 +178,7 @@ int qlora_dequantize(const qlora_nf4* q, uint16_t* out, hipStream_t stream) {
   if (numel == 0) return QLORA_OK;
   if (!valid_nf4(q) || !out) return QLORA_ERR_ARG;
   if (!aligned16(q->codes) || !aligned16(out)) return QLORA_ERR_ALIGN;
+  (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
   const hipError_t e =
       qlora::launch_dequantize(q->codes, q->absmax8, q->scale2, q->mean, tables().tab, numel, out, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
@@ -202,6 +204,7 @@ int qlora_linear_fwd(const qlora_nf4* W, const uint16_t* X, int64_t M, const uin
   if (!aligned16(X) || !aligned16(L1) || !aligned16(L2) || !aligned16(Y) || !aligned16(T_out) || !aligned16(ws))
     return QLORA_ERR_ALIGN;
   if (ws_bytes < qlora::linear_workspace_layout(M, W->cols, W->rows, r).total) return QLORA_ERR_WORKSPACE;
+  (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
   const hipError_t e = qlora::linear_forward(view_of(W), tables().tab, X, M, L1, L2, r, scale, Y, T_out, ws, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
@@ -219,6 +222,7 @@ int qlora_linear_bwd(const qlora_nf4* W, const uint16_t* X, const uint16_t* dY, 
       !aligned16(dL1) || !aligned16(dL2) || !aligned16(ws))
     return QLORA_ERR_ALIGN;
   if (ws_bytes < qlora::linear_workspace_layout(M, W->cols, W->rows, r).total) return QLORA_ERR_WORKSPACE;
+  (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
   const hipError_t e = qlora::linear_backward(view_of(W), tables().tab, X, dY, M, L1, L2, r, scale, T, dX, dL1,
                                               dL2, grad_dtype == QLORA_BF16, ws, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
