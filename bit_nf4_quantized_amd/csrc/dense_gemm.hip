@@ -1,0 +1,325 @@
+// bf16 MFMA GEMM core for the large-M QLoRA products on gfx950, and the
+// streaming dequantisers that feed it.
+//
+//   C[M][N] = alpha * ( sum_k A[m][k] B[n][k]  +  sum_j A2[m][j] B2[n][j] )
+//
+// with A, B (and the LoRA slab A2, B2) bf16 row-major and the reduction
+// contiguous ("NT"), fp32 accumulation and one RNE rounding to bf16. Used for
+//   forward  Y  = X  . Wd^T + (s X L1) . L2          (B = Wd [N][K], B2 = L2^T)
+//   backward dX = dY . Wd   + (s dY L2^T) . L1^T     (B = Wd^T [K][N], B2 = L1)
+// where Wd is the doubleDequant of the NF4 weight (QLoRA pages, diycv.top,
+// section 关键公式), written to a bf16 workspace by dequant_rows_kernel /
+// dequant_cols_kernel just before the GEMM. Streaming the weight once more
+// through HBM (2.5 B per weight, a few percent of the GEMM time at these
+// shapes) keeps the MFMA loop free of per-weight VALU work.
+//
+// Tiling (one workgroup per 256 x 256 output tile, 256 threads = 4 waves,
+// one wave per SIMD):
+//   * each wave owns a 128 x 128 sub-tile = 4 x 4 v_mfma_f32_32x32x16_bf16
+//     accumulators (256 fp32 registers per lane);
+//   * K advances in stages of 64: the A and B stage tiles (2 x 32 KB) are
+//     copied global -> LDS by global_load_lds_dwordx4 (no register staging),
+//     double-buffered (128 KB of the 160 KB LDS), so stage k+1 streams in
+//     while stage k feeds the MFMAs;
+//   * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at
+//     position c ^ (r & 7), so the 16-byte fragment reads of 8 consecutive
+//     rows hit 8 different bank groups;
+//   * workgroups are numbered so that the 8 XCDs (each with its own L2) get
+//     contiguous blocks of tiles, ordered in groups of 8 tile-rows so that
+//     concurrently running tiles share A rows and B columns.
+// Rows beyond M or N are read clamped (finite data) and never stored. Every
+// operand must be readable for K (or K2) columns and hold less than 4 GB, so
+// that per-lane offsets fit in 32 bits (the launcher splits larger M).
+#include "common.h"
+#include "launch.h"
+
+namespace qlora {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void gbl_void_t;
+
+constexpr int TM = 256, TN = 256, TK = 64;
+constexpr int kThreads = 256;
+constexpr int kStageElems = TM * TK;  // elements per operand per stage (TM == TN)
+
+struct DenseArgs {
+  const uint16_t* A;
+  const uint16_t* B;
+  const uint16_t* A2;
+  const uint16_t* B2;
+  uint16_t* C;
+  int64_t lda, ldb, ld2, ldc;
+  int64_t M, N;
+  int64_t K;        // main reduction, multiple of TK (operands readable up to K columns)
+  int64_t K2;       // slab reduction, multiple of TK (0 = no slab)
+  float alpha;
+  int tiles_m, tiles_n;
+};
+
+// One stage of one operand: rows [row0, row0+256) x columns [k0, k0+64).
+// Each wave moves 8 rows per instruction (64 lanes x 16 bytes), 8
+// instructions per wave. Lane i of instruction j writes LDS bytes
+// [16 i, 16 i + 16) of the wave's 1 KB slice: row 8(8w+j) + i/8, physical
+// chunk i%8, which holds logical chunk (i%8) ^ (i/8). The address is a
+// wave-uniform base (matrix + k0, advanced per stage) plus a per-lane 32-bit
+// byte offset that is fixed for the whole K loop.
+struct StageOffsets {
+  uint32_t off[8];
+};
+
+__device__ __forceinline__ StageOffsets stage_offsets(int64_t ld, int64_t row0, int64_t nrows) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane >> 3;
+  const int chunk = (lane & 7) ^ lr;
+  StageOffsets o;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int64_t r = row0 + (wave * 8 + j) * 8 + lr;
+    if (r > nrows - 1) r = nrows - 1;
+    o.off[j] = (uint32_t)((r * ld + chunk * 8) * 2);
+  }
+  return o;
+}
+
+__device__ __forceinline__ void stage_load(const uint16_t* __restrict__ P, int64_t k0, const StageOffsets& o,
+                                           uint16_t* lds) {
+  const int wave = threadIdx.x >> 6;
+  const char* base = reinterpret_cast<const char*>(P + k0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int slice = wave * 8 + j;  // 0..31
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + o.off[j]), (lds_void_t*)(lds + slice * 8 * TK), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * TK + ((chunk ^ (row & 7)) << 3); }
+
+__global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(DenseArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2][2][kStageElems];  // [buffer][A, B]
+
+  // tile order: workgroup b runs on XCD b % 8; give each XCD a contiguous
+  // range of tile ids (a bijection for any tile count), then walk the tiles
+  // in groups of 8 tile-rows so that co-resident tiles share A and B.
+  const int ntiles = p.tiles_m * p.tiles_n;
+  const int bid = blockIdx.x;
+  const int xcd = bid % 8, q = ntiles / 8, rem = ntiles % 8;
+  const int t = xcd * q + (xcd < rem ? xcd : rem) + bid / 8;
+  const int group = 8;
+  const int g = t / (group * p.tiles_n);
+  const int first_m = g * group;
+  const int gm = (p.tiles_m - first_m) < group ? (p.tiles_m - first_m) : group;
+  const int tl = t - g * group * p.tiles_n;
+  const int tm = first_m + tl % gm;
+  const int tn = tl / gm;
+  const int64_t m0 = (int64_t)tm * TM, n0 = (int64_t)tn * TN;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nmain = (int)(p.K / TK), nslab = (int)(p.K2 / TK);
+  const int nk = nmain + nslab;
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  const StageOffsets offA = stage_offsets(p.lda, m0, p.M);
+  const StageOffsets offB = stage_offsets(p.ldb, n0, p.N);
+  auto issue = [&](int st, int buf) {
+    if (st < nmain) {
+      const int64_t k0 = (int64_t)st * TK;
+      stage_load(p.A, k0, offA, smem[buf][0]);
+      stage_load(p.B, k0, offB, smem[buf][1]);
+    } else {
+      const int64_t k0 = (int64_t)(st - nmain) * TK;
+      stage_load(p.A2, k0, stage_offsets(p.ld2, m0, p.M), smem[buf][0]);
+      stage_load(p.B2, k0, stage_offsets(p.ld2, n0, p.N), smem[buf][1]);
+    }
+  };
+
+  if (nk > 0) issue(0, 0);
+  for (int st = 0; st < nk; ++st) {
+    const int buf = st & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (st + 1 < nk) issue(st + 1, buf ^ 1);
+    const uint16_t* As = smem[buf][0];
+    const uint16_t* Bs = smem[buf][1];
+#pragma unroll
+    for (int kk = 0; kk < TK / 16; ++kk) {
+      const int ch = 2 * kk + (lane >> 5);
+      bf16x8_t a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ra = wm * 128 + i * 32 + (lane & 31);
+        const int rb = wn * 128 + i * 32 + (lane & 31);
+        a[i] = *reinterpret_cast<const bf16x8_t*>(As + lds_off(ra, ch));
+        b[i] = *reinterpret_cast<const bf16x8_t*>(Bs + lds_off(rb, ch));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // Epilogue through LDS (the stage buffers are free now): each wave writes
+  // half of its 128 x 128 sub-tile (64 rows) as bf16 into its own padded LDS
+  // slice, then stores it to C in 16-byte row chunks. In a 32x32 accumulator,
+  // register v of lane l is row (v%4) + 4(l/32) + 8(v/4), column l%32.
+  constexpr int kEpiStride = 128 + 8;  // padded row (elements): rows r and r+4 land 16 banks apart
+  __syncthreads();
+  uint16_t* ep = &smem[0][0][0] + wave * (64 * kEpiStride);
+  const int64_t row_base = m0 + wm * 128, col_base = n0 + wn * 128;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const int i = 2 * h + ii;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = ii * 32 + (v & 3) + 4 * (lane >> 5) + 8 * (v >> 2);
+          const int c = j * 32 + (lane & 31);
+          ep[r * kEpiStride + c] = f32_to_bf16(p.alpha * acc[i][j][v]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done (wave-private slice)
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int r = it * 4 + (lane >> 4);  // 64 rows, 16 lanes per row
+      const int ch = lane & 15;            // 16-byte chunk within the 128-column row
+      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ep + r * kEpiStride + ch * 8);
+      const int64_t row = row_base + h * 64 + r;
+      const int64_t col = col_base + ch * 8;
+      if (row < p.M && col < p.N) *reinterpret_cast<u32x4_t*>(p.C + row * p.ldc + col) = val;
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads of this half done before the next half overwrites it
+  }
+}
+
+// Wd[n][k] for the forward product: 16 weights per thread, the standalone
+// dequant arithmetic (bf16(RN32(q[code] * a'))), rows of the workspace
+// padded to ldo columns (ldo >= K).
+__global__ __launch_bounds__(256) void dequant_rows_kernel(NF4View W, NF4Table tab, uint16_t* __restrict__ out) {
+  __shared__ float s_q[16];
+  if (threadIdx.x < 16) s_q[threadIdx.x] = tab.q[threadIdx.x];
+  __syncthreads();
+  const float mu = W.mean[0];
+  const int64_t numel = W.rows * W.cols;
+  const int64_t nunits = numel / 16;  // cols % 64 == 0
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < nunits;
+       u += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e0 = u * 16;
+    const int64_t blk = e0 / kBlock;
+    const float ap = block_scale(W.absmax8[blk], W.scale2[blk / kDqBlock], mu);
+    const u32x2_t c = *reinterpret_cast<const u32x2_t*>(W.codes + (e0 >> 1));
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t word = (i < 4) ? c.x : c.y;
+      const uint32_t byte = (word >> (8 * (i & 3))) & 0xFFu;
+      o[i] = pack_bf16x2(s_q[byte & 15u] * ap, s_q[byte >> 4] * ap);
+    }
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + e0);
+    dst[0] = u32x4_t{o[0], o[1], o[2], o[3]};
+    dst[1] = u32x4_t{o[4], o[5], o[6], o[7]};
+  }
+}
+
+// WdT[k][n] = Wd[n][k] for the dX product, rows padded to ldo >= N columns
+// with zeros. One workgroup per 64 x 64 tile (64 weight rows n, 64 weight
+// columns k = one 64-block per row): each thread dequantises 16 weights of
+// one row, the tile is transposed through LDS, and written 16 bytes per thread.
+__global__ __launch_bounds__(256) void dequant_cols_kernel(NF4View W, NF4Table tab, uint16_t* __restrict__ out,
+                                                           int64_t ldo) {
+  __shared__ float s_q[16];
+  __shared__ uint16_t tile[64][64 + 8];
+  if (threadIdx.x < 16) s_q[threadIdx.x] = tab.q[threadIdx.x];
+  __syncthreads();
+  const float mu = W.mean[0];
+  const int64_t K = W.cols, N = W.rows;
+  const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
+  const int t = threadIdx.x;
+  {
+    const int row = t >> 2, part = t & 3;  // 64 rows x 4 parts of 16 weights
+    const int64_t n = n0 + row;
+    uint32_t o[8];
+    if (n < N) {
+      const int64_t e0 = n * K + k0 + part * 16;
+      const int64_t blk = e0 / kBlock;
+      const float ap = block_scale(W.absmax8[blk], W.scale2[blk / kDqBlock], mu);
+      const u32x2_t c = *reinterpret_cast<const u32x2_t*>(W.codes + (e0 >> 1));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t word = (i < 4) ? c.x : c.y;
+        const uint32_t byte = (word >> (8 * (i & 3))) & 0xFFu;
+        o[i] = pack_bf16x2(s_q[byte & 15u] * ap, s_q[byte >> 4] * ap);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      tile[row][part * 16 + 2 * i] = (uint16_t)(o[i] & 0xFFFFu);
+      tile[row][part * 16 + 2 * i + 1] = (uint16_t)(o[i] >> 16);
+    }
+  }
+  __syncthreads();
+  {
+    const int kr = t >> 2, part = t & 3;  // output row k0+kr, columns n0 + 16 part .. +16
+    const int64_t k = k0 + kr;
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      o[i] = (uint32_t)tile[part * 16 + 2 * i][kr] | ((uint32_t)tile[part * 16 + 2 * i + 1][kr] << 16);
+    const int64_t c0 = n0 + part * 16;
+    if (k < K && c0 < ldo) {
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + k * ldo + c0);
+      dst[0] = u32x4_t{o[0], o[1], o[2], o[3]};
+      dst[1] = u32x4_t{o[4], o[5], o[6], o[7]};
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dequant_rows(const NF4View& W, const NF4Table& tab, uint16_t* out, hipStream_t stream) {
+  const int64_t nunits = W.rows * W.cols / 16;
+  int64_t blocks = (nunits + 255) / 256;
+  if (blocks > 256 * 32) blocks = 256 * 32;
+  hipLaunchKernelGGL(dequant_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W, tab, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_cols(const NF4View& W, const NF4Table& tab, uint16_t* out, int64_t ldo,
+                               hipStream_t stream) {
+  const dim3 grid((unsigned)(W.cols / 64), (unsigned)((ldo + 63) / 64));
+  hipLaunchKernelGGL(dequant_cols_kernel, grid, dim3(256), 0, stream, W, tab, out, ldo);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                          int64_t M, int64_t N, int64_t K, const uint16_t* A2, const uint16_t* B2, int64_t ld2,
+                          int64_t K2, uint16_t* C, int64_t ldc, float alpha, hipStream_t stream) {
+  DenseArgs p;
+  p.A = A; p.B = B; p.A2 = A2; p.B2 = B2; p.C = C;
+  p.lda = lda; p.ldb = ldb; p.ld2 = ld2; p.ldc = ldc;
+  p.M = M; p.N = N; p.K = K; p.K2 = K2; p.alpha = alpha;
+  p.tiles_m = (int)((M + TM - 1) / TM);
+  p.tiles_n = (int)((N + TN - 1) / TN);
+  const int ntiles = p.tiles_m * p.tiles_n;
+  hipLaunchKernelGGL(gemm_nt_kernel, dim3((unsigned)ntiles), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace qlora

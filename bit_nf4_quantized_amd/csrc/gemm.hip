@@ -26,6 +26,8 @@
 // the fragment reads of 8 consecutive rows hit distinct banks. Global loads
 // of step k+1 are issued before the MFMAs of step k; the weight tile is
 // dequantised after them.
+#include <initializer_list>
+
 #include "common.h"
 #include "launch.h"
 
@@ -331,19 +333,30 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
   }
 }
 
-// out[i] = alpha * sum_z P[z][i] (fixed z order) as bf16 or fp32; out2 (if
-// non-null) = bf16(alpha2 * sum).
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, int Z, int64_t count,
-                                                            float alpha, void* __restrict__ out, int out_bf16,
-                                                            float alpha2, uint16_t* __restrict__ out2) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+// Fixed-order split-K reduction of partials P[z][rows][cols]:
+//   out[m][j]  = alpha  * sum_z P[z][m][j]   (bf16 or fp32, row stride ldo;
+//                columns [cols, ldo) of a bf16 out are zero-filled)
+//   out2[m][j] = bf16(alpha2 * sum)          (optional, row stride cols)
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, int Z, int64_t rows,
+                                                            int64_t cols, float alpha, void* __restrict__ out,
+                                                            int out_bf16, int64_t ldo, float alpha2,
+                                                            uint16_t* __restrict__ out2) {
+  const int64_t count = rows * cols;
+  const int64_t total = rows * ldo;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
-    float s = 0.0f;
-    for (int z = 0; z < Z; ++z) s += P[(int64_t)z * count + i];
-    const float v = alpha * s;
+    const int64_t m = i / ldo, j = i - m * ldo;
+    if (j >= cols) {  // padding columns of a bf16 slab operand
+      static_cast<uint16_t*>(out)[i] = 0;
+      continue;
+    }
+    const int64_t src = m * cols + j;
+    float acc = 0.0f;
+    for (int z = 0; z < Z; ++z) acc += P[(int64_t)z * count + src];
+    const float v = alpha * acc;
     if (out_bf16) static_cast<uint16_t*>(out)[i] = f32_to_bf16(v);
     else static_cast<float*>(out)[i] = v;
-    if (out2) out2[i] = f32_to_bf16(alpha2 * s);
+    if (out2) out2[src] = f32_to_bf16(alpha2 * acc);
   }
 }
 
@@ -352,9 +365,10 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p
     p[i] = 0u;
 }
 
-// dst[c][r] = src[r][c] for a bf16 [R][C] matrix.
+// dst[c][r] = src[r][c] for a bf16 [R][C] matrix; dst rows have stride ldd
+// >= R and columns [R, ldd) are zero.
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src, int64_t R,
-                                                             int64_t C, uint16_t* __restrict__ dst) {
+                                                             int64_t C, uint16_t* __restrict__ dst, int64_t ldd) {
   __shared__ uint16_t tile[32][33];
   const int64_t c0 = (int64_t)blockIdx.x * 32, r0 = (int64_t)blockIdx.y * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
@@ -365,7 +379,18 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
   __syncthreads();
   for (int y = ty; y < 32; y += 8) {
     const int64_t c = c0 + y, r = r0 + tx;
-    if (r < R && c < C) dst[c * R + r] = tile[tx][y];
+    if (r < ldd && c < C) dst[c * ldd + r] = tile[tx][y];
+  }
+}
+
+// dst[r][c] = src[r][c] for c < C, 0 for C <= c < ldd (bf16).
+__global__ __launch_bounds__(256) void pad_cols_kernel(const uint16_t* __restrict__ src, int64_t R, int64_t C,
+                                                       uint16_t* __restrict__ dst, int64_t ldd) {
+  const int64_t total = R * ldd;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / ldd, c = i - r * ldd;
+    dst[i] = c < C ? src[r * C + c] : 0;
   }
 }
 
@@ -402,14 +427,20 @@ Split choose_split(int64_t tiles, int64_t klen) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-hipError_t reduce(const float* P, int Z, int64_t count, float alpha, void* out, bool out_bf16, float alpha2,
-                  uint16_t* out2, hipStream_t stream) {
-  int64_t blocks = cdiv(count, 256);
+hipError_t reduce(const float* P, int Z, int64_t rows, int64_t cols, float alpha, void* out, bool out_bf16,
+                  int64_t ldo, float alpha2, uint16_t* out2, hipStream_t stream) {
+  int64_t blocks = cdiv(rows * ldo, 256);
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, P, Z, count, alpha, out,
-                     out_bf16 ? 1 : 0, alpha2, out2);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, P, Z, rows, cols, alpha,
+                     out, out_bf16 ? 1 : 0, ldo, alpha2, out2);
   return hipGetLastError();
+}
+
+int64_t grid_for(int64_t total) {
+  int64_t b = cdiv(total, 256);
+  if (b > 4096) b = 4096;
+  return b < 1 ? 1 : b;
 }
 
 GemmArgs base_args() {
@@ -426,6 +457,8 @@ hipError_t launch_gemv(const NF4View& W, const NF4Table& tab, const uint16_t* X,
 LinearWorkspace linear_workspace_layout(int64_t M, int64_t K, int64_t N, int r) {
   LinearWorkspace L;
   const int64_t mtiles = cdiv(M, BM);
+  const int64_t rp = cdiv(r, 64) * 64;  // LoRA slab width, zero-padded to the GEMM K-stage
+  const int64_t np = cdiv(N, 64) * 64;
   const Split sT = choose_split(mtiles * cdiv(r, BN), K);
   const Split sU = choose_split(mtiles * cdiv(r, BN), N);
   const Split s1 = choose_split(cdiv(K, BM) * cdiv(r, BN), M);
@@ -437,18 +470,36 @@ LinearWorkspace linear_workspace_layout(int64_t M, int64_t K, int64_t N, int r) 
   upd((size_t)s1.Z * K * r * 4);
   upd((size_t)s2.Z * r * N * 4);
   size_t off = 0;
-  L.l2t_off = off; off += align_up((size_t)N * r * 2, 256);
-  L.st_off = off;  off += align_up((size_t)M * r * 2, 256);
+  L.l2t_off = off; off += align_up((size_t)N * rp * 2, 256);
+  L.l1p_off = off; off += align_up((size_t)K * rp * 2, 256);
+  L.st_off = off;  off += align_up((size_t)M * rp * 2, 256);
   L.t_off = off;   off += align_up((size_t)M * r * 2, 256);
-  L.su_off = off;  off += align_up((size_t)M * r * 2, 256);
+  L.su_off = off;  off += align_up((size_t)M * rp * 2, 256);
   L.part_off = off; L.part_bytes = align_up(part, 256); off += L.part_bytes;
+  // dense path: the dequantised weight (forward [N][K], backward [K][np])
+  L.wd_off = off;
+  L.wd_bytes = M > 16 ? align_up((size_t)K * (size_t)(np > N ? np : N) * 2, 256) : 0;
+  off += L.wd_bytes;
   L.total = off > 0 ? off : 256;
   return L;
 }
 
-// T = X L1 (fp32 split-K partials), then sT = bf16(s T) and optionally T_out = bf16(T).
+namespace {
+
+// Dense (dequantise-then-GEMM) path limits: every operand of the NT GEMM is
+// addressed with 32-bit per-lane offsets.
+bool fits_dense(std::initializer_list<int64_t> bytes) {
+  for (int64_t b : bytes)
+    if (b >= ((int64_t)1 << 31)) return false;
+  return true;
+}
+
+}  // namespace
+
+// T = X L1 (fp32 split-K partials), then sT = bf16(s T) with row stride ldst
+// (zero-padded columns) and optionally T_out = bf16(T) [M][r].
 static hipError_t lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* L1, int r, float s,
-                            uint16_t* sT, uint16_t* T_out, float* part, hipStream_t stream) {
+                            uint16_t* sT, int64_t ldst, uint16_t* T_out, float* part, hipStream_t stream) {
   GemmArgs a = base_args();
   a.M = M; a.N = r; a.K = K;
   a.A = X; a.lda = K;
@@ -458,7 +509,7 @@ static hipError_t lora_down(const uint16_t* X, int64_t M, int64_t K, const uint1
   a.C = part; a.ldc = r;
   hipError_t e = run_gemm<A_ROW, B_COL, EPI_F32, false>(a, sp.Z, stream);
   if (e != hipSuccess) return e;
-  return reduce(part, sp.Z, M * (int64_t)r, s, sT, true, 1.0f, T_out, stream);
+  return reduce(part, sp.Z, M, r, s, sT, true, ldst, 1.0f, T_out, stream);
 }
 
 hipError_t linear_forward(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M,
@@ -467,21 +518,35 @@ hipError_t linear_forward(const NF4View& W, const NF4Table& tab, const uint16_t*
   const int64_t K = W.cols, N = W.rows;
   if (M == 0) return hipSuccess;
   const LinearWorkspace L = linear_workspace_layout(M, K, N, r);
+  const int64_t rp = cdiv(r, 64) * 64;
   char* base = static_cast<char*>(ws);
   uint16_t* l2t = reinterpret_cast<uint16_t*>(base + L.l2t_off);
   uint16_t* sT = reinterpret_cast<uint16_t*>(base + L.st_off);
   float* part = reinterpret_cast<float*>(base + L.part_off);
 
-  hipError_t e = lora_down(X, M, K, L1, r, s, sT, T_out, part, stream);
+  if (M <= 16) {
+    hipError_t e = lora_down(X, M, K, L1, r, s, sT, r, T_out, part, stream);
+    if (e != hipSuccess) return e;
+    return timed(kTimeGemv, stream, [&] { return launch_gemv(W, tab, X, M, sT, L2, r, Y, stream); });
+  }
+
+  const bool dense = fits_dense({M * K * 2, N * K * 2, M * rp * 2, N * rp * 2});
+  const int64_t ldst = dense ? rp : r;
+  hipError_t e = lora_down(X, M, K, L1, r, s, sT, ldst, T_out, part, stream);
   if (e != hipSuccess) return e;
-
-  if (M <= 16) return timed(kTimeGemv, stream, [&] { return launch_gemv(W, tab, X, M, sT, L2, r, Y, stream); });
-
-  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)cdiv(N, 32), (unsigned)cdiv(r, 32)), dim3(256), 0,
-                     stream, L2, (int64_t)r, N, l2t);
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)cdiv(N, 32), (unsigned)cdiv(ldst, 32)), dim3(256), 0,
+                     stream, L2, (int64_t)r, N, l2t, ldst);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
+  if (dense) {
+    uint16_t* wd = reinterpret_cast<uint16_t*>(base + L.wd_off);
+    e = launch_dequant_rows(W, tab, wd, stream);
+    if (e != hipSuccess) return e;
+    return timed(kTimeFwdGemm, stream, [&] {
+      return launch_gemm_nt(X, K, wd, K, M, N, K, sT, l2t, rp, rp, Y, N, 1.0f, stream);
+    });
+  }
   GemmArgs a = base_args();
   a.M = M; a.N = N; a.K = K; a.k_split = K;
   a.A = X; a.lda = K;
@@ -497,10 +562,12 @@ hipError_t linear_backward(const NF4View& W, const NF4Table& tab, const uint16_t
                            void* ws, hipStream_t stream) {
   const int64_t K = W.cols, N = W.rows;
   const LinearWorkspace L = linear_workspace_layout(M, K, N, r);
+  const int64_t rp = cdiv(r, 64) * 64;
   char* base = static_cast<char*>(ws);
   uint16_t* tbuf = reinterpret_cast<uint16_t*>(base + L.t_off);
   uint16_t* sT = reinterpret_cast<uint16_t*>(base + L.st_off);
   uint16_t* sU = reinterpret_cast<uint16_t*>(base + L.su_off);
+  uint16_t* l1p = reinterpret_cast<uint16_t*>(base + L.l1p_off);
   float* part = reinterpret_cast<float*>(base + L.part_off);
   hipError_t e;
 
@@ -513,6 +580,9 @@ hipError_t linear_backward(const NF4View& W, const NF4Table& tab, const uint16_t
     return hipGetLastError();
   }
 
+  const bool dense = dX && M > 16 && (N % 64) == 0 && fits_dense({M * N * 2, K * N * 2, M * rp * 2, K * rp * 2});
+  const int64_t ldsu = dense ? rp : r;
+
   // U = dY L2^T -> sU = bf16(s U)
   {
     GemmArgs a = base_args();
@@ -524,11 +594,27 @@ hipError_t linear_backward(const NF4View& W, const NF4Table& tab, const uint16_t
     a.C = part; a.ldc = r;
     e = run_gemm<A_ROW, B_ROW, EPI_F32, false>(a, sp.Z, stream);
     if (e != hipSuccess) return e;
-    e = reduce(part, sp.Z, M * (int64_t)r, s, sU, true, 0.0f, nullptr, stream);
+    e = reduce(part, sp.Z, M, r, s, sU, true, ldsu, 0.0f, nullptr, stream);
     if (e != hipSuccess) return e;
   }
   // dX = dY dequant(Wt) + sU L1^T
-  if (dX) {
+  if (dX && dense) {
+    const uint16_t* l1s = L1;
+    if (rp != r) {
+      hipLaunchKernelGGL(pad_cols_kernel, dim3((unsigned)grid_for(K * rp)), dim3(256), 0, stream, L1, K,
+                         (int64_t)r, l1p, rp);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      l1s = l1p;
+    }
+    uint16_t* wdt = reinterpret_cast<uint16_t*>(base + L.wd_off);
+    e = launch_dequant_cols(W, tab, wdt, N, stream);
+    if (e != hipSuccess) return e;
+    e = timed(kTimeDxGemm, stream, [&] {
+      return launch_gemm_nt(dY, N, wdt, N, M, K, N, sU, l1s, rp, rp, dX, K, 1.0f, stream);
+    });
+    if (e != hipSuccess) return e;
+  } else if (dX) {
     GemmArgs a = base_args();
     a.M = M; a.N = K; a.K = N; a.k_split = N;
     a.A = dY; a.lda = N;
@@ -540,7 +626,7 @@ hipError_t linear_backward(const NF4View& W, const NF4Table& tab, const uint16_t
   }
   // T = bf16(X L1) unless the caller kept it from the forward pass
   if (!T) {
-    e = lora_down(X, M, K, L1, r, 1.0f, sT, tbuf, part, stream);
+    e = lora_down(X, M, K, L1, r, 1.0f, sT, r, tbuf, part, stream);
     if (e != hipSuccess) return e;
     T = tbuf;
   }
@@ -549,13 +635,13 @@ hipError_t linear_backward(const NF4View& W, const NF4Table& tab, const uint16_t
     GemmArgs a = base_args();
     a.M = K; a.N = r; a.K = M;
     a.A = X; a.lda = K;
-    a.B = sU; a.ldb = r;
+    a.B = sU; a.ldb = ldsu;
     const Split sp = choose_split(cdiv(K, BM) * cdiv(r, BN), M);
     a.k_split = sp.k_split;
     a.C = part; a.ldc = r;
     e = run_gemm<A_COL, B_COL, EPI_F32, false>(a, sp.Z, stream);
     if (e != hipSuccess) return e;
-    e = reduce(part, sp.Z, K * (int64_t)r, 1.0f, dL1, grad_bf16, 0.0f, nullptr, stream);
+    e = reduce(part, sp.Z, K, r, 1.0f, dL1, grad_bf16, r, 0.0f, nullptr, stream);
     if (e != hipSuccess) return e;
   }
   // dL2 = s T^T dY
@@ -569,7 +655,7 @@ hipError_t linear_backward(const NF4View& W, const NF4Table& tab, const uint16_t
     a.C = part; a.ldc = N;
     e = run_gemm<A_COL, B_COL, EPI_F32, false>(a, sp.Z, stream);
     if (e != hipSuccess) return e;
-    e = reduce(part, sp.Z, (int64_t)r * N, s, dL2, grad_bf16, 0.0f, nullptr, stream);
+    e = reduce(part, sp.Z, r, N, s, dL2, grad_bf16, N, 0.0f, nullptr, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -81,16 +81,26 @@ struct NF4View {
 
 // Workspace of the linear layer (shared by forward and backward).
 struct LinearWorkspace {
-  size_t l2t_off;    // bf16 [N][r]   L2 transposed
-  size_t st_off;     // bf16 [M][r]   s * (X L1)
+  size_t l2t_off;    // bf16 [N][rp]  L2 transposed (rp = r rounded up to 64, zero-padded)
+  size_t l1p_off;    // bf16 [K][rp]  L1 zero-padded to rp columns
+  size_t st_off;     // bf16 [M][rp]  s * (X L1)
   size_t t_off;      // bf16 [M][r]   X L1 (when the caller gives no T)
-  size_t su_off;     // bf16 [M][r]   s * (dY L2^T)
+  size_t su_off;     // bf16 [M][rp]  s * (dY L2^T)
   size_t part_off;   // fp32 split-K partials
   size_t part_bytes;
+  size_t wd_off;     // bf16 dequantised weight for the dense GEMM path
+  size_t wd_bytes;
   size_t total;
 };
 
 LinearWorkspace linear_workspace_layout(int64_t M, int64_t K, int64_t N, int r);
+
+hipError_t launch_dequant_rows(const NF4View& W, const NF4Table& tab, uint16_t* out, hipStream_t stream);
+hipError_t launch_dequant_cols(const NF4View& W, const NF4Table& tab, uint16_t* out, int64_t ldo,
+                               hipStream_t stream);
+hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M, int64_t N,
+                          int64_t K, const uint16_t* A2, const uint16_t* B2, int64_t ld2, int64_t K2, uint16_t* C,
+                          int64_t ldc, float alpha, hipStream_t stream);
 
 hipError_t linear_forward(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M,
                           const uint16_t* L1, const uint16_t* L2, int r, float s, uint16_t* Y,
