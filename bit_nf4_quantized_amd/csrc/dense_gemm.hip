@@ -13,17 +13,19 @@
 // through HBM (2.5 B per weight, a few percent of the GEMM time at these
 // shapes) keeps the MFMA loop free of per-weight VALU work.
 //
-// Tiling (one workgroup per 256 x 256 output tile, 256 threads = 4 waves,
-// one wave per SIMD):
-//   * each wave owns a 128 x 128 sub-tile = 4 x 4 v_mfma_f32_32x32x16_bf16
-//     accumulators (256 fp32 registers per lane);
+// Tiling (one workgroup per 256 x 256 output tile, 512 threads = 8 waves,
+// two waves per SIMD so that one wave's MFMAs cover the other's LDS reads):
+//   * each wave owns a 128 x 64 sub-tile = 4 x 2 v_mfma_f32_32x32x16_bf16
+//     accumulators (128 fp32 registers per lane);
 //   * K advances in stages of 64: the A and B stage tiles (2 x 32 KB) are
 //     copied global -> LDS by global_load_lds_dwordx4 (no register staging),
 //     double-buffered (128 KB of the 160 KB LDS), so stage k+1 streams in
 //     while stage k feeds the MFMAs;
 //   * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at
-//     position c ^ (r & 7), so the 16-byte fragment reads of 8 consecutive
-//     rows hit 8 different bank groups;
+//     position c ^ ((r >> 1) & 7): two rows share one 256-byte line of the
+//     64 LDS banks, so the 16-byte fragment reads of 16 consecutive rows hit
+//     16 different bank groups (measured: fewer conflict cycles and faster
+//     than the 8-row swizzle c ^ (r & 7));
 //   * workgroups are numbered so that the 8 XCDs (each with its own L2) get
 //     contiguous blocks of tiles, ordered in groups of 8 tile-rows so that
 //     concurrently running tiles share A rows and B columns.
@@ -41,7 +43,12 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void gbl_void_t;
 
 constexpr int TM = 256, TN = 256, TK = 64;
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int WTN = 64;          // wave sub-tile: 128 rows x 64 columns
+constexpr int NJ = WTN / 32;
+constexpr int RPI = 8;           // rows per wave load instruction (64 lanes x 16 B = 8 rows of 128 B)
+constexpr int IPW = TM / RPI / kWaves;  // load instructions per wave per operand per stage
 constexpr int kStageElems = TM * TK;  // elements per operand per stage (TM == TN)
 
 struct DenseArgs {
@@ -59,24 +66,27 @@ struct DenseArgs {
 };
 
 // One stage of one operand: rows [row0, row0+256) x columns [k0, k0+64).
-// Each wave moves 8 rows per instruction (64 lanes x 16 bytes), 8
+// Each wave moves 8 rows per instruction (64 lanes x 16 bytes), IPW
 // instructions per wave. Lane i of instruction j writes LDS bytes
-// [16 i, 16 i + 16) of the wave's 1 KB slice: row 8(8w+j) + i/8, physical
-// chunk i%8, which holds logical chunk (i%8) ^ (i/8). The address is a
+// [16 i, 16 i + 16) of a 1 KB slice: row 8(IPW w + j) + i/8, physical chunk
+// i%8, which holds logical chunk (i%8) ^ swz(row). The address is a
 // wave-uniform base (matrix + k0, advanced per stage) plus a per-lane 32-bit
 // byte offset that is fixed for the whole K loop.
 struct StageOffsets {
-  uint32_t off[8];
+  uint32_t off[IPW];
 };
+
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 __device__ __forceinline__ StageOffsets stage_offsets(int64_t ld, int64_t row0, int64_t nrows) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane >> 3;
-  const int chunk = (lane & 7) ^ lr;
   StageOffsets o;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    int64_t r = row0 + (wave * 8 + j) * 8 + lr;
+  for (int j = 0; j < IPW; ++j) {
+    const int rloc = (wave * IPW + j) * RPI + lr;
+    const int chunk = (lane & 7) ^ swz(rloc);
+    int64_t r = row0 + rloc;
     if (r > nrows - 1) r = nrows - 1;
     o.off[j] = (uint32_t)((r * ld + chunk * 8) * 2);
   }
@@ -88,13 +98,13 @@ __device__ __forceinline__ void stage_load(const uint16_t* __restrict__ P, int64
   const int wave = threadIdx.x >> 6;
   const char* base = reinterpret_cast<const char*>(P + k0);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int slice = wave * 8 + j;  // 0..31
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + o.off[j]), (lds_void_t*)(lds + slice * 8 * TK), 16, 0, 0);
+  for (int j = 0; j < IPW; ++j) {
+    const int slice = wave * IPW + j;
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + o.off[j]), (lds_void_t*)(lds + slice * RPI * TK), 16, 0, 0);
   }
 }
 
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * TK + ((chunk ^ (row & 7)) << 3); }
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * TK + ((chunk ^ swz(row)) << 3); }
 
 __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(DenseArgs p) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2][2][kStageElems];  // [buffer][A, B]
@@ -116,15 +126,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(DenseArgs p) {
   const int64_t m0 = (int64_t)tm * TM, n0 = (int64_t)tn * TN;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves
   const int nmain = (int)(p.K / TK), nslab = (int)(p.K2 / TK);
   const int nk = nmain + nslab;
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
@@ -153,37 +163,42 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(DenseArgs p) {
 #pragma unroll
     for (int kk = 0; kk < TK / 16; ++kk) {
       const int ch = 2 * kk + (lane >> 5);
-      bf16x8_t a[4], b[4];
+      bf16x8_t a[4], b[NJ];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ra = wm * 128 + i * 32 + (lane & 31);
-        const int rb = wn * 128 + i * 32 + (lane & 31);
         a[i] = *reinterpret_cast<const bf16x8_t*>(As + lds_off(ra, ch));
-        b[i] = *reinterpret_cast<const bf16x8_t*>(Bs + lds_off(rb, ch));
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int rb = wn * WTN + j * 32 + (lane & 31);
+        b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + lds_off(rb, ch));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
   }
 
   // Epilogue through LDS (the stage buffers are free now): each wave writes
-  // half of its 128 x 128 sub-tile (64 rows) as bf16 into its own padded LDS
+  // half of its 128 x 64 sub-tile (64 rows) as bf16 into its own padded LDS
   // slice, then stores it to C in 16-byte row chunks. In a 32x32 accumulator,
   // register v of lane l is row (v%4) + 4(l/32) + 8(v/4), column l%32.
-  constexpr int kEpiStride = 128 + 8;  // padded row (elements): rows r and r+4 land 16 banks apart
+  constexpr int kEpiStride = WTN + 8;  // padded row (elements)
+  constexpr int CPRO = WTN / 8;        // 16-byte chunks per sub-tile row
+  constexpr int RPIT = 64 / CPRO;      // rows stored per iteration
   __syncthreads();
   uint16_t* ep = &smem[0][0][0] + wave * (64 * kEpiStride);
-  const int64_t row_base = m0 + wm * 128, col_base = n0 + wn * 128;
+  const int64_t row_base = m0 + wm * 128, col_base = n0 + wn * WTN;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
       const int i = 2 * h + ii;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < NJ; ++j) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = ii * 32 + (v & 3) + 4 * (lane >> 5) + 8 * (v >> 2);
@@ -194,9 +209,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(DenseArgs p) {
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done (wave-private slice)
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const int r = it * 4 + (lane >> 4);  // 64 rows, 16 lanes per row
-      const int ch = lane & 15;            // 16-byte chunk within the 128-column row
+    for (int it = 0; it < 64 / RPIT; ++it) {
+      const int r = it * RPIT + lane / CPRO;
+      const int ch = lane % CPRO;
       const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ep + r * kEpiStride + ch * 8);
       const int64_t row = row_base + h * 64 + r;
       const int64_t col = col_base + ch * 8;

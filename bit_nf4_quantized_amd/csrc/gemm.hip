@@ -475,6 +475,9 @@ LinearWorkspace linear_workspace_layout(int64_t M, int64_t K, int64_t N, int r) 
   L.st_off = off;  off += align_up((size_t)M * rp * 2, 256);
   L.t_off = off;   off += align_up((size_t)M * r * 2, 256);
   L.su_off = off;  off += align_up((size_t)M * rp * 2, 256);
+  L.l1t_off = off; off += align_up((size_t)64 * K * 2, 256);
+  L.l2p_off = off; off += align_up((size_t)64 * N * 2, 256);
+  if (r <= 64) upd(skinny_partial_bytes(M, K, N));
   L.part_off = off; L.part_bytes = align_up(part, 256); off += L.part_bytes;
   // dense path: the dequantised weight (forward [N][K], backward [K][np])
   L.wd_off = off;
@@ -496,10 +499,32 @@ bool fits_dense(std::initializer_list<int64_t> bytes) {
 
 }  // namespace
 
+// The skinny adapter kernels take rank <= 64 and address the streamed
+// activation with 32-bit offsets.
+static bool skinny_ok(int r, int64_t M, int64_t cols) { return r <= 64 && fits_dense({M * cols * 2}); }
+
+// L1t[j][k] = L1[k][j] for j < r, zero rows for r <= j < 64 (the B operand of
+// the skinny T product).
+static hipError_t make_l1t(const uint16_t* L1, int64_t K, int r, uint16_t* l1t, hipStream_t stream) {
+  if (r < 64) {
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)grid_for((64 - r) * K / 2)), dim3(256), 0, stream,
+                       reinterpret_cast<uint32_t*>(l1t + (int64_t)r * K), (size_t)((64 - r) * K / 2));
+  }
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)cdiv(r, 32), (unsigned)cdiv(K, 32)), dim3(256), 0, stream,
+                     L1, K, (int64_t)r, l1t, K);
+  return hipGetLastError();
+}
+
 // T = X L1 (fp32 split-K partials), then sT = bf16(s T) with row stride ldst
 // (zero-padded columns) and optionally T_out = bf16(T) [M][r].
 static hipError_t lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* L1, int r, float s,
-                            uint16_t* sT, int64_t ldst, uint16_t* T_out, float* part, hipStream_t stream) {
+                            uint16_t* sT, int64_t ldst, uint16_t* T_out, float* part, uint16_t* l1t,
+                            hipStream_t stream) {
+  if (skinny_ok(r, M, K)) {
+    hipError_t e = make_l1t(L1, K, r, l1t, stream);
+    if (e != hipSuccess) return e;
+    return skinny_nt(X, K, l1t, K, M, K, r, part, s, sT, ldst, 1.0f, T_out, stream);
+  }
   GemmArgs a = base_args();
   a.M = M; a.N = r; a.K = K;
   a.A = X; a.lda = K;
@@ -524,15 +549,16 @@ hipError_t linear_forward(const NF4View& W, const NF4Table& tab, const uint16_t*
   uint16_t* sT = reinterpret_cast<uint16_t*>(base + L.st_off);
   float* part = reinterpret_cast<float*>(base + L.part_off);
 
+  uint16_t* l1t = reinterpret_cast<uint16_t*>(base + L.l1t_off);
   if (M <= 16) {
-    hipError_t e = lora_down(X, M, K, L1, r, s, sT, r, T_out, part, stream);
+    hipError_t e = lora_down(X, M, K, L1, r, s, sT, r, T_out, part, l1t, stream);
     if (e != hipSuccess) return e;
     return timed(kTimeGemv, stream, [&] { return launch_gemv(W, tab, X, M, sT, L2, r, Y, stream); });
   }
 
   const bool dense = fits_dense({M * K * 2, N * K * 2, M * rp * 2, N * rp * 2});
   const int64_t ldst = dense ? rp : r;
-  hipError_t e = lora_down(X, M, K, L1, r, s, sT, ldst, T_out, part, stream);
+  hipError_t e = lora_down(X, M, K, L1, r, s, sT, ldst, T_out, part, l1t, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)cdiv(N, 32), (unsigned)cdiv(ldst, 32)), dim3(256), 0,
                      stream, L2, (int64_t)r, N, l2t, ldst);
@@ -583,8 +609,21 @@ hipError_t linear_backward(const NF4View& W, const NF4Table& tab, const uint16_t
   const bool dense = dX && M > 16 && (N % 64) == 0 && fits_dense({M * N * 2, K * N * 2, M * rp * 2, K * rp * 2});
   const int64_t ldsu = dense ? rp : r;
 
+  uint16_t* l1t = reinterpret_cast<uint16_t*>(base + L.l1t_off);
+  uint16_t* l2p = reinterpret_cast<uint16_t*>(base + L.l2p_off);
   // U = dY L2^T -> sU = bf16(s U)
-  {
+  if (skinny_ok(r, M, N) && (N % 64) == 0) {
+    const uint16_t* b = L2;
+    if (r < 64) {  // B operand with 64 rows: L2 then zero rows
+      hipLaunchKernelGGL(pad_cols_kernel, dim3((unsigned)grid_for(64 * N)), dim3(256), 0, stream, L2, (int64_t)1,
+                         (int64_t)r * N, l2p, (int64_t)64 * N);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      b = l2p;
+    }
+    e = skinny_nt(dY, N, b, N, M, N, r, part, s, sU, ldsu, 0.0f, nullptr, stream);
+    if (e != hipSuccess) return e;
+  } else {
     GemmArgs a = base_args();
     a.M = M; a.N = r; a.K = N;
     a.A = dY; a.lda = N;
@@ -626,9 +665,15 @@ hipError_t linear_backward(const NF4View& W, const NF4Table& tab, const uint16_t
   }
   // T = bf16(X L1) unless the caller kept it from the forward pass
   if (!T) {
-    e = lora_down(X, M, K, L1, r, 1.0f, sT, r, tbuf, part, stream);
+    e = lora_down(X, M, K, L1, r, 1.0f, tbuf, r, nullptr, part, l1t, stream);
     if (e != hipSuccess) return e;
     T = tbuf;
+  }
+  if (skinny_ok(r, M, K) && skinny_ok(r, M, N)) {
+    // dL1 = X^T sU  ([K][r]);  dL2 = s (dY^T T)^T  ([r][N])
+    e = skinny_tn(X, K, K, sU, ldsu, M, r, part, 1.0f, false, grad_bf16, dL1, stream);
+    if (e != hipSuccess) return e;
+    return skinny_tn(dY, N, N, T, r, M, r, part, s, true, grad_bf16, dL2, stream);
   }
   // dL1 = X^T sU
   {

@@ -79,6 +79,19 @@ struct NF4View {
   int64_t rows, cols;  // stored [rows][cols]
 };
 
+// Skinny adapter products (rank <= 64), skinny_gemm.hip.
+struct SkinnySplit {
+  int Z;        // reduction slices
+  int64_t len;  // reduction length per slice (multiple of 64)
+};
+SkinnySplit skinny_split(int64_t tiles, int64_t klen);
+size_t skinny_partial_bytes(int64_t M, int64_t K, int64_t N);
+hipError_t skinny_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M, int64_t K, int r,
+                     float* part, float alpha, uint16_t* out, int64_t ldo, float alpha2, uint16_t* out2,
+                     hipStream_t stream);
+hipError_t skinny_tn(const uint16_t* L, int64_t ldl, int64_t W, const uint16_t* S, int64_t lds, int64_t M, int r,
+                     float* part, float alpha, bool transpose, bool out_bf16, void* out, hipStream_t stream);
+
 // Workspace of the linear layer (shared by forward and backward).
 struct LinearWorkspace {
   size_t l2t_off;    // bf16 [N][rp]  L2 transposed (rp = r rounded up to 64, zero-padded)
@@ -86,6 +99,8 @@ struct LinearWorkspace {
   size_t st_off;     // bf16 [M][rp]  s * (X L1)
   size_t t_off;      // bf16 [M][r]   X L1 (when the caller gives no T)
   size_t su_off;     // bf16 [M][rp]  s * (dY L2^T)
+  size_t l1t_off;    // bf16 [64][K]  L1 transposed, rows >= r zero (skinny path)
+  size_t l2p_off;    // bf16 [64][N]  L2 with rows >= r zero (skinny path, r < 64)
   size_t part_off;   // fp32 split-K partials
   size_t part_bytes;
   size_t wd_off;     // bf16 dequantised weight for the dense GEMM path

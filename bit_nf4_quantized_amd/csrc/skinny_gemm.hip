@@ -1,0 +1,329 @@
+// Skinny adapter products of the QLoRA linear on gfx950 (rank r <= 64):
+//
+//   forward   T   = X L1           [M][r]   (reduction over K)
+//   backward  U   = dY L2^T        [M][r]   (reduction over N)
+//             dL1 = s X^T U        [K][r]   (reduction over the M tokens)
+//             dL2 = s (X L1)^T dY  [r][N]   (reduction over the M tokens)
+//
+// (QLoRA pages, diycv.top, section 问题背景 LoRA equation and section
+// 关键公式.) Each product reads one large activation (X or dY, 64-180 MB at
+// 8192 tokens) once and a small rank-r operand, so it is HBM-bound; the
+// kernels stream the large operand with coalesced 16-byte loads, keep the
+// whole rank dimension (padded to 64) in one tile, and use
+// v_mfma_f32_32x32x16_bf16 for the products. The reduction is split over
+// blockIdx.z into fp32 partials that splitk_reduce_kernel sums in a fixed
+// order, so results are deterministic.
+//
+// skinny_nt_kernel:  C[z][m][j] = sum_{k in slice z} A[m][k] B[j][k]
+//   A [M][K] and B [64][K] (rows j >= r are zero) are both K-contiguous and
+//   are copied global -> LDS by global_load_lds_dwordx4; 128 rows x 64 j per
+//   workgroup, 4 waves of 32 rows, K-stages of 64, 3-stage ring.
+// skinny_tn_kernel:  C[z][c][j] = sum_{m in slice z} L[m][c] S[m][j]
+//   the reduction runs down the rows of both operands, so each thread loads
+//   two rows x 8 columns and writes them to LDS transposed as (m, m+1)
+//   pairs; 128 columns c x 64 j per workgroup, M-stages of 64.
+#include "common.h"
+#include "launch.h"
+
+namespace qlora {
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void gbl_void_t;
+
+constexpr int SK = 64;     // reduction per stage (elements)
+constexpr int SJ = 64;     // rank columns per tile (r padded)
+constexpr int SM = 128;    // large-operand rows (nt) or columns (tn) per tile
+constexpr int kSkThreads = 256;
+
+// 16-byte chunk c of LDS row `row` lives at c ^ sk_swz(row): (row >> 1) keeps
+// the fragment reads of 16 consecutive rows on distinct bank groups, and
+// (row >> 4) separates the rows that 8 neighbouring threads write at the
+// same reduction index when a tile is transposed into LDS.
+__device__ __forceinline__ int sk_swz(int row) { return ((row >> 1) ^ (row >> 4)) & 7; }
+__device__ __forceinline__ int sk_off(int row, int chunk) { return row * SK + ((chunk ^ sk_swz(row)) << 3); }
+
+// ---- NT: both operands contiguous in the reduction -----------------------------
+
+constexpr int kNtStages = 3;
+
+struct NtArgs {
+  const uint16_t* A;  // [M][lda]
+  const uint16_t* B;  // [SJ][ldb]  (64 rows; rows >= r zero)
+  float* C;           // [Z][M][SJ]
+  int64_t lda, ldb, M, K, k_split;
+};
+
+__global__ __launch_bounds__(kSkThreads) void skinny_nt_kernel(NtArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t sA[kNtStages][SM * SK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB[kNtStages][SJ * SK];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t m0 = (int64_t)blockIdx.x * SM;
+  const int64_t kz0 = (int64_t)blockIdx.z * p.k_split;
+  const int64_t kz1 = (kz0 + p.k_split < p.K) ? kz0 + p.k_split : p.K;
+  const int nk = kz0 < kz1 ? (int)((kz1 - kz0) / SK) : 0;
+
+  // per-lane 32-bit offsets of the direct-to-LDS copies (8 rows x 128 B per instruction)
+  const int lr = lane >> 3;
+  uint32_t offA[4], offB[2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // A: 128 rows = 16 instructions, 4 per wave
+    const int rloc = (wave * 4 + j) * 8 + lr;
+    int64_t r = m0 + rloc;
+    if (r > p.M - 1) r = p.M - 1;
+    offA[j] = (uint32_t)((r * p.lda + (((lane & 7) ^ sk_swz(rloc)) * 8)) * 2);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {  // B: 64 rows = 8 instructions, 2 per wave
+    const int rloc = (wave * 2 + j) * 8 + lr;
+    offB[j] = (uint32_t)((rloc * p.ldb + (((lane & 7) ^ sk_swz(rloc)) * 8)) * 2);
+  }
+  auto issue = [&](int st, int buf) {
+    const int64_t k0 = kz0 + (int64_t)st * SK;
+    const char* a = reinterpret_cast<const char*>(p.A + k0);
+    const char* b = reinterpret_cast<const char*>(p.B + k0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(a + offA[j]), (lds_void_t*)(sA[buf] + (wave * 4 + j) * 8 * SK),
+                                       16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(b + offB[j]), (lds_void_t*)(sB[buf] + (wave * 2 + j) * 8 * SK),
+                                       16, 0, 0);
+  };
+
+  f32x16_t acc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[t][v] = 0.0f;
+
+#pragma unroll
+  for (int s = 0; s < kNtStages - 1; ++s)
+    if (s < nk) issue(s, s);
+  for (int st = 0; st < nk; ++st) {
+    const int buf = st % kNtStages;
+    if (st + 1 < nk) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");  // stage st+1 (6 loads) may stay in flight
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (st + kNtStages - 1 < nk) issue(st + kNtStages - 1, (st + kNtStages - 1) % kNtStages);
+#pragma unroll
+    for (int kk = 0; kk < SK / 16; ++kk) {
+      const int ch = 2 * kk + (lane >> 5);
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(sA[buf] + sk_off(wave * 32 + (lane & 31), ch));
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(sB[buf] + sk_off(t * 32 + (lane & 31), ch));
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[t], 0, 0, 0);
+      }
+    }
+  }
+  // C[z][m][j]: lane l, register v -> row (v%4) + 4(l/32) + 8(v/4), column l%32
+  float* Cz = p.C + (int64_t)blockIdx.z * p.M * SJ;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int j = t * 32 + (lane & 31);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t m = m0 + wave * 32 + (v & 3) + 4 * (lane >> 5) + 8 * (v >> 2);
+      if (m < p.M) Cz[m * SJ + j] = acc[t][v];
+    }
+  }
+}
+
+// ---- TN: both operands run the reduction down their rows ----------------------------
+
+struct TnArgs {
+  const uint16_t* L;  // [M][ldl]  large operand (X or dY)
+  const uint16_t* S;  // [M][lds]  small operand (U or T), r columns valid
+  float* C;           // [Z][W][SJ]
+  int64_t ldl, lds, M, W, r, m_split;
+};
+
+__global__ __launch_bounds__(kSkThreads) void skinny_tn_kernel(TnArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t sL[SM * SK];  // [c][m]
+  __shared__ __attribute__((aligned(1024))) uint16_t sS[SJ * SK];  // [j][m]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * SM;
+  const int64_t mz0 = (int64_t)blockIdx.z * p.m_split;
+  const int64_t mz1 = (mz0 + p.m_split < p.M) ? mz0 + p.m_split : p.M;
+
+  // staging roles: L tile = 64 rows x 128 columns -> thread: row pair rp, two 8-column chunks
+  const int l_cq = tid & 7, l_rp = tid >> 3;              // 8 threads per row pair, 32 row pairs
+  // S tile = 64 rows x 64 columns -> thread: row pair, one 8-column chunk (first 256 threads)
+  const int s_cq = tid & 7, s_rp = tid >> 3;
+
+  f32x16_t acc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[t][v] = 0.0f;
+
+  u32x4_t lv[2][2], sv[2];
+  auto load = [&](int64_t ms) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t m = ms + 2 * l_rp + h;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int64_t c = c0 + (l_cq * 2 + q) * 8;
+        lv[h][q] = (m < mz1 && c < p.W) ? *reinterpret_cast<const u32x4_t*>(p.L + m * p.ldl + c)
+                                        : u32x4_t{0, 0, 0, 0};
+      }
+      const int64_t cs = s_cq * 8;
+      sv[h] = (m < mz1 && cs < p.r) ? *reinterpret_cast<const u32x4_t*>(p.S + m * p.lds + cs) : u32x4_t{0, 0, 0, 0};
+    }
+  };
+  // write (m, m+1) pairs of column c as one dword at [c][m]
+  auto put_pairs = [&](uint16_t* T, int cbase, const u32x4_t& r0, const u32x4_t& r1, int mloc) {
+    const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
+    const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t a = (e & 1) ? (w0[e >> 1] >> 16) : (w0[e >> 1] & 0xFFFFu);
+      const uint32_t b = (e & 1) ? (w1[e >> 1] >> 16) : (w1[e >> 1] & 0xFFFFu);
+      const int row = cbase + e;
+      *reinterpret_cast<uint32_t*>(T + sk_off(row, mloc >> 3) + (mloc & 7)) = a | (b << 16);
+    }
+  };
+
+  if (mz0 < mz1) load(mz0);
+  for (int64_t ms = mz0; ms < mz1; ms += SK) {
+    __syncthreads();  // previous stage's fragment reads are done
+    const int mloc = 2 * l_rp;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) put_pairs(sL, (l_cq * 2 + q) * 8, lv[0][q], lv[1][q], mloc);
+    put_pairs(sS, s_cq * 8, sv[0], sv[1], 2 * s_rp);
+    __syncthreads();
+    if (ms + SK < mz1) load(ms + SK);  // next stage's global loads overlap the MFMAs
+#pragma unroll
+    for (int kk = 0; kk < SK / 16; ++kk) {
+      const int ch = 2 * kk + (lane >> 5);
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(sL + sk_off(wave * 32 + (lane & 31), ch));
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(sS + sk_off(t * 32 + (lane & 31), ch));
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[t], 0, 0, 0);
+      }
+    }
+  }
+  float* Cz = p.C + (int64_t)blockIdx.z * p.W * SJ;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int j = t * 32 + (lane & 31);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t c = c0 + wave * 32 + (v & 3) + 4 * (lane >> 5) + 8 * (v >> 2);
+      if (c < p.W) Cz[c * SJ + j] = acc[t][v];
+    }
+  }
+}
+
+// out = alpha * sum_z P[z] over a [rows][SJ] slab, columns j < r:
+//   mode 0: out[m][j] (row stride ldo; columns [r, ldo) zero) in bf16, plus
+//           optional out2[m][j] = bf16(alpha2 * sum) with row stride r
+//   mode 1: out[m][j] fp32 or bf16, row stride r
+//   mode 2: transposed, out[j][m] fp32 or bf16, row stride rows
+__global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ P, int Z, int64_t rows, int r,
+                                                            float alpha, int mode, int out_bf16, void* __restrict__ out,
+                                                            int64_t ldo, float alpha2, uint16_t* __restrict__ out2) {
+  const int64_t width = (mode == 0) ? ldo : r;
+  const int64_t total = rows * width;
+  const int64_t slab = rows * SJ;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int64_t m, j;
+    if (mode == 2) {  // iterate in output order: i = j * rows + m
+      j = i / rows;
+      m = i - j * rows;
+    } else {
+      m = i / width;
+      j = i - m * width;
+    }
+    if (j >= r) {
+      static_cast<uint16_t*>(out)[i] = 0;
+      continue;
+    }
+    float acc = 0.0f;
+    for (int z = 0; z < Z; ++z) acc += P[(int64_t)z * slab + m * SJ + j];
+    const float v = alpha * acc;
+    if (out_bf16) static_cast<uint16_t*>(out)[i] = f32_to_bf16(v);
+    else static_cast<float*>(out)[i] = v;
+    if (mode == 0 && out2) out2[m * r + j] = f32_to_bf16(alpha2 * acc);
+  }
+}
+
+int64_t sk_cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int64_t sk_grid(int64_t total) {
+  int64_t b = sk_cdiv(total, 256);
+  if (b > 8192) b = 8192;
+  return b < 1 ? 1 : b;
+}
+
+}  // namespace
+
+// Number of reduction slices for a skinny product with `tiles` output tiles
+// over a reduction of length klen (multiples of 64), so that about 512
+// workgroups stream the large operand.
+SkinnySplit skinny_split(int64_t tiles, int64_t klen) {
+  const int64_t steps = sk_cdiv(klen, SK);
+  if (steps < 1) return SkinnySplit{1, SK};
+  int64_t z = sk_cdiv(512, tiles < 1 ? 1 : tiles);
+  if (z > 32) z = 32;
+  if (z > steps) z = steps;
+  if (z < 1) z = 1;
+  const int64_t per = sk_cdiv(steps, z);
+  SkinnySplit s;
+  s.len = per * SK;
+  s.Z = (int)sk_cdiv(steps, per);
+  if (s.Z < 1) s.Z = 1;
+  return s;
+}
+
+size_t skinny_partial_bytes(int64_t M, int64_t K, int64_t N) {
+  const SkinnySplit a = skinny_split(sk_cdiv(M, SM), K);
+  const SkinnySplit b = skinny_split(sk_cdiv(M, SM), N);
+  const SkinnySplit c = skinny_split(sk_cdiv(K, SM), M);
+  const SkinnySplit d = skinny_split(sk_cdiv(N, SM), M);
+  size_t m = (size_t)a.Z * M;
+  if ((size_t)b.Z * M > m) m = (size_t)b.Z * M;
+  if ((size_t)c.Z * K > m) m = (size_t)c.Z * K;
+  if ((size_t)d.Z * N > m) m = (size_t)d.Z * N;
+  return m * SJ * sizeof(float);
+}
+
+// C = A B^T over K with B [64][ldb] (rows >= r zero), then reduce.
+hipError_t skinny_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M, int64_t K, int r,
+                     float* part, float alpha, uint16_t* out, int64_t ldo, float alpha2, uint16_t* out2,
+                     hipStream_t stream) {
+  const SkinnySplit sp = skinny_split(sk_cdiv(M, SM), K);
+  NtArgs a;
+  a.A = A; a.B = B; a.C = part; a.lda = lda; a.ldb = ldb; a.M = M; a.K = K; a.k_split = sp.len;
+  hipLaunchKernelGGL(skinny_nt_kernel, dim3((unsigned)sk_cdiv(M, SM), 1, (unsigned)sp.Z), dim3(kSkThreads), 0, stream,
+                     a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)sk_grid(M * ldo)), dim3(256), 0, stream, part, sp.Z, M, r,
+                     alpha, 0, 1, (void*)out, ldo, alpha2, out2);
+  return hipGetLastError();
+}
+
+// C[c][j] = sum_m L[m][c] S[m][j], then reduce to out (transposed if `transpose`).
+hipError_t skinny_tn(const uint16_t* L, int64_t ldl, int64_t W, const uint16_t* S, int64_t lds, int64_t M, int r,
+                     float* part, float alpha, bool transpose, bool out_bf16, void* out, hipStream_t stream) {
+  const SkinnySplit sp = skinny_split(sk_cdiv(W, SM), M);
+  TnArgs a;
+  a.L = L; a.S = S; a.C = part; a.ldl = ldl; a.lds = lds; a.M = M; a.W = W; a.r = r; a.m_split = sp.len;
+  hipLaunchKernelGGL(skinny_tn_kernel, dim3((unsigned)sk_cdiv(W, SM), 1, (unsigned)sp.Z), dim3(kSkThreads), 0, stream,
+                     a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)sk_grid(W * (int64_t)r)), dim3(256), 0, stream, part, sp.Z,
+                     W, r, alpha, transpose ? 2 : 1, out_bf16 ? 1 : 0, out, (int64_t)r, 0.0f, (uint16_t*)nullptr);
+  return hipGetLastError();
+}
+
+}  // namespace qlora
