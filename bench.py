@@ -14,14 +14,19 @@ value = algorithmic fwd+bwd flops per step / time per step, with flops
 weight gradient; dequantisation is not counted).
 
 The same run also measures:
-  * roofline of the dominant fused dequant-GEMM kernel, from HIP events that
-    the library records around each of its launches on the call's stream;
+  * roofline of the dominant kernel, the bf16 MFMA GEMM (gemm_nt_kernel) that
+    computes both Y = X Wd^T + (s X L1) L2 and dX = dY Wd + (s dY L2^T) L1^T,
+    from HIP events that the library records around each of its launches on
+    the call's stream; its HBM traffic comes from rocprofv3 FETCH_SIZE /
+    WRITE_SIZE counters stored under profiles/ (scaled by the same counters
+    on a plain device copy, see --copy-probe) and is reported only while the
+    kernel source still has the hash recorded with them;
   * the small-M dequant-GEMV (M in {1, 4, 16}; 4096->11008 and 11008->4096)
     in GB/s against 8 TB/s, cycling >= 24 distinct weight copies (> 512 MB)
     so the 256 MB last-level cache cannot serve the weights;
   * NF4 + DQ quantisation throughput on a LLaMA-65B-shaped tensor;
-  * the CPU oracle on a bounded sample (all 7 linears, 512 of the 8192
-    tokens) as a baseline.
+  * the CPU oracle on the same step (all 7 linears, 8192 tokens) as a
+    baseline.
 Prints one JSON line.
 """
 
@@ -39,6 +44,8 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+GEMM_SOURCE = os.path.join(ROOT, "bit_nf4_quantized_amd", "csrc", "dense_gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_nt_llama7b-layer_hbm-traffic.md")
 
 
 def log(msg):
@@ -91,6 +98,42 @@ def run_step(api, layers, ws):
         api.qlora_linear_fwd(d["q"], d["X"], d["L1"], d["L2"], d["s"], Y=d["Y"], T_out=d["T"], workspace=ws)
         api.qlora_linear_bwd(d["q"], d["X"], d["dY"], d["L1"], d["L2"], d["s"], T=d["T"], dX=d["dX"],
                              dL1=d["dL1"], dL2=d["dL2"], workspace=ws)
+
+
+def gemm_traffic():
+    """HBM bytes per gemm_nt_kernel launch from the stored counter summary, or
+    None when it is absent or was taken on a different kernel source."""
+    import hashlib
+
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel source sha256") != src:
+        return None
+    try:
+        return float(fields["bytes per launch (scaled)"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(nbytes=1 << 30, reps=5):
+    """A plain device-to-device copy of known size, for scaling the HBM byte
+    counters (run it under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)."""
+    import torch
+
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": nbytes, "reps": reps}), flush=True)
 
 
 def kernel_summary(durs_ms, flops):
@@ -178,7 +221,7 @@ def bench_quantize(api, workloads, reps=5):
     return res
 
 
-def cpu_baseline(host, tokens=2048):
+def cpu_baseline(host, tokens=8192):
     """The oracle (dequant + forward + backward) on all 7 linears for a sample
     of the tokens, on the host cores; reported in the same unit."""
     import numpy as np
@@ -202,7 +245,7 @@ def cpu_baseline(host, tokens=2048):
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "seconds": dt,
-            "sample": f"all 7 linears, first {tokens} of 8192 tokens: float64 NumPy dequant + fwd + bwd "
+            "sample": f"all 7 linears, {tokens} of 8192 tokens: float64 NumPy dequant + fwd + bwd "
                       f"(BLAS threads = cores; elementwise steps single-threaded)"}
 
 
@@ -214,6 +257,8 @@ def main():
     ap.add_argument("--workload", default="llama7b-layer", choices=["llama7b-layer", "llama33b-layer"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the GEMV and quantize sections")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a 1 GiB device copy (calibration of the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -228,6 +273,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe()
+        return
     api.library()
     name = args.workload
     layers, host, ws = setup_layer(api, workloads, name)
@@ -255,16 +303,19 @@ def main():
     value = flops_step / (ms_step * 1e-3) / 1e12
     log(f"step {ms_step:.3f} ms, {value:.1f} TFLOP/s (wall {wall / args.steps * 1e3:.3f} ms/step)")
 
-    kf = kernel_summary(t_fwd.durations_ms(), fwd_flops * args.steps)
-    kd = kernel_summary(t_dx.durations_ms(), dx_flops * args.steps)
-    dom_name, dom = ("fwd_gemm", kf) if kf["total_ms"] >= kd["total_ms"] else ("dx_gemm", kd)
+    dfwd, ddx = t_fwd.durations_ms(), t_dx.durations_ms()
+    kf = kernel_summary(dfwd, fwd_flops * args.steps)
+    kd = kernel_summary(ddx, dx_flops * args.steps)
+    kg = kernel_summary(dfwd + ddx, fwd_flops * args.steps + dx_flops * args.steps)
     log(f"fwd GEMM {kf['tflops']:.1f} TFLOP/s avg {kf['avg_ms']:.3f} ms; "
         f"dX GEMM {kd['tflops']:.1f} TFLOP/s avg {kd['avg_ms']:.3f} ms")
-    roofline = {"bound": "mfma", "achieved": dom["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": dom["tflops"] / PEAK_BF16_TFLOPS, "traffic": None,
-                "kernel": {"fwd_gemm": "gemm_kernel<A_ROW,B_NF4,EPI_BF16,slab>",
-                           "dx_gemm": "gemm_kernel<A_ROW,B_NF4T,EPI_BF16,slab>"}[dom_name],
-                "avg_launch_ms": dom["avg_ms"], "launches": dom["launches"]}
+    # gemm_nt_kernel runs both products (one launch each per linear): its
+    # algorithmic flops per launch averaged over the 14 launches of a step,
+    # over its average launch duration.
+    roofline = {"bound": "mfma", "achieved": kg["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": kg["tflops"] / PEAK_BF16_TFLOPS, "traffic": gemm_traffic(),
+                "kernel": "gemm_nt_kernel", "avg_launch_ms": kg["avg_ms"], "launches": kg["launches"],
+                "flops_per_launch": (sum(fwd_flops) + sum(dx_flops)) / (2 * len(layers))}
 
     shp_desc = ", ".join(f"{d['shape'].name} {d['shape'].K}->{d['shape'].N}" for d in layers)
     result = {

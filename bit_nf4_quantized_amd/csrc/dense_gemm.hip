@@ -14,13 +14,22 @@
 // shapes) keeps the MFMA loop free of per-weight VALU work.
 //
 // Tiling (one workgroup per 256 x 256 output tile, 512 threads = 8 waves,
-// two waves per SIMD so that one wave's MFMAs cover the other's LDS reads):
+// two waves per SIMD):
 //   * each wave owns a 128 x 64 sub-tile = 4 x 2 v_mfma_f32_32x32x16_bf16
 //     accumulators (128 fp32 registers per lane);
 //   * K advances in stages of 64: the A and B stage tiles (2 x 32 KB) are
 //     copied global -> LDS by global_load_lds_dwordx4 (no register staging),
-//     double-buffered (128 KB of the 160 KB LDS), so stage k+1 streams in
-//     while stage k feeds the MFMAs;
+//     double-buffered (128 KB of the 160 KB LDS);
+//   * software pipeline: the fragments of k-step kk+1 are read from LDS into
+//     a second register set while the 8 MFMAs of k-step kk run; the stage
+//     barrier sits before the last k-step, so the first fragments of the
+//     next stage are read, and the copy of stage st+2 into the buffer just
+//     consumed is started, while those MFMAs run;
+//   * the LDS copies are issued from inline assembly: with the compiler
+//     builtin for them, the generated code waited for all fragment reads
+//     (lgkmcnt(0)) and for the in-flight copy of the next stage (vmcnt(0))
+//     before MFMA groups, which serialises the pipeline. The kernel places
+//     the copy waits itself (vmcnt before each stage barrier);
 //   * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at
 //     position c ^ ((r >> 1) & 7): two rows share one 256-byte line of the
 //     64 LDS banks, so the 16-byte fragment reads of 16 consecutive rows hit
@@ -45,7 +54,10 @@ typedef const __attribute__((address_space(1))) void gbl_void_t;
 constexpr int TM = 256, TN = 256, TK = 64;
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int WTN = 64;          // wave sub-tile: 128 rows x 64 columns
+constexpr int WGN = 4;           // waves along N (2 along M)
+constexpr int WTM = 128;         // wave sub-tile: 128 rows x 64 columns
+constexpr int WTN = 64;
+constexpr int MI = WTM / 32;
 constexpr int NJ = WTN / 32;
 constexpr int RPI = 8;           // rows per wave load instruction (64 lanes x 16 B = 8 rows of 128 B)
 constexpr int IPW = TM / RPI / kWaves;  // load instructions per wave per operand per stage
@@ -93,14 +105,19 @@ __device__ __forceinline__ StageOffsets stage_offsets(int64_t ld, int64_t row0, 
   return o;
 }
 
-__device__ __forceinline__ void stage_load(const uint16_t* __restrict__ P, int64_t k0, const StageOffsets& o,
-                                           uint16_t* lds) {
-  const int wave = threadIdx.x >> 6;
-  const char* base = reinterpret_cast<const char*>(P + k0);
+// Issues IPW global_load_lds_dwordx4 (global address = uniform base in
+// SGPRs + per-lane 32-bit offset; LDS address = M0 + 16 * lane). The copies
+// are not visible to the compiler: the caller waits for them with an
+// explicit vmcnt before the barrier that publishes the stage.
+__device__ __forceinline__ void stage_load(const uint16_t* __restrict__ P, const StageOffsets& o, uint16_t* lds) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const char* base = reinterpret_cast<const char*>(P);
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
     const int slice = wave * IPW + j;
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + o.off[j]), (lds_void_t*)(lds + slice * RPI * TK), 16, 0, 0);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)(lds + slice * RPI * TK));
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(o.off[j]), "s"(base), "s"(m0) : "memory", "m0");
   }
 }
 
@@ -126,13 +143,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(DenseArgs p) {
   const int64_t m0 = (int64_t)tm * TM, n0 = (int64_t)tn * TN;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 2, wn = wave & 3;  // 2 x 4 waves
+  const int wm = wave / WGN, wn = wave % WGN;
   const int nmain = (int)(p.K / TK), nslab = (int)(p.K2 / TK);
   const int nk = nmain + nslab;
 
-  f32x16_t acc[4][NJ];
+  f32x16_t acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
@@ -140,47 +157,80 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(DenseArgs p) {
 
   const StageOffsets offA = stage_offsets(p.lda, m0, p.M);
   const StageOffsets offB = stage_offsets(p.ldb, n0, p.N);
+  const StageOffsets offA2 = stage_offsets(p.ld2, m0, p.M);
+  const StageOffsets offB2 = stage_offsets(p.ld2, n0, p.N);
+  // Stage st covers columns [64 st, 64 st + 64) of (A, B) for st < nmain,
+  // then the slab (A2, B2). Operand selection is branch-free so that the
+  // copy can be scheduled among the MFMAs of the same block.
   auto issue = [&](int st, int buf) {
-    if (st < nmain) {
-      const int64_t k0 = (int64_t)st * TK;
-      stage_load(p.A, k0, offA, smem[buf][0]);
-      stage_load(p.B, k0, offB, smem[buf][1]);
-    } else {
-      const int64_t k0 = (int64_t)(st - nmain) * TK;
-      stage_load(p.A2, k0, stage_offsets(p.ld2, m0, p.M), smem[buf][0]);
-      stage_load(p.B2, k0, stage_offsets(p.ld2, n0, p.N), smem[buf][1]);
+    const bool slab = st >= nmain;
+    const int64_t k0 = (int64_t)(slab ? st - nmain : st) * TK;
+    StageOffsets oa, ob;
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      oa.off[j] = slab ? offA2.off[j] : offA.off[j];
+      ob.off[j] = slab ? offB2.off[j] : offB.off[j];
     }
+    stage_load((slab ? p.A2 : p.A) + k0, oa, smem[buf][0]);
+    stage_load((slab ? p.B2 : p.B) + k0, ob, smem[buf][1]);
   };
-
-  if (nk > 0) issue(0, 0);
-  for (int st = 0; st < nk; ++st) {
-    const int buf = st & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (st + 1 < nk) issue(st + 1, buf ^ 1);
+  bf16x8_t fa[2][MI], fb[2][NJ];  // two register sets of k-step fragments
+  auto frag = [&](int buf, int kk, int set) {
     const uint16_t* As = smem[buf][0];
     const uint16_t* Bs = smem[buf][1];
+    const int ch = 2 * kk + (lane >> 5);
 #pragma unroll
-    for (int kk = 0; kk < TK / 16; ++kk) {
-      const int ch = 2 * kk + (lane >> 5);
-      bf16x8_t a[4], b[NJ];
+    for (int i = 0; i < MI; ++i)
+      fa[set][i] = *reinterpret_cast<const bf16x8_t*>(As + lds_off(wm * WTM + i * 32 + (lane & 31), ch));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ra = wm * 128 + i * 32 + (lane & 31);
-        a[i] = *reinterpret_cast<const bf16x8_t*>(As + lds_off(ra, ch));
-      }
+    for (int j = 0; j < NJ; ++j)
+      fb[set][j] = *reinterpret_cast<const bf16x8_t*>(Bs + lds_off(wn * WTN + j * 32 + (lane & 31), ch));
+  };
+  auto mma = [&](int set) {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int rb = wn * WTN + j * 32 + (lane & 31);
-        b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + lds_off(rb, ch));
-      }
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+  };
+  // scheduling hint: the reads of the next k-step first, then this k-step's MFMAs
+  auto order = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, MI + NJ, 0);  // DS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, MI * NJ, 0);  // MFMAs
+  };
+  // One stage; on entry the fragments of its k-step 0 are in set 0 and the
+  // next stage's copy was started one stage earlier.
+  auto stage = [&](int st, bool refill, bool next) {
+    const int buf = st & 1;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int kk = 0; kk < TK / 16 - 1; ++kk) {
+      frag(buf, kk + 1, (kk + 1) & 1);
+      mma(kk & 1);
+      order();
     }
+    // every read of buf by this wave has been issued; the barrier's release
+    // fence completes them, vmcnt(0) completes this wave's copy of stage st+1
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    if (next) frag(buf ^ 1, 0, 0);
+    if (refill) issue(st + 2, buf);
+    mma(1);
+    order();
+  };
+  if (nk > 0) issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  if (nk > 0) {
+    if (nk > 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * IPW) : "memory");  // stage 0 landed
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    frag(0, 0, 0);
   }
+  int st = 0;
+  for (; st + 2 < nk; ++st) stage(st, true, true);
+  if (st + 1 < nk) stage(st++, false, true);
+  if (st < nk) stage(st, false, false);
 
   // Epilogue through LDS (the stage buffers are free now): each wave writes
   // half of its 128 x 64 sub-tile (64 rows) as bf16 into its own padded LDS
@@ -191,9 +241,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(DenseArgs p) {
   constexpr int RPIT = 64 / CPRO;      // rows stored per iteration
   __syncthreads();
   uint16_t* ep = &smem[0][0][0] + wave * (64 * kEpiStride);
-  const int64_t row_base = m0 + wm * 128, col_base = n0 + wn * WTN;
+  const int64_t row_base = m0 + wm * WTM, col_base = n0 + wn * WTN;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < MI / 2; ++h) {
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
       const int i = 2 * h + ii;
