@@ -451,6 +451,9 @@ GemmArgs base_args() {
 
 }  // namespace
 
+size_t small_t_partial_bytes(int64_t M, int64_t K, int r);
+hipError_t launch_small_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* L1, int r, float s,
+                                  uint16_t* sT, int64_t ldst, uint16_t* T_out, float* part, hipStream_t stream);
 hipError_t launch_gemv(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M,
                        const uint16_t* sT, const uint16_t* L2, int r, uint16_t* Y, hipStream_t stream);
 
@@ -478,6 +481,7 @@ LinearWorkspace linear_workspace_layout(int64_t M, int64_t K, int64_t N, int r) 
   L.l1t_off = off; off += align_up((size_t)64 * K * 2, 256);
   L.l2p_off = off; off += align_up((size_t)64 * N * 2, 256);
   if (r <= 64) upd(skinny_partial_bytes(M, K, N));
+  if (M <= 16) upd(small_t_partial_bytes(M, K, r));
   L.part_off = off; L.part_bytes = align_up(part, 256); off += L.part_bytes;
   // dense path: the dequantised weight (forward [N][K], backward [K][np])
   L.wd_off = off;
@@ -551,7 +555,7 @@ hipError_t linear_forward(const NF4View& W, const NF4Table& tab, const uint16_t*
 
   uint16_t* l1t = reinterpret_cast<uint16_t*>(base + L.l1t_off);
   if (M <= 16) {
-    hipError_t e = lora_down(X, M, K, L1, r, s, sT, r, T_out, part, l1t, stream);
+    hipError_t e = launch_small_lora_down(X, M, K, L1, r, s, sT, r, T_out, part, stream);
     if (e != hipSuccess) return e;
     return timed(kTimeGemv, stream, [&] { return launch_gemv(W, tab, X, M, sT, L2, r, Y, stream); });
   }

@@ -3,11 +3,24 @@
 // (QLoRA pages, diycv.top, section 关键公式; inference keeps the 4-bit base
 // and the trained adapters, section 训练与推理流程 "推理").
 //
-// The weight is read once and is the only large stream, so the kernel is
-// HBM-bound: each wave owns one weight row n and its 64 lanes stream that
-// row's packed codes in 16-byte pieces (32 weights, half a 64-block, per
-// lane per step), dequantise them exactly as the standalone dequant does
-// (bf16(RN32(q[code] * a'))), and accumulate the M dot products in fp32.
+// The packed weight is the only large stream (0.52 B per weight), so these
+// kernels are HBM- and latency-bound. Shared by both kernels below:
+//   * one workgroup per 16 weight rows; the K axis is cut into steps of 128
+//     and the waves take the steps round-robin;
+//   * in a step, lane l holds weight row l%16 and the 32 consecutive k of
+//     lane group l/16 (16 bytes of codes, half a 64-block): four
+//     v_mfma_f32_16x16x32_bf16 multiply them with the matching 32 k of X
+//     (B operand: column m = l%16; columns m >= M are never stored), so the
+//     M dot products cost no VALU work;
+//   * the weights are dequantised exactly as the standalone dequant does,
+//     bf16(RN32(q[code] * a')), with the 16-entry codebook in LDS (16
+//     distinct words: no bank conflicts);
+//   * the waves' partial sums are added in a fixed order through LDS and Y
+//     is rounded to bf16 once.
+// gemv_kernel (the streamed kernel, used when its LDS layout fits) moves the
+// codes and X through per-wave LDS rings with global_load_lds; gemv_ring_kernel
+// (short or very long rows) keeps the next 4 steps of each wave in registers.
+// The small-M LoRA down projection bf16(s X L1) that feeds them is at the end.
 #include "common.h"
 #include "launch.h"
 
@@ -15,93 +28,505 @@ namespace qlora {
 
 namespace {
 
-template <int MT>
-__global__ __launch_bounds__(256) void gemv_kernel(NF4View W, NF4Table tab, const uint16_t* __restrict__ X,
-                                                   int64_t M, const uint16_t* __restrict__ sT,
-                                                   const uint16_t* __restrict__ L2, int r,
-                                                   uint16_t* __restrict__ Y) {
-  __shared__ float sQ[16];
-  const int tid = threadIdx.x;
-  if (tid < 16) sQ[tid] = tab.q[tid];
-  __syncthreads();
-  const float mu = W.mean[0];
-  const int64_t K = W.cols, N = W.rows;
-  const int wave = tid >> 6, lane = tid & 63;
+constexpr int kGvRows = 16;   // weight rows per workgroup = MFMA rows
+constexpr int kGvStep = 128;  // k per step: 4 lane groups x 32
+constexpr int kGvDepth = 4;   // steps in flight per wave
+constexpr int kGvMaxRank = 256; // largest rank the C ABI accepts
 
-  for (int64_t n = (int64_t)blockIdx.x * 4 + wave; n < N; n += (int64_t)gridDim.x * 4) {
-    float acc[MT];
+struct GvStep {
+  u32x4_t codes;   // 32 codes of this lane's row
+  u32x4_t x[4];    // X[m][k .. k+32) for this lane's column m
+  uint32_t a8;     // E4M3 block constant
+  float sigma;     // DQ scale of the block's group
+  int k;           // first k of the lane's 32 (>= K: past the row, masked)
+};
+
+// ---- register-ring kernel ----------------------------------------------------
+// Each wave keeps the codes, block constants and X fragments of its next 4
+// steps in registers; the rank-r LoRA term is added in fp32 (sT and the 16
+// columns of L2 are staged in LDS while the first code loads are in flight).
+template <int kGvWaves>
+__global__ __launch_bounds__(64 * kGvWaves) void gemv_ring_kernel(NF4View W, NF4Table tab, const uint16_t* __restrict__ X,
+                                                          int M, const uint16_t* __restrict__ sT, int ldst,
+                                                          const uint16_t* __restrict__ L2, int r,
+                                                          uint16_t* __restrict__ Y) {
+  __shared__ float sQ[16];
+  __shared__ float red[kGvWaves][kGvRows * 16];
+  __shared__ uint16_t sL2[kGvMaxRank * kGvRows];  // L2[j][n0 .. n0+16)
+  __shared__ uint16_t sS[16 * kGvMaxRank];        // sT[m][j]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t K = W.cols, N = W.rows;
+  const int64_t n0 = (int64_t)blockIdx.x * kGvRows;
+
+  const float mu = W.mean[0];
+  const int row = lane & 15, grp = lane >> 4;
+  int64_t n = n0 + row;
+  if (n > N - 1) n = N - 1;  // rows past N are computed on a valid row and never stored
+  const uint8_t* crow = W.codes + n * (K >> 1);
+  const int64_t blk_row = n * (K / kBlock);
+  // X column m = row; columns m >= M read row 0 and are never stored (each
+  // MFMA output column depends on its own B column only)
+  const uint16_t* xrow = X + (int64_t)(row < M ? row : 0) * K;
+  const int nsteps = (int)((K + kGvStep - 1) / kGvStep);
+
+  // Loads are unconditional (addresses clamped into the row) so that the
+  // compiler can count them exactly; steps past the row are masked in compute.
+  auto load = [&](int s, GvStep& g) {
+    g.k = s * kGvStep + grp * 32;
+    const int kc = g.k < K ? g.k : (int)K - 32;
+    g.codes = *reinterpret_cast<const u32x4_t*>(crow + (kc >> 1));
+    const int64_t blk = blk_row + (kc >> 6);
+    g.a8 = W.absmax8[blk];
+    g.sigma = W.scale2[blk / kDqBlock];
+    const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(xrow + kc);
 #pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
-    for (int64_t kc = (int64_t)lane * 32; kc < K; kc += 64 * 32) {
-      const u32x4_t c = *reinterpret_cast<const u32x4_t*>(W.codes + n * (K >> 1) + (kc >> 1));
-      const int64_t blk = n * (K / kBlock) + kc / kBlock;
-      const float ap = block_scale(W.absmax8[blk], W.scale2[blk / kDqBlock], mu);
-      const uint32_t words[4] = {c.x, c.y, c.z, c.w};
-      float w[32];
+    for (int j = 0; j < 4; ++j) g.x[j] = xp[j];
+  };
+
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute = [&](const GvStep& g) {
+    const bool valid = g.k < K;
+    const float ap = valid ? block_scale(g.a8, g.sigma, mu) : 0.0f;
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    const uint32_t words[4] = {g.codes.x, g.codes.y, g.codes.z, g.codes.w};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t byte = (words[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-        const uint32_t pr = pack_bf16x2(sQ[byte & 15u] * ap, sQ[byte >> 4] * ap);
-        w[2 * i] = __uint_as_float(pr << 16);
-        w[2 * i + 1] = __uint_as_float(pr & 0xFFFF0000u);
+    for (int j = 0; j < 4; ++j) {
+      u32x4_t wv;
+      uint32_t* wp = reinterpret_cast<uint32_t*>(&wv);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t byte = (words[j] >> (8 * i)) & 0xFFu;
+        wp[i] = pack_bf16x2(sQ[byte & 15u] * ap, sQ[byte >> 4] * ap);
       }
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if (m < M) {
-          const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(X + m * K + kc);
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const u32x4_t xv = xp[q4];
-            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-              const int i = q4 * 8 + h * 2;
-              acc[m] = __builtin_fmaf(w[i], __uint_as_float(xw[h] << 16), acc[m]);
-              acc[m] = __builtin_fmaf(w[i + 1], __uint_as_float(xw[h] & 0xFFFF0000u), acc[m]);
-            }
-          }
-        }
-      }
+      const u32x4_t xv = valid ? g.x[j] : z;  // zero weights times finite zeros past the row
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv),
+                                                     __builtin_bit_cast(bf16x8_t, xv), acc, 0, 0, 0);
     }
-    // LoRA branch: sum_j sT[m][j] L2[j][n]
-    for (int j = lane; j < r; j += 64) {
-      const float l2 = bf16_to_f32(L2[(int64_t)j * N + n]);
+  };
+
+  // ring of kGvDepth steps: this wave's i-th step (wave + kGvWaves * i) sits
+  // in slot i % kGvDepth; trailing steps past the row compute zeros
+  GvStep ring[kGvDepth];
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
-        if (m < M) acc[m] = __builtin_fmaf(bf16_to_f32(sT[m * r + j]), l2, acc[m]);
+  for (int d = 0; d < kGvDepth; ++d) load(wave + kGvWaves * d, ring[d]);
+
+  // codebook and LoRA operands into LDS while the first code loads are in flight
+  constexpr int kThreads = 64 * kGvWaves;
+  if (tid < 16) sQ[tid] = tab.q[tid];
+  for (int i = tid; i < r * kGvRows; i += kThreads) {
+    const int j = i / kGvRows, c = i % kGvRows;
+    const int64_t nc = n0 + c;
+    sL2[i] = nc < N ? L2[(int64_t)j * N + nc] : (uint16_t)0;
+  }
+  for (int i = tid; i < M * r; i += kThreads) sS[i] = sT[(int64_t)(i / r) * ldst + (i % r)];
+  __syncthreads();
+  for (int s0 = wave; s0 < nsteps; s0 += kGvWaves * kGvDepth) {
+#pragma unroll
+    for (int d = 0; d < kGvDepth; ++d) {
+      compute(ring[d]);
+      load(s0 + kGvWaves * (d + kGvDepth), ring[d]);
     }
+  }
+
+  // acc register i of lane l is C[row 4 (l/16) + i][column l%16] = partial Y[m][n0 + row]
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      float v = acc[m];
-      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-      acc[m] = v;
-    }
-    if (lane == 0) {
+  for (int i = 0; i < 4; ++i) red[wave][(4 * grp + i) * 16 + row] = acc[i];
+  __syncthreads();
+  if (tid < kGvRows * 16) {
+    const int nr = tid / 16, m = tid % 16;
+    float v = 0.0f;
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
-        if (m < M) Y[m * N + n] = f32_to_bf16(acc[m]);
+    for (int w = 0; w < kGvWaves; ++w) v += red[w][nr * 16 + m];
+    if (m < M) {
+      for (int j = 0; j < r; ++j) v = __builtin_fmaf(bf16_to_f32(sS[m * r + j]), bf16_to_f32(sL2[j * kGvRows + nr]), v);
+      const int64_t ny = n0 + nr;
+      if (ny < N) Y[(int64_t)m * N + ny] = f32_to_bf16(v);
     }
   }
 }
 
+// ---- streamed kernel ---------------------------------------------------------
+//
+// Every wave streams its own k-steps (steps wave, wave + W, ... of 128 k)
+// through its own LDS ring of NS slots, filled by global_load_lds_dwordx4:
+// a slot holds the 16 rows x 64 bytes of codes of the step (one copy) and
+// the step's 128 k of the M rows of X (one copy of up to 4 rows, or four).
+// Nothing a wave reads was copied by another wave, so the K loop has no
+// barrier: each wave waits on its own vmcnt, with up to NS - 1 steps in
+// flight and no registers held by them. 16-byte chunks are XOR-swizzled so
+// that the 16 rows read by one MFMA operand hit distinct banks. Lane l of a
+// step holds weight row l%16 and the 32 k of lane group l/16; it dequantises
+// them through the 16-entry codebook in LDS with the block constant a' from
+// a per-workgroup table and issues 4 MFMAs (two accumulators, alternated).
+// The LoRA term is MFMAs on wave 0 (A = the tile's L2 columns, B = bf16(s T));
+// the waves' partial sums are added in a fixed order through LDS.
+
+typedef __attribute__((address_space(3))) void gv_lds_t;
+
+__device__ __forceinline__ void gv_dma16(const void* gbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(gbase), "s"(m0) : "memory", "m0");
+}
+
+__device__ __forceinline__ void gv_dma4(const void* gbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(voff), "s"(gbase), "s"(m0) : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 40] (the count is an immediate)
+__device__ __forceinline__ void gv_wait_vm(int n) {
+  switch (n) {
+#define GV_W(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+    GV_W(1) GV_W(2) GV_W(3) GV_W(4) GV_W(5) GV_W(6) GV_W(7) GV_W(8) GV_W(9) GV_W(10) GV_W(11) GV_W(12)
+    GV_W(13) GV_W(14) GV_W(15) GV_W(16) GV_W(17) GV_W(18) GV_W(19) GV_W(20) GV_W(21) GV_W(22) GV_W(23)
+    GV_W(24) GV_W(25) GV_W(26) GV_W(27) GV_W(28) GV_W(29) GV_W(30) GV_W(31) GV_W(32) GV_W(33) GV_W(34)
+    GV_W(35) GV_W(36) GV_W(37) GV_W(38) GV_W(39) GV_W(40)
+#undef GV_W
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+struct GvLayout {
+  uint32_t slot_bytes, x_off, ring_bytes, red_off, l2_off, s_off, a_off, ab_off, sc_off, total;
+  int nblk_p, rp;
+};
+
+// mx: X rows held per slot (1, 4 or 16)
+__host__ __device__ inline GvLayout gv_layout(int waves, int mx, int ns, int64_t K, int r) {
+  GvLayout L;
+  L.x_off = 1024u;                              // codes: 16 rows x 64 bytes
+  L.slot_bytes = 1024u + (uint32_t)mx * 256u;   // X: mx rows x 128 k (one, four or sixteen)
+  L.ring_bytes = L.slot_bytes * ns;
+  const int nblk = (int)(K / kBlock);
+  L.nblk_p = nblk | 1;                          // odd row pitch: rows on different banks
+  L.rp = (r + 31) & ~31;                        // LoRA rank padded to the MFMA depth
+  uint32_t off = L.ring_bytes * waves;
+  L.a_off = off;    off += 16u * L.nblk_p * 4u;
+  L.ab_off = off;   off += ((16u * nblk + 255u) / 256u) * 256u;     // the tile's absmax bytes
+  L.sc_off = off;   off += 256u;                                    // its DQ scales (<= 64 groups)
+  L.total = (off + 15u) & ~15u;
+  // after the K loop the rings are free: LoRA operands and the partial sums
+  L.l2_off = 0;                                 // L2 columns of the tile, [16][rp]
+  L.s_off = 16u * L.rp * 2u;                    // bf16(s T), [16][rp], rows >= M zero
+  L.red_off = 2u * 16u * L.rp * 2u;             // partial sums, [W][256] fp32 (fits: rings >= 40 KB)
+  return L;
+}
+
+template <int W, int MX, int NS>
+__global__ __launch_bounds__(64 * W) void gemv_kernel(NF4View Wt, NF4Table tab, const uint16_t* __restrict__ X,
+                                                      int M, const uint16_t* __restrict__ sT, int ldst,
+                                                      const uint16_t* __restrict__ L2, int r,
+                                                      uint16_t* __restrict__ Y) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char gv_smem[];
+  __shared__ float sQ[16];
+  constexpr int kThreads = 64 * W;
+  constexpr int kXCopies = MX <= 4 ? 1 : MX / 4;  // copies of X per step (4 rows each; MX = 1: 16 lanes)
+  constexpr int kDma = 1 + kXCopies;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t K = Wt.cols, N = Wt.rows;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const GvLayout L = gv_layout(W, MX, NS, K, r);
+  const int nsteps = (int)((K + 127) / 128);
+  const int mysteps = nsteps > wave ? (nsteps - wave + W - 1) / W : 0;
+  unsigned char* ring = gv_smem + wave * L.ring_bytes;
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(gv_lds_t*)ring;
+
+  // copy lanes: codes lane l -> row l/4, slot chunk l%4 holding chunk (l%4) ^ ((row>>2)&3)
+  const int crow = lane >> 2;
+  const int cchunk = (lane & 3) ^ ((crow >> 2) & 3);
+  int64_t nrow = n0 + crow;
+  if (nrow > N - 1) nrow = N - 1;
+  const uint32_t crow_off = (uint32_t)(nrow * (K >> 1));  // codes < 4 GB (checked by the launcher)
+  // X lane l of copy t -> row 4t + l/16, slot chunk l%16 holding chunk (l%16) ^ (row & 15)
+  uint32_t xrow[kXCopies], xch[kXCopies];
+#pragma unroll
+  for (int t = 0; t < kXCopies; ++t) {
+    const int m = 4 * t + (lane >> 4);
+    xch[t] = (uint32_t)((lane & 15) ^ (m & 15));
+    xrow[t] = (uint32_t)((m < M ? m : 0) * K * 2);   // rows >= M: any valid row
+  }
+  auto issue = [&](int i) {  // this wave's i-th step into slot i % NS
+    const int s = wave + W * i;
+    const uint32_t sl = ring_lds + (uint32_t)(i % NS) * L.slot_bytes;
+    int64_t cb = (int64_t)s * 64 + 16 * cchunk;        // this lane's 16 bytes of the step's codes
+    if (cb > (K >> 1) - 16) cb = (K >> 1) - 16;        // past the row: any valid chunk (masked)
+    gv_dma16(Wt.codes, crow_off + (uint32_t)cb, __builtin_amdgcn_readfirstlane(sl));
+#pragma unroll
+    for (int t = 0; t < kXCopies; ++t) {
+      int64_t xk = (int64_t)s * 128 + 8 * xch[t];
+      if (xk > K - 8) xk = K - 8;                      // past the row: any valid chunk (masked)
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(sl + L.x_off + (uint32_t)(t * 1024));
+      if (MX > 1 || lane < 16) gv_dma16(X, xrow[t] + (uint32_t)(xk * 2), m0);
+    }
+  };
+
+  // Shared tables. The tile's absmax bytes (16 nblk contiguous bytes) and its
+  // DQ scales are copied into LDS by wave 0 ahead of its step copies, so that
+  // waiting for them (an exact vmcnt) does not wait for the step copies; the
+  // a' table is then built from LDS.
+  float* sA = reinterpret_cast<float*>(gv_smem + L.a_off);
+  uint16_t* sL2 = reinterpret_cast<uint16_t*>(gv_smem + L.l2_off);
+  uint16_t* sS = reinterpret_cast<uint16_t*>(gv_smem + L.s_off);
+  float* red = reinterpret_cast<float*>(gv_smem + L.red_off);
+  const int nblk = (int)(K / kBlock);
+  const int64_t nb_total = N * nblk, ng_total = (nb_total + kDqBlock - 1) / kDqBlock;
+  const int64_t ab0 = n0 * nblk;                       // first block of the tile
+  const int64_t g0 = ab0 / kDqBlock;
+  const int ab_copies = (16 * nblk + 255) / 256;      // 4 bytes per lane: N % 8 == 0 makes nb_total % 8 == 0,
+  if (wave == 0) {                                     // so no 4-byte piece straddles the end of the tensor
+    for (int t = 0; t < ab_copies; ++t) {
+      int64_t off = ab0 + 256 * t + 4 * lane;
+      if (off > nb_total - 4) off = nb_total - 4;      // past the tensor (rows >= N only): any valid bytes
+      gv_dma4(Wt.absmax8, (uint32_t)off, __builtin_amdgcn_readfirstlane(
+                                             (uint32_t)(uintptr_t)(gv_lds_t*)(gv_smem + L.ab_off + 256 * t)));
+    }
+    int64_t g = g0 + lane;
+    if (g > ng_total - 1) g = ng_total - 1;
+    gv_dma4(Wt.scale2, (uint32_t)(g * 4), __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(gv_lds_t*)(gv_smem + L.sc_off)));
+  }
+  for (int i = 0; i < NS - 1 && i < mysteps; ++i) issue(i);
+  if (wave == 0) gv_wait_vm((NS - 1 < mysteps ? NS - 1 : mysteps) * kDma);  // the table copies have landed
+  if (tid < 16) sQ[tid] = tab.q[tid];
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // (__syncthreads would drain the copies)
+  {
+    const float mu = Wt.mean[0];
+    const unsigned char* ab = gv_smem + L.ab_off;
+    const float* sc = reinterpret_cast<const float*>(gv_smem + L.sc_off);
+    for (int i = tid; i < 16 * nblk; i += kThreads) {
+      int gi = (int)((ab0 + i) / kDqBlock - g0);
+      if (gi > 63) gi = 63;                           // rows >= N only
+      sA[(i / nblk) * L.nblk_p + i % nblk] = block_scale(ab[i], sc[gi], mu);
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // a' table visible
+
+  const int row = lane & 15, grp = lane >> 4;
+  const bool xlane = row < M;                   // lanes whose X column is stored
+  f32x4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  const int cread = row * 64 + 16 * (grp ^ ((row >> 2) & 3));
+  const int xt = row >> 2, xread = (row & 3) * 256;        // copy and row within it
+  for (int i = 0; i < mysteps; ++i) {
+    const int after = mysteps - 1 - i < NS - 2 ? mysteps - 1 - i : NS - 2;  // steps issued after i
+    gv_wait_vm(after * kDma);
+    if (i + NS - 1 < mysteps) issue(i + NS - 1);
+    const unsigned char* sl = ring + (i % NS) * L.slot_bytes;
+    const int64_t k = (int64_t)(wave + W * i) * 128 + 32 * grp;
+    const bool valid = k < K;
+    const u32x4_t codes = *reinterpret_cast<const u32x4_t*>(sl + cread);
+    const float ap = valid ? sA[row * L.nblk_p + (int)(k >> 6)] : 0.0f;
+    const uint32_t words[4] = {codes.x, codes.y, codes.z, codes.w};
+    // all 32 codebook reads of the step first (one LDS round trip), then the products
+    float qv[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) qv[e] = sQ[(words[e >> 3] >> (4 * (e & 7))) & 15u];
+    u32x4_t xf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xf[j] = z;
+      if (xlane && valid)
+        xf[j] = *reinterpret_cast<const u32x4_t*>(sl + L.x_off + xt * 1024 + xread + 16 * ((4 * grp + j) ^ (row & 15)));
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 36, 0);  // the LDS reads as one group
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x4_t wv;
+      uint32_t* wp = reinterpret_cast<uint32_t*>(&wv);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wp[q] = pack_bf16x2(qv[8 * j + 2 * q] * ap, qv[8 * j + 2 * q + 1] * ap);
+      const u32x4_t xv = xf[j];
+      if (j & 1)
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv),
+                                                        __builtin_bit_cast(bf16x8_t, xv), acc1, 0, 0, 0);
+      else
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wv),
+                                                        __builtin_bit_cast(bf16x8_t, xv), acc0, 0, 0, 0);
+    }
+  }
+  f32x4_t acc = acc0 + acc1;
+
+  // LoRA term on wave 0: A = the tile's L2 columns (rows n), B = bf16(s T)^T
+  __syncthreads();  // every wave is done with its ring
+  for (int i = tid; i < 16 * L.rp; i += kThreads) {
+    const int c = i / L.rp, j = i % L.rp;
+    const int64_t nc = n0 + c;
+    sL2[i] = (j < r && nc < N) ? L2[(int64_t)j * N + nc] : (uint16_t)0;
+    sS[i] = (j < r && c < M) ? sT[(int64_t)c * ldst + j] : (uint16_t)0;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    for (int j0 = 0; j0 < L.rp; j0 += 32) {
+      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(sL2 + row * L.rp + j0 + 8 * grp);
+      const u32x4_t b = *reinterpret_cast<const u32x4_t*>(sS + row * L.rp + j0 + 8 * grp);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                     acc, 0, 0, 0);
+    }
+  }
+
+  // acc register i of lane l: Y[m = l%16][n0 + 4 (l/16) + i], partial over this wave's k
+#pragma unroll
+  for (int q = 0; q < 4; ++q) red[wave * 256 + (4 * grp + q) * 16 + row] = acc[q];
+  __syncthreads();
+  if (tid < 256) {
+    const int nr = tid / 16, m = tid % 16;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) v += red[w * 256 + nr * 16 + m];
+    const int64_t ny = n0 + nr;
+    if (m < M && ny < N) Y[(int64_t)m * N + ny] = f32_to_bf16(v);
+  }
+}
+
+constexpr uint32_t kGvMaxLds = 160u * 1024u - 64u;  // dynamic part (the codebook is static)
+
+// Returns false (nothing launched) when the LDS layout does not fit.
+template <int W, int MX, int NS>
+bool launch_streamed(const NF4View& Wt, const NF4Table& tab, const uint16_t* X, int M, const uint16_t* sT,
+                     const uint16_t* L2, int r, uint16_t* Y, int64_t tiles, hipStream_t stream, hipError_t* err) {
+  const GvLayout L = gv_layout(W, MX, NS, Wt.cols, r);
+  if (L.total > kGvMaxLds || L.red_off + 1024u * W > L.ring_bytes * W) return false;
+  static bool attr_set = false;  // raise the dynamic-LDS limit once per instantiation (idempotent)
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_kernel<W, MX, NS>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGvMaxLds);
+    (void)hipGetLastError();  // a refusal shows up as a launch error below
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((gemv_kernel<W, MX, NS>), dim3((unsigned)tiles), dim3(64 * W), L.total, stream, Wt, tab, X, M,
+                     sT, r, L2, r, Y);
+  *err = hipGetLastError();
+  return true;
+}
+
+// ---- small-M LoRA down projection -------------------------------------------
+//
+// T = X L1 for M <= 16 rows, in two short kernels:
+//   * partial sums over k-slices of 512: one workgroup of 16 waves per slice
+//     and 64 columns; wave w multiplies its 32 rows of the slice with
+//     v_mfma_f32_16x16x32_bf16 (A = the rows of X, B = the columns of L1,
+//     zero rows beyond M), and the 16 waves' sums are added in a fixed order
+//     through LDS;
+//   * a fixed-order sum over the (K/512) slices that writes bf16(s T)
+//     for the second adapter product, and bf16(T) when asked.
+
+constexpr int kTsWaves = 16;
+constexpr int kTsRows = 32;                  // L1 rows per wave
+constexpr int kTsK = kTsWaves * kTsRows;     // k per slice
+
+__global__ __launch_bounds__(64 * kTsWaves) void small_t_partial_kernel(const uint16_t* __restrict__ X, int M,
+                                                                        int64_t K, const uint16_t* __restrict__ L1,
+                                                                        int r, float* __restrict__ P) {
+  // wave w: the 32 rows kw .. kw+32 of the slice, 4 MFMA column tiles of 16;
+  // A = X rows (lane l: row l%16, k 8 (l/16) .. +8), B = L1 columns (lane l:
+  // column l%16 of the tile, the same 8 k)
+  __shared__ float red[kTsWaves][16][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t kw = (int64_t)blockIdx.x * kTsK + wave * kTsRows + 8 * (lane >> 4);
+  const int row = lane & 15;
+  const int j0 = blockIdx.y * 64;
+  u32x4_t xa = {0u, 0u, 0u, 0u};
+  if (row < M && kw < K) xa = *reinterpret_cast<const u32x4_t*>(X + (int64_t)row * K + kw);  // K % 64 == 0
+  uint32_t h[4][8];  // all 32 loads first (one round trip)
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    const int j = j0 + 16 * jt + row;
+    const bool in = j < r && kw < K;
+    const uint16_t* lp = L1 + (in ? kw * r + j : 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[jt][i] = lp[in ? (int64_t)i * r : 0];
+    if (!in) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) h[jt][i] = 0u;
+    }
+  }
+  f32x4_t acc[4];
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    const u32x4_t b = {h[jt][0] | (h[jt][1] << 16), h[jt][2] | (h[jt][3] << 16), h[jt][4] | (h[jt][5] << 16),
+                       h[jt][6] | (h[jt][7] << 16)};
+    const f32x4_t zero = {0.0f, 0.0f, 0.0f, 0.0f};
+    acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa), __builtin_bit_cast(bf16x8_t, b),
+                                                       zero, 0, 0, 0);
+  }
+  // acc[jt] register i of lane l: T[m = 4 (l/16) + i][j = j0 + 16 jt + l%16]
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][4 * (lane >> 4) + i][16 * jt + row] = acc[jt][i];
+  __syncthreads();
+  const int m = wave;  // thread (m, lane) of the first 16 waves sums the waves in order
+  float v = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kTsWaves; ++w) v += red[w][m][lane];
+  if (m < M && j0 + lane < r) P[((int64_t)blockIdx.x * M + m) * r + j0 + lane] = v;
+}
+
+__global__ __launch_bounds__(256) void small_t_reduce_kernel(const float* __restrict__ P, int Z, int M, int r, float s,
+                                                             uint16_t* __restrict__ sT, int64_t ldst,
+                                                             uint16_t* __restrict__ T_out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= M * r) return;
+  float v = 0.0f;
+  int z = 0;
+  for (; z + 8 <= Z; z += 8) {  // loads of 8 slices in flight, added in order
+    float p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) p[u] = P[(int64_t)(z + u) * M * r + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v += p[u];
+  }
+  for (; z < Z; ++z) v += P[(int64_t)z * M * r + i];
+  const int m = i / r, j = i % r;
+  sT[(int64_t)m * ldst + j] = f32_to_bf16(s * v);
+  if (T_out) T_out[(int64_t)m * r + j] = f32_to_bf16(v);
+}
+
 }  // namespace
+
+size_t small_t_partial_bytes(int64_t M, int64_t K, int r) {
+  return (size_t)((K + kTsK - 1) / kTsK) * (size_t)M * (size_t)r * 4;
+}
+
+hipError_t launch_small_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* L1, int r, float s,
+                                  uint16_t* sT, int64_t ldst, uint16_t* T_out, float* part, hipStream_t stream) {
+  if (M < 1 || M > 16) return hipErrorInvalidValue;
+  const int Z = (int)((K + kTsK - 1) / kTsK);
+  hipLaunchKernelGGL(small_t_partial_kernel, dim3((unsigned)Z, (unsigned)((r + 63) / 64)), dim3(64 * kTsWaves), 0,
+                     stream, X, (int)M, K, L1, r, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(small_t_reduce_kernel, dim3((unsigned)((M * r + 255) / 256)), dim3(256), 0, stream, part, Z,
+                     (int)M, r, s, sT, ldst, T_out);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemv(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M,
                        const uint16_t* sT, const uint16_t* L2, int r, uint16_t* Y, hipStream_t stream) {
-  const int64_t N = W.rows;
-  int64_t blocks = (N + 3) / 4;
-  if (blocks > 65535) blocks = 65535;
-  const dim3 grid((unsigned)blocks), block(256);
-  if (M <= 1)
-    hipLaunchKernelGGL(gemv_kernel<1>, grid, block, 0, stream, W, tab, X, M, sT, L2, r, Y);
-  else if (M <= 2)
-    hipLaunchKernelGGL(gemv_kernel<2>, grid, block, 0, stream, W, tab, X, M, sT, L2, r, Y);
-  else if (M <= 4)
-    hipLaunchKernelGGL(gemv_kernel<4>, grid, block, 0, stream, W, tab, X, M, sT, L2, r, Y);
-  else if (M <= 8)
-    hipLaunchKernelGGL(gemv_kernel<8>, grid, block, 0, stream, W, tab, X, M, sT, L2, r, Y);
+  if (M < 1 || M > 16 || r > kGvMaxRank || (W.cols % kBlock) != 0) return hipErrorInvalidValue;
+  const int64_t N = W.rows, K = W.cols;
+  const int64_t tiles = (N + kGvRows - 1) / kGvRows;
+  const int m = (int)M;
+  // streamed kernel: 4 waves when there are enough row tiles for two or more
+  // workgroups per CU, else 8
+  if (K >= 128 && K <= 32768 && N * K / 2 < ((int64_t)1 << 32)) {
+    hipError_t e = hipSuccess;
+    bool done;
+    if (tiles >= 512)
+      done = m <= 1   ? launch_streamed<4, 1, 8>(W, tab, X, m, sT, L2, r, Y, tiles, stream, &e)
+             : m <= 4 ? launch_streamed<4, 4, 5>(W, tab, X, m, sT, L2, r, Y, tiles, stream, &e)
+                      : launch_streamed<4, 16, 2>(W, tab, X, m, sT, L2, r, Y, tiles, stream, &e);
+    else
+      done = m <= 1   ? launch_streamed<8, 1, 8>(W, tab, X, m, sT, L2, r, Y, tiles, stream, &e)
+             : m <= 4 ? launch_streamed<8, 4, 6>(W, tab, X, m, sT, L2, r, Y, tiles, stream, &e)
+                      : launch_streamed<8, 16, 3>(W, tab, X, m, sT, L2, r, Y, tiles, stream, &e);
+    if (done) return e;
+  }
+  // register-ring kernel: short rows, very long rows, or layouts beyond the LDS
+  if (tiles >= 512)
+    hipLaunchKernelGGL(gemv_ring_kernel<4>, dim3((unsigned)tiles), dim3(256), 0, stream, W, tab, X, m, sT, r, L2, r, Y);
   else
-    hipLaunchKernelGGL(gemv_kernel<16>, grid, block, 0, stream, W, tab, X, M, sT, L2, r, Y);
+    hipLaunchKernelGGL(gemv_ring_kernel<8>, dim3((unsigned)tiles), dim3(512), 0, stream, W, tab, X, m, sT, r, L2, r, Y);
   return hipGetLastError();
 }
 

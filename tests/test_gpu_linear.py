@@ -97,6 +97,18 @@ def test_gemv_small_m(api, M):
     compare(run_case(api, inp, need_bwd=False), ref, f"gemv M={M}")
 
 
+@pytest.mark.parametrize("M,K,N,r", [
+    (1, 64 * 9, 264, 8),        # K % 128 == 64: the last k-step is half a step
+    (16, 64 * 35, 8 * 13, 256),  # largest rank, ragged rows
+    (5, 64, 8, 64),             # one block per row, one partial row tile
+])
+def test_gemv_ragged(api, M, K, N, r):
+    say(f"gemv M={M} K={K} N={N} r={r}")
+    inp = case(M, K, N, r, 0.5, 200 + M + K, with_grad=False)
+    ref, _ = oracle_case(inp)
+    compare(run_case(api, inp, need_bwd=False), ref, f"gemv {M}x{K}x{N} r={r}")
+
+
 def test_lora_only_and_zero_adapter(api):
     say("linear W = 0 (LoRA branch alone) and L2 = 0")
     inp = case(96, 256, 192, 32, 0.75, 5)
