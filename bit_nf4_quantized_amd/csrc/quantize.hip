@@ -61,12 +61,40 @@ __device__ __forceinline__ void load8<uint16_t>(const uint16_t* __restrict__ w, 
   }
 }
 
-// Nearest-code index of a normalised value: number of thresholds <= x.
-__device__ __forceinline__ uint32_t nearest_code(float x, const NF4Thresholds& th) {
-  uint32_t c = 0;
-#pragma unroll
-  for (int j = 0; j < 15; ++j) c += (x >= th.t[j]) ? 1u : 0u;
-  return c;
+template <typename InT>
+__device__ __forceinline__ void unpack8(const u32x4_t* raw, float v[8]);
+
+template <>
+__device__ __forceinline__ void unpack8<float>(const u32x4_t* raw, float v[8]) {
+  v[0] = __uint_as_float(raw[0].x); v[1] = __uint_as_float(raw[0].y);
+  v[2] = __uint_as_float(raw[0].z); v[3] = __uint_as_float(raw[0].w);
+  v[4] = __uint_as_float(raw[1].x); v[5] = __uint_as_float(raw[1].y);
+  v[6] = __uint_as_float(raw[1].z); v[7] = __uint_as_float(raw[1].w);
+}
+
+template <>
+__device__ __forceinline__ void unpack8<uint16_t>(const u32x4_t* raw, float v[8]) {
+  const u32x4_t a = raw[0];
+  v[0] = __uint_as_float(a.x << 16); v[1] = __uint_as_float(a.x & 0xFFFF0000u);
+  v[2] = __uint_as_float(a.y << 16); v[3] = __uint_as_float(a.y & 0xFFFF0000u);
+  v[4] = __uint_as_float(a.z << 16); v[5] = __uint_as_float(a.z & 0xFFFF0000u);
+  v[6] = __uint_as_float(a.w << 16); v[7] = __uint_as_float(a.w & 0xFFFF0000u);
+}
+
+// Nearest-code index of a normalised value: the number of thresholds <= x
+// (t ascending, 15 of them), found by a 4-level binary search. The candidate
+// thresholds of each level are chosen with value selects (v_cndmask), never
+// with an indexed access.
+__device__ __forceinline__ float sel(bool c, float a, float b) { return c ? a : b; }
+
+__device__ __forceinline__ uint32_t nearest_code(float x, const float t[15]) {
+  const bool b8 = x >= t[7];
+  const bool b4 = x >= sel(b8, t[11], t[3]);
+  const bool b2 = x >= sel(b8, sel(b4, t[13], t[9]), sel(b4, t[5], t[1]));
+  const float hi = sel(b4, sel(b2, t[14], t[12]), sel(b2, t[10], t[8]));
+  const float lo = sel(b4, sel(b2, t[6], t[4]), sel(b2, t[2], t[0]));
+  const bool b1 = x >= sel(b8, hi, lo);
+  return (b8 ? 8u : 0u) + (b4 ? 4u : 0u) + (b2 ? 2u : 0u) + (b1 ? 1u : 0u);
 }
 
 template <typename InT>
@@ -79,11 +107,31 @@ __global__ __launch_bounds__(kQuantThreads) void quant_blocks_kernel(
   const int64_t g = blockIdx.x;
   const int64_t gbase = g * kGroupWeights;
 
-  for (int it = 0; it < kGroupWeights / (kQuantThreads * 8); ++it) {
+  float tt[15];
+#pragma unroll
+  for (int j = 0; j < 15; ++j) tt[j] = th.t[j];
+  constexpr int kIters = kGroupWeights / (kQuantThreads * 8);
+  constexpr int kWords = sizeof(InT) * 8 / 16;         // 16-byte pieces per 8 elements
+  // all of this thread's full 16-byte loads first (one memory round trip per
+  // group); a ragged tail is loaded element-wise in its iteration
+  u32x4_t raw[kIters][kWords];
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int64_t e0 = gbase + it * (kQuantThreads * 8) + t * 8;
+#pragma unroll
+    for (int q = 0; q < kWords; ++q) {
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      raw[it][q] = (e0 + 8 <= numel) ? reinterpret_cast<const u32x4_t*>(w + e0)[q] : z;
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
     const int local = it * (kQuantThreads * 8) + t * 8;  // element offset in the group
     const int64_t e0 = gbase + local;
     float v[8];
-    if (e0 < numel) {
+    if (e0 + 8 <= numel) {
+      unpack8<InT>(raw[it], v);
+    } else if (e0 < numel) {
       load8<InT>(w, e0, numel, v);
     } else {
 #pragma unroll
@@ -100,7 +148,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_blocks_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float x = v[i] * r;
-      uint32_t c = zero_block ? 7u : nearest_code(x, th);
+      uint32_t c = zero_block ? 7u : nearest_code(x, tt);
       if (e0 + i >= numel) c = 0u;            // padding beyond the tensor
       packed |= c << (4 * i);
     }
