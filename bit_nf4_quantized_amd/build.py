@@ -46,9 +46,14 @@ def common_flags() -> list[str]:
     ]
 
 
+# Per-source code-generation options: the GEMV kernels keep MFMA results in
+# VGPRs (their accumulators feed VALU FMAs; AGPR copies would cost VALU issue).
+EXTRA_FLAGS = {"gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ_DIR, src + ".o")
-    cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + common_flags() + EXTRA_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -399,6 +399,333 @@ bool launch_streamed(const NF4View& Wt, const NF4Table& tab, const uint16_t* X, 
   return true;
 }
 
+// ---- byte-table kernel ---------------------------------------------------------
+//
+// Within one 64-block of a row every weight carries the same constant a', so
+// the row's dot product with an X column is  sum_blocks a' * sum_k q[c_k] x_k.
+// This kernel computes the inner sums with MFMAs whose A operand is bf16(q[c])
+// and applies a' afterwards, in fp32, four FMAs per block and lane. The K loop
+// then does no per-weight arithmetic beyond one LDS lookup per code byte: a
+// 256-entry table maps a byte (two codes, low nibble first) straight to the
+// packed pair bf16(q[lo]) | bf16(q[hi]) << 16. The table is replicated 32 times,
+// copy c in LDS bank c, and lane l reads copy l % 32, so lookups never conflict.
+// The effective weight is bf16(q)·a' rather than bf16(q·a'): both round once
+// to bf16 precision, and the result differs from the dequantised product only
+// at that rounding level.
+//
+// Layout of a step (128 k = two 64-blocks of a row): lane l loads 16 bytes of
+// row l%16 (one 16-byte load per lane: 8-byte loads reach only about 70 % of
+// the streaming rate), and a cross-half lane swap (v_permlane32_swap) gives
+// every lane 16 codes of each block. MFMA h (h = 0, 1) of a block takes the
+// lane's codes 8h .. 8h+8 and the matching 8 k of X, so each MFMA sums one
+// block only.
+// The codes of the next D steps of a wave are in flight in registers; X is
+// staged once in LDS when it fits (XL), else its fragments ride with the codes.
+// Each wave computes the block constants of its own next D steps into a
+// private LDS ring, so the only workgroup barrier before the K loop waits for
+// the table and the staged X. The LoRA term (operands loaded first) is added
+// by wave 0 after its K loop, and the waves' partial sums are added in a
+// fixed order through LDS.
+
+constexpr int kLutCopies = 32;
+constexpr uint32_t kLutBytes = 256u * kLutCopies * 4u;   // 32 KB
+
+struct GlLayout {
+  uint32_t a_off, lora_off, x_off, xpitch, total;
+};
+
+// waves, ring depth, X rows staged in LDS (0 when X rides in registers)
+__host__ __device__ inline GlLayout gl_layout(int64_t K, int waves, int depth, int mx_lds) {
+  GlLayout L;
+  uint32_t off = kLutBytes;                      // the table; partial sums reuse it at the end
+  L.a_off = off; off += (uint32_t)(waves * depth) * 128u;  // per wave: a' [slot][block][16 rows] fp32
+  L.lora_off = off; off += 2u * 64u * 32u;       // wave 0's packed LoRA fragments, 2 rank chunks x 64 lanes x 32 B
+  L.xpitch = (uint32_t)K * 2u + 16u;             // 16-byte skew between X rows
+  L.x_off = off; off += (uint32_t)mx_lds * L.xpitch;
+  L.total = off;
+  return L;
+}
+
+template <int D, bool XL>
+struct GlSlot {
+  u32x4_t c;                       // 16 bytes of codes: row l%16, bytes 16 (l/16) .. +16 of the step
+  u32x4_t x[XL ? 1 : 2][2];        // X fragments (register path only)
+};
+
+template <int W, int D, bool XL>
+__global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table tab, const uint16_t* __restrict__ X,
+                                                          int M, const uint16_t* __restrict__ sT, int ldst,
+                                                          const uint16_t* __restrict__ L2, int r,
+                                                          uint16_t* __restrict__ Y) {
+  static_assert(D % 4 == 0, "a round of D steps gives each lane D/4 (row, step) block-constant pairs");
+  extern __shared__ __attribute__((aligned(16))) unsigned char gl_smem[];
+  constexpr int kThreads = 64 * W;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t K = Wt.cols, N = Wt.rows;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int nblk = (int)(K / kBlock);
+  const GlLayout L = gl_layout(K, W, D, XL ? M : 0);
+  const int nsteps = nblk / 2;                   // K % 128 == 0
+  const int mysteps = nsteps > wave ? (nsteps - wave + W - 1) / W : 0;
+  const int row = lane & 15, grp = lane >> 4;
+  const int xm = row < M ? row : 0;              // X column of this lane (unused columns repeat row 0)
+  const f32x4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  const int64_t nrow = n0 + row < N ? n0 + row : N - 1;  // rows past N are computed on a valid row, never stored
+
+  // ---- loads, in the order they are needed: they complete in issue order ----
+  // LoRA operands for wave 0 (ranks <= 64; the term is added after the K loop):
+  // A = L2[j][n0 + row], B = sT[row][j], rank chunks of 32. The prologue loads
+  // are unconditional (addresses clamped in bounds): a load under a branch
+  // makes the compiler wait for it where the branch joins.
+  constexpr int kLoraChunks = 2;
+  uint32_t la[kLoraChunks][8];
+  u32x4_t lb[kLoraChunks];
+  const int rp = (r + 31) & ~31;
+#pragma unroll
+  for (int c = 0; c < kLoraChunks; ++c) {
+    const int j0 = 32 * c + 8 * grp;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = j0 + e < r ? j0 + e : r - 1;
+      la[c][e] = L2[(int64_t)j * N + nrow];
+    }
+    const int jb = j0 < r ? j0 : 0;              // r % 8 == 0: a chunk of 8 is all in or all out
+    lb[c] = *reinterpret_cast<const u32x4_t*>(sT + (int64_t)xm * ldst + jb);
+  }
+  // Block constants, one round of D steps ahead: lane l computes a' of row l%16
+  // for the wave's steps base + l/16 + 4k (both 64-blocks of the step).
+  constexpr int kAPairs = D / 4;
+  uint32_t a16[kAPairs];
+  float sg[kAPairs];
+  auto load_a = [&](int base) {
+#pragma unroll
+    for (int k = 0; k < kAPairs; ++k) {
+      int s = wave + W * (base + grp + 4 * k);
+      if (s >= nsteps) s = 0;                    // past the row: any valid step (not used)
+      const int64_t b = nrow * nblk + 2 * s;     // blocks 2s, 2s+1 share a DQ group (256 is even)
+      a16[k] = *reinterpret_cast<const uint16_t*>(Wt.absmax8 + b);
+      sg[k] = Wt.scale2[b / kDqBlock];
+    }
+  };
+  load_a(0);
+  const float mu = Wt.mean[0];
+  // X chunks of 8 (staged path)
+  constexpr int kXPer = 4;                       // the launcher stages X only when M K / 8 <= kXPer threads
+  const int xchunks = XL ? M * (int)(K / 8) : 0;
+  const int kc8 = (int)(K / 8);
+  u32x4_t xv[kXPer];
+  if constexpr (XL) {
+#pragma unroll
+    for (int u = 0; u < kXPer; ++u) {
+      int c = tid + u * kThreads;
+      if (c > xchunks - 1) c = xchunks - 1;      // past the staged rows: a repeated chunk (not stored)
+      xv[u] = *reinterpret_cast<const u32x4_t*>(X + (int64_t)(c / kc8) * K + 8 * (c % kc8));
+    }
+  }
+  // codes (and X fragments) of this wave's first D steps
+  const uint8_t* crow = Wt.codes + nrow * (K >> 1);
+  const uint16_t* xrow = X + (int64_t)xm * K;
+  const int kb = 32 * (grp & 1) + 16 * (grp >> 1);  // k-offset in a block of this lane's 16 codes (see compute)
+  auto load = [&](int i, GlSlot<D, XL>& sl) {
+    int s = wave + W * i;
+    if (s >= nsteps) s = wave < nsteps ? wave : 0;  // past the row: any valid step (not computed)
+    sl.c = *reinterpret_cast<const u32x4_t*>(crow + 64 * s + 16 * grp);
+    if constexpr (!XL) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) sl.x[b][h] = *reinterpret_cast<const u32x4_t*>(xrow + 128 * s + 64 * b + kb + 8 * h);
+    }
+  };
+  GlSlot<D, XL> ring[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) load(d, ring[d]);
+  // keep every use of the loaded values below the last load, so that no wait
+  // for an early load delays the issue of the code loads (the empty asm
+  // statements after the table build take the loaded registers, and no memory
+  // access moves across them)
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+
+  // ---- tables in LDS ----
+  const uint32_t lane4 = (uint32_t)(lane & 31) << 2;
+  if (tid < 256) {  // entry tid: the pair (low nibble, high nibble), 32 copies
+    // lane j of qv holds bf16(q[j]) (written from the scalar arguments; no
+    // indexed access to the argument segment), then two cross-lane reads
+    uint32_t qv = 0u;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t u = __float_as_uint(tab.q[j]);       // finite: round to nearest even in scalar integer ops
+      const uint32_t b = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+      asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(qv) : "s"(b), "i"(j));
+    }
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute((tid & 15) << 2, (int)qv);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute((tid >> 4) << 2, (int)qv);
+    const uint32_t v = (lo & 0xFFFFu) | (hi << 16);
+    const u32x4_t v4 = {v, v, v, v};
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(gl_smem + (uint32_t)tid * (kLutCopies * 4u));
+#pragma unroll
+    for (int q = 0; q < kLutCopies / 4; ++q) dst[q] = v4;
+  }
+#pragma unroll
+  for (int c = 0; c < kLoraChunks; ++c) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(la[c][e]) :: "memory");
+    asm volatile("" : "+v"(lb[c]) :: "memory");
+  }
+#pragma unroll
+  for (int k = 0; k < kAPairs; ++k) asm volatile("" : "+v"(a16[k]), "+v"(sg[k]) :: "memory");
+  if constexpr (XL) {
+#pragma unroll
+    for (int u = 0; u < kXPer; ++u) asm volatile("" : "+v"(xv[u]) :: "memory");
+  }
+  if (wave == 0) {  // packed LoRA fragments, read back by the same lanes after the K loop
+    u32x4_t* lp = reinterpret_cast<u32x4_t*>(gl_smem + L.lora_off) + 2 * lane;
+#pragma unroll
+    for (int c = 0; c < kLoraChunks; ++c) {
+      const bool in = 32 * c + 8 * grp < r;
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      const u32x4_t a = {la[c][0] | (la[c][1] << 16), la[c][2] | (la[c][3] << 16), la[c][4] | (la[c][5] << 16),
+                         la[c][6] | (la[c][7] << 16)};
+      lp[c * 128] = in ? a : z;
+      lp[c * 128 + 1] = in ? lb[c] : z;
+    }
+  }
+  if constexpr (XL) {  // the staged X rows (the launcher keeps them within one round of loads)
+#pragma unroll
+    for (int u = 0; u < kXPer; ++u) {
+      const int c = tid + u * kThreads;
+      if (c < xchunks)
+        *reinterpret_cast<u32x4_t*>(gl_smem + L.x_off + (uint32_t)(c / kc8) * L.xpitch + 16u * (uint32_t)(c % kc8)) = xv[u];
+    }
+  }
+  // this wave's a' ring: [slot][block][16 rows]; written and read by this wave only
+  float* aw = reinterpret_cast<float*>(gl_smem + L.a_off + (uint32_t)wave * (D * 128u));
+  auto store_a = [&]() {
+#pragma unroll
+    for (int k = 0; k < kAPairs; ++k) {
+      const int slot = grp + 4 * k;
+      aw[(slot * 2 + 0) * 16 + row] = block_scale(a16[k] & 0xFFu, sg[k], mu);
+      aw[(slot * 2 + 1) * 16 + row] = block_scale((a16[k] >> 8) & 0xFFu, sg[k], mu);
+    }
+  };
+  store_a();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // table and X visible; code loads stay in flight
+
+  // ---- K loop ----
+  auto lut = [&](uint32_t w, int t) -> uint32_t {
+    const uint32_t sh = t == 0 ? (w << 7) : (w >> (8 * t - 7));
+    return *reinterpret_cast<const uint32_t*>(gl_smem + ((sh & 0x7F80u) | lane4));
+  };
+  f32x4_t acc = zero4;
+  auto compute = [&](int i, const GlSlot<D, XL>& sl) {  // K % 128 == 0: both blocks of a step are in the row
+    const int s = wave + W * i;
+    // Lanes 0-31 loaded block 0 of the step (k 0-31 in lanes 0-15, k 32-63 in
+    // lanes 16-31), lanes 32-63 block 1. Swapping dwords 0,1 of the upper half
+    // with dwords 2,3 of the lower half leaves every lane with 16 codes of each
+    // block: lane group g holds k kb(g) .. kb(g)+16, kb = 0, 32, 16, 48.
+    const auto p02 = __builtin_amdgcn_permlane32_swap(sl.c.x, sl.c.z, false, false);
+    const auto p13 = __builtin_amdgcn_permlane32_swap(sl.c.y, sl.c.w, false, false);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int blk = 2 * s + b;
+      const u32x2_t cw = {b == 0 ? p02[0] : p02[1], b == 0 ? p13[0] : p13[1]};
+      const u32x4_t a0 = {lut(cw.x, 0), lut(cw.x, 1), lut(cw.x, 2), lut(cw.x, 3)};
+      const u32x4_t a1 = {lut(cw.y, 0), lut(cw.y, 1), lut(cw.y, 2), lut(cw.y, 3)};
+      u32x4_t x0, x1;
+      if constexpr (XL) {
+        const unsigned char* xp = gl_smem + L.x_off + (uint32_t)xm * L.xpitch + (uint32_t)(64 * blk + kb) * 2u;
+        x0 = *reinterpret_cast<const u32x4_t*>(xp);
+        x1 = *reinterpret_cast<const u32x4_t*>(xp + 16);
+      } else {
+        x0 = sl.x[b][0];
+        x1 = sl.x[b][1];
+      }
+      f32x4_t p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0),
+                                                          __builtin_bit_cast(bf16x8_t, x0), zero4, 0, 0, 0);
+      p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), __builtin_bit_cast(bf16x8_t, x1),
+                                                  p, 0, 0, 0);
+      // register q of lane l is row 4 (l/16) + q of the tile
+      const f32x4_t s4 = *reinterpret_cast<const f32x4_t*>(aw + ((i % D) * 2 + b) * 16 + 4 * grp);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(s4[q], p[q], acc[q]);
+    }
+  };
+  // full rounds (one basic block each, so the waits stay exact), then the last
+  int base = 0;
+  for (; base + D < mysteps; base += D) {
+    load_a(base + D);  // the next round's block constants, ahead of its code loads
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      compute(base + d, ring[d]);
+      load(base + D + d, ring[d]);
+      __builtin_amdgcn_sched_barrier(0);  // slot by slot: each waits only for its own loads
+    }
+    store_a();  // this round's constants are consumed
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (base + d < mysteps) compute(base + d, ring[d]);
+
+  // ---- LoRA term (wave 0): acc += sum_j L2[j][n] sT[m][j] ----
+  if (wave == 0) {
+    const u32x4_t* lp = reinterpret_cast<const u32x4_t*>(gl_smem + L.lora_off) + 2 * lane;
+#pragma unroll
+    for (int c = 0; c < kLoraChunks; ++c) {
+      if (32 * c < rp)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lp[c * 128]),
+                                                       __builtin_bit_cast(bf16x8_t, lp[c * 128 + 1]), acc, 0, 0, 0);
+    }
+    for (int j0 = 32 * kLoraChunks; j0 < rp; j0 += 32) {  // ranks above 64
+      const int jj = j0 + 8 * grp;
+      const bool in = jj < r;
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+      u32x4_t b = {0u, 0u, 0u, 0u};
+      if (in) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = (uint32_t)L2[(int64_t)(jj + 2 * e) * N + nrow] | ((uint32_t)L2[(int64_t)(jj + 2 * e + 1) * N + nrow] << 16);
+        b = *reinterpret_cast<const u32x4_t*>(sT + (int64_t)xm * ldst + jj);
+      }
+      const u32x4_t a = {w[0], w[1], w[2], w[3]};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                     acc, 0, 0, 0);
+    }
+  }
+
+  // ---- fixed-order sum of the waves' partials ----
+  float* red = reinterpret_cast<float*>(gl_smem);   // reuses the table
+  __syncthreads();
+  // acc register q of lane l: Y[m = l%16][n0 + 4 (l/16) + q]
+#pragma unroll
+  for (int q = 0; q < 4; ++q) red[wave * 256 + (4 * grp + q) * 16 + row] = acc[q];
+  __syncthreads();
+  if (tid < 256) {
+    const int nr = tid / 16, m = tid % 16;
+    float v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) v += red[w * 256 + nr * 16 + m];
+    const int64_t ny = n0 + nr;
+    if (m < M && ny < N) Y[(int64_t)m * N + ny] = f32_to_bf16(v);
+  }
+}
+
+template <int W, int D, bool XL>
+hipError_t launch_lut(const NF4View& Wt, const NF4Table& tab, const uint16_t* X, int M, const uint16_t* sT,
+                      const uint16_t* L2, int r, uint16_t* Y, int64_t tiles, uint32_t lds, hipStream_t stream) {
+  static bool attr_set = false;  // raise the dynamic-LDS limit once per instantiation (idempotent)
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_lut_kernel<W, D, XL>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGvMaxLds);
+    (void)hipGetLastError();  // a refusal shows up as a launch error below
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((gemv_lut_kernel<W, D, XL>), dim3((unsigned)tiles), dim3(64 * W), lds, stream, Wt, tab, X, M, sT,
+                     r, L2, r, Y);
+  return hipGetLastError();
+}
+
 // ---- small-M LoRA down projection -------------------------------------------
 //
 // T = X L1 for M <= 16 rows, in two short kernels:
@@ -507,6 +834,32 @@ hipError_t launch_gemv(const NF4View& W, const NF4Table& tab, const uint16_t* X,
   const int64_t N = W.rows, K = W.cols;
   const int64_t tiles = (N + kGvRows - 1) / kGvRows;
   const int m = (int)M;
+  // byte-table kernel: every workgroup of the launch resident at once (LDS
+  // budget per workgroup = LDS per CU / workgroups per CU), 4 waves when a CU
+  // holds three or more workgroups, else 8; X staged in LDS when it fits
+  if (K % 128 == 0) {
+    static int cus = 0;  // compute units of the device (the same on every device this library runs on)
+    if (cus <= 0) {
+      int dev = 0, n = 0;
+      if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+        cus = n;
+      (void)hipGetLastError();
+      if (cus <= 0) cus = 256;
+    }
+    int64_t per_cu = (tiles + cus - 1) / cus;
+    if (per_cu > 4) per_cu = 4;
+    const uint32_t budget = (uint32_t)(160 * 1024 / per_cu) - 1024u;
+    const int64_t xchunks = M * K / 8;   // X staged by one round of kXPer loads per thread
+    if (per_cu >= 3) {
+      const GlLayout xl = gl_layout(K, 4, 4, m), xr = gl_layout(K, 4, 4, 0);
+      if (xl.total <= budget && xchunks <= 4 * 256) return launch_lut<4, 4, true>(W, tab, X, m, sT, L2, r, Y, tiles, xl.total, stream);
+      if (xr.total <= budget) return launch_lut<4, 4, false>(W, tab, X, m, sT, L2, r, Y, tiles, xr.total, stream);
+    } else {
+      const GlLayout xl = gl_layout(K, 8, 4, m), xr = gl_layout(K, 8, 4, 0);
+      if (xl.total <= budget && xchunks <= 4 * 512) return launch_lut<8, 4, true>(W, tab, X, m, sT, L2, r, Y, tiles, xl.total, stream);
+      if (xr.total <= budget) return launch_lut<8, 4, false>(W, tab, X, m, sT, L2, r, Y, tiles, xr.total, stream);
+    }
+  }
   // streamed kernel: 4 waves when there are enough row tiles for two or more
   // workgroups per CU, else 8
   if (K >= 128 && K <= 32768 && N * K / 2 < ((int64_t)1 << 32)) {

@@ -11,7 +11,7 @@
 // kernels stream the large operand with coalesced 16-byte loads, keep the
 // whole rank dimension (padded to 64) in one tile, and use
 // v_mfma_f32_32x32x16_bf16 for the products. The reduction is split over
-// blockIdx.z into fp32 partials that splitk_reduce_kernel sums in a fixed
+// blockIdx.z into fp32 partials that skinny_reduce_kernel sums in a fixed
 // order, so results are deterministic.
 //
 // skinny_nt_kernel:  C[z][m][j] = sum_{k in slice z} A[m][k] B[j][k]

@@ -109,6 +109,20 @@ def test_gemv_ragged(api, M, K, N, r):
     compare(run_case(api, inp, need_bwd=False), ref, f"gemv {M}x{K}x{N} r={r}")
 
 
+@pytest.mark.parametrize("M,K,N,r", [
+    (1, 256, 8200, 64),     # 513 row tiles: 4-wave workgroups, X staged in LDS, ragged last tile
+    (16, 1024, 8200, 64),   # 4-wave workgroups, X fragments in registers
+    (16, 4096, 200, 72),    # 8-wave workgroups, X in registers, rank above 64
+    (3, 2048, 1000, 8),     # 8-wave workgroups, X staged, rank 8
+    (2, 128, 40, 256),      # one k-step per row (idle waves), largest rank
+])
+def test_gemv_paths(api, M, K, N, r):
+    say(f"gemv path M={M} K={K} N={N} r={r}")
+    inp = case(M, K, N, r, 0.25, 300 + M + K + N, with_grad=False)
+    ref, _ = oracle_case(inp)
+    compare(run_case(api, inp, need_bwd=False), ref, f"gemv {M}x{K}x{N} r={r}")
+
+
 def test_lora_only_and_zero_adapter(api):
     say("linear W = 0 (LoRA branch alone) and L2 = 0")
     inp = case(96, 256, 192, 32, 0.75, 5)
