@@ -440,7 +440,7 @@ __host__ __device__ inline GlLayout gl_layout(int64_t K, int waves, int depth, i
   uint32_t off = kLutBytes;                      // the table; partial sums reuse it at the end
   L.a_off = off; off += (uint32_t)(waves * depth) * 128u;  // per wave: a' [slot][block][16 rows] fp32
   L.lora_off = off; off += 2u * 64u * 32u;       // wave 0's packed LoRA fragments, 2 rank chunks x 64 lanes x 32 B
-  L.xpitch = (uint32_t)K * 2u + 16u;             // 16-byte skew between X rows
+  L.xpitch = (uint32_t)K * 2u;                   // X rows back to back (staged only for M <= 2 in practice)
   L.x_off = off; off += (uint32_t)mx_lds * L.xpitch;
   L.total = off;
   return L;
@@ -462,22 +462,27 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
   constexpr int kThreads = 64 * W;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t K = Wt.cols, N = Wt.rows;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int nblk = (int)(K / kBlock);
+  // Sizes fit 32-bit arithmetic (the launcher checks the byte extents), so each
+  // load is a uniform 64-bit base plus a 32-bit per-lane byte offset, and the
+  // products are 24-bit multiplies: a 64-bit address costs several quarter-rate
+  // VALU instructions, which the prologue of every wave would pay.
+  const int K = (int)Wt.cols, N = (int)Wt.rows;
+  const int n0 = (int)blockIdx.x * 16;
+  const int nblk = K / kBlock;
   const GlLayout L = gl_layout(K, W, D, XL ? M : 0);
   const int nsteps = nblk / 2;                   // K % 128 == 0
   const int mysteps = nsteps > wave ? (nsteps - wave + W - 1) / W : 0;
   const int row = lane & 15, grp = lane >> 4;
   const int xm = row < M ? row : 0;              // X column of this lane (unused columns repeat row 0)
   const f32x4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
-  const int64_t nrow = n0 + row < N ? n0 + row : N - 1;  // rows past N are computed on a valid row, never stored
+  const int nrow = n0 + row < N ? n0 + row : N - 1;  // rows past N are computed on a valid row, never stored
+  auto ld16 = [](const void* base, uint32_t off) { return *reinterpret_cast<const u32x4_t*>(static_cast<const char*>(base) + off); };
 
   // ---- loads, in the order they are needed: they complete in issue order ----
   // LoRA operands for wave 0 (ranks <= 64; the term is added after the K loop):
   // A = L2[j][n0 + row], B = sT[row][j], rank chunks of 32. The prologue loads
-  // are unconditional (addresses clamped in bounds): a load under a branch
-  // makes the compiler wait for it where the branch joins.
+  // are unconditional (addresses in bounds): a load under a branch makes the
+  // compiler wait for it where the branch joins.
   constexpr int kLoraChunks = 2;
   uint32_t la[kLoraChunks][8];
   u32x4_t lb[kLoraChunks];
@@ -485,57 +490,56 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
 #pragma unroll
   for (int c = 0; c < kLoraChunks; ++c) {
     const int j0 = 32 * c + 8 * grp;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int j = j0 + e < r ? j0 + e : r - 1;
-      la[c][e] = L2[(int64_t)j * N + nrow];
-    }
     const int jb = j0 < r ? j0 : 0;              // r % 8 == 0: a chunk of 8 is all in or all out
-    lb[c] = *reinterpret_cast<const u32x4_t*>(sT + (int64_t)xm * ldst + jb);
+    const uint32_t o = (__umul24((uint32_t)jb, (uint32_t)N) + (uint32_t)nrow) * 2u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      la[c][e] = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(L2) + o + (uint32_t)(e * N) * 2u);
+    lb[c] = ld16(sT, (__umul24((uint32_t)xm, (uint32_t)ldst) + (uint32_t)jb) * 2u);
   }
   // Block constants, one round of D steps ahead: lane l computes a' of row l%16
   // for the wave's steps base + l/16 + 4k (both 64-blocks of the step).
   constexpr int kAPairs = D / 4;
   uint32_t a16[kAPairs];
   float sg[kAPairs];
+  const uint32_t arow = __umul24((uint32_t)nrow, (uint32_t)nblk);  // first block of this lane's row
   auto load_a = [&](int base) {
 #pragma unroll
     for (int k = 0; k < kAPairs; ++k) {
       int s = wave + W * (base + grp + 4 * k);
       if (s >= nsteps) s = 0;                    // past the row: any valid step (not used)
-      const int64_t b = nrow * nblk + 2 * s;     // blocks 2s, 2s+1 share a DQ group (256 is even)
+      const uint32_t b = arow + 2u * (uint32_t)s;  // blocks 2s, 2s+1 share a DQ group (256 is even)
       a16[k] = *reinterpret_cast<const uint16_t*>(Wt.absmax8 + b);
-      sg[k] = Wt.scale2[b / kDqBlock];
+      sg[k] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(Wt.scale2) + (b >> 8) * 4u);
     }
   };
   load_a(0);
   const float mu = Wt.mean[0];
-  // X chunks of 8 (staged path)
+  // X chunks of 8 (staged path), row-major: chunk c is bytes 16c .. 16c+16 of X
   constexpr int kXPer = 4;                       // the launcher stages X only when M K / 8 <= kXPer threads
-  const int xchunks = XL ? M * (int)(K / 8) : 0;
-  const int kc8 = (int)(K / 8);
+  const int xchunks = XL ? M * (K / 8) : 0;
   u32x4_t xv[kXPer];
   if constexpr (XL) {
 #pragma unroll
     for (int u = 0; u < kXPer; ++u) {
       int c = tid + u * kThreads;
       if (c > xchunks - 1) c = xchunks - 1;      // past the staged rows: a repeated chunk (not stored)
-      xv[u] = *reinterpret_cast<const u32x4_t*>(X + (int64_t)(c / kc8) * K + 8 * (c % kc8));
+      xv[u] = ld16(X, 16u * (uint32_t)c);
     }
   }
   // codes (and X fragments) of this wave's first D steps
-  const uint8_t* crow = Wt.codes + nrow * (K >> 1);
-  const uint16_t* xrow = X + (int64_t)xm * K;
+  const uint32_t crow = __umul24((uint32_t)nrow, (uint32_t)(K >> 1)) + 16u * (uint32_t)grp;
   const int kb = 32 * (grp & 1) + 16 * (grp >> 1);  // k-offset in a block of this lane's 16 codes (see compute)
+  const uint32_t xrow = (__umul24((uint32_t)xm, (uint32_t)K) + (uint32_t)kb) * 2u;
   auto load = [&](int i, GlSlot<D, XL>& sl) {
     int s = wave + W * i;
     if (s >= nsteps) s = wave < nsteps ? wave : 0;  // past the row: any valid step (not computed)
-    sl.c = *reinterpret_cast<const u32x4_t*>(crow + 64 * s + 16 * grp);
+    sl.c = ld16(Wt.codes, crow + 64u * (uint32_t)s);
     if constexpr (!XL) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) sl.x[b][h] = *reinterpret_cast<const u32x4_t*>(xrow + 128 * s + 64 * b + kb + 8 * h);
+        for (int h = 0; h < 2; ++h) sl.x[b][h] = ld16(X, xrow + 2u * (uint32_t)(128 * s + 64 * b + 8 * h));
     }
   };
   GlSlot<D, XL> ring[D];
@@ -596,8 +600,7 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
 #pragma unroll
     for (int u = 0; u < kXPer; ++u) {
       const int c = tid + u * kThreads;
-      if (c < xchunks)
-        *reinterpret_cast<u32x4_t*>(gl_smem + L.x_off + (uint32_t)(c / kc8) * L.xpitch + 16u * (uint32_t)(c % kc8)) = xv[u];
+      if (c < xchunks) *reinterpret_cast<u32x4_t*>(gl_smem + L.x_off + 16u * (uint32_t)c) = xv[u];
     }
   }
   // this wave's a' ring: [slot][block][16 rows]; written and read by this wave only
@@ -837,7 +840,9 @@ hipError_t launch_gemv(const NF4View& W, const NF4Table& tab, const uint16_t* X,
   // byte-table kernel: every workgroup of the launch resident at once (LDS
   // budget per workgroup = LDS per CU / workgroups per CU), 4 waves when a CU
   // holds three or more workgroups, else 8; X staged in LDS when it fits
-  if (K % 128 == 0) {
+  const bool fits32 = N < (1 << 24) && K < (1 << 24) && N * K / 2 < ((int64_t)1 << 32) &&
+                      (int64_t)m * K * 2 < ((int64_t)1 << 32) && (int64_t)r * N * 2 < ((int64_t)1 << 32);
+  if (K % 128 == 0 && fits32) {  // 32-bit byte offsets and 24-bit products in the kernel
     static int cus = 0;  // compute units of the device (the same on every device this library runs on)
     if (cus <= 0) {
       int dev = 0, n = 0;
