@@ -225,7 +225,6 @@ __global__ __launch_bounds__(kSkThreads) void skinny_tn_kernel(TnArgs p) {
 //   mode 0: out[m][j] (row stride ldo; columns [r, ldo) zero) in bf16, plus
 //           optional out2[m][j] = bf16(alpha2 * sum) with row stride r
 //   mode 1: out[m][j] fp32 or bf16, row stride r
-//   mode 2: transposed, out[j][m] fp32 or bf16, row stride rows
 __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ P, int Z, int64_t rows, int r,
                                                             float alpha, int mode, int out_bf16, void* __restrict__ out,
                                                             int64_t ldo, float alpha2, uint16_t* __restrict__ out2) {
@@ -234,14 +233,7 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
   const int64_t slab = rows * SJ;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
-    int64_t m, j;
-    if (mode == 2) {  // iterate in output order: i = j * rows + m
-      j = i / rows;
-      m = i - j * rows;
-    } else {
-      m = i / width;
-      j = i - m * width;
-    }
+    const int64_t m = i / width, j = i - m * width;
     if (j >= r) {
       static_cast<uint16_t*>(out)[i] = 0;
       continue;
@@ -252,6 +244,46 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
     if (out_bf16) static_cast<uint16_t*>(out)[i] = f32_to_bf16(v);
     else static_cast<float*>(out)[i] = v;
     if (mode == 0 && out2) out2[m * r + j] = f32_to_bf16(alpha2 * acc);
+  }
+}
+
+// Transposed reduction: out[j][c] = alpha * sum_z P[z][c][j] for j < r, c < W,
+// output row stride W. One workgroup per 64 columns c: the Z partial tiles
+// (64 c x 64 j, contiguous) are read with 16-byte loads and summed in a fixed
+// z order, then transposed through LDS so that every output row segment is
+// written contiguously.
+__global__ __launch_bounds__(256) void skinny_reduce_t_kernel(const float* __restrict__ P, int Z, int64_t W, int r,
+                                                              float alpha, int out_bf16, void* __restrict__ out) {
+  __shared__ float tile[64][65];
+  const int t = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * 64;
+  const int cl = t >> 2, jq = (t & 3) * 16;     // column c0 + cl, ranks jq .. jq+16
+  const int64_t c = c0 + cl;
+  f32x4_t acc[4] = {};
+  if (c < W) {
+    const int64_t slab = W * SJ;
+    for (int z = 0; z < Z; ++z) {
+      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(P + (int64_t)z * slab + c * SJ + jq);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] += src[q];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[cl][jq + 4 * q + e] = acc[q][e];
+  __syncthreads();
+  const int j = t >> 2, cq = (t & 3) * 16;      // rank j, columns c0 + cq .. +16
+  if (j < r) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t cc = c0 + cq + e;
+      if (cc < W) {
+        const float v = alpha * tile[cq + e][j];
+        if (out_bf16) static_cast<uint16_t*>(out)[(int64_t)j * W + cc] = f32_to_bf16(v);
+        else static_cast<float*>(out)[(int64_t)j * W + cc] = v;
+      }
+    }
   }
 }
 
@@ -321,8 +353,12 @@ hipError_t skinny_tn(const uint16_t* L, int64_t ldl, int64_t W, const uint16_t* 
                      a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)sk_grid(W * (int64_t)r)), dim3(256), 0, stream, part, sp.Z,
-                     W, r, alpha, transpose ? 2 : 1, out_bf16 ? 1 : 0, out, (int64_t)r, 0.0f, (uint16_t*)nullptr);
+  if (transpose)
+    hipLaunchKernelGGL(skinny_reduce_t_kernel, dim3((unsigned)sk_cdiv(W, 64)), dim3(256), 0, stream, part, sp.Z, W, r,
+                       alpha, out_bf16 ? 1 : 0, out);
+  else
+    hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)sk_grid(W * (int64_t)r)), dim3(256), 0, stream, part, sp.Z,
+                       W, r, alpha, 1, out_bf16 ? 1 : 0, out, (int64_t)r, 0.0f, (uint16_t*)nullptr);
   return hipGetLastError();
 }
 
