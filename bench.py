@@ -25,6 +25,9 @@ The same run also measures:
     in GB/s against 8 TB/s, cycling >= 24 distinct weight copies (> 512 MB)
     so the 256 MB last-level cache cannot serve the weights;
   * NF4 + DQ quantisation throughput on a LLaMA-65B-shaped tensor;
+  * the four 4-bit data types (NF4, Int4, FP4 E2M1, FP4 E3M0, all with DQ)
+    on a 4096 x 11008 weight: relative RMS error of the dequantised weight
+    for normal (0.1 % outliers) and Student-t weights, and quantise GB/s;
   * the CPU oracle on the same step (all 7 linears, 8192 tokens) as a
     baseline.
 Prints one JSON line.
@@ -221,6 +224,43 @@ def bench_quantize(api, workloads, reps=5):
     return res
 
 
+def bench_qtypes(api, workloads, reps=5):
+    """The four 4-bit data types on a 4096 x 11008 weight: relative RMS error of
+    the dequantised weight (normal with 0.1 % outliers x10, and Student-t
+    df = 4, both std 0.02) and quantise throughput (fp32 input)."""
+    import numpy as np
+    import torch
+
+    out = {}
+    rng = np.random.default_rng(2024)
+    weights = {"normal+outliers": workloads.draw_weight(rng, 11008, 4096, "normal+outliers", 0.02),
+               "student-t4": workloads.draw_weight(rng, 11008, 4096, "student-t4", 0.02)}
+    for name in api.QTYPES:
+        res = {}
+        for kind, Wh in weights.items():
+            W = torch.from_numpy(Wh).cuda()
+            q = api.qlora_quantize(W, qtype=name)
+            d = api.qlora_dequantize(q).float()
+            err = ((d - W).double().pow(2).mean() / W.double().pow(2).mean()).sqrt().item()
+            res[f"rel_rms_err_{kind}"] = err
+            if kind == "normal+outliers":
+                ws = torch.empty(api.qlora_quant_sizes(11008, 4096)["workspace"], dtype=torch.uint8, device="cuda")
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record()
+                for _ in range(reps):
+                    api.qlora_quantize(W, out=q, workspace=ws)
+                e1.record()
+                torch.cuda.synchronize()
+                call_ms = e0.elapsed_time(e1) / reps
+                res["quantize_call_ms"] = call_ms
+                res["quantize_GBps"] = (W.numel() * 4 + nf4_bytes(4096, 11008)) / (call_ms * 1e-3) / 1e9
+        out[name] = res
+        log(f"qtype {name}: rel RMS err normal+outliers {res['rel_rms_err_normal+outliers']:.4f}, "
+            f"student-t4 {res['rel_rms_err_student-t4']:.4f}; quantize {res['quantize_GBps']:.0f} GB/s")
+    return out
+
+
 def cpu_baseline(host, tokens=8192):
     """The oracle (dequant + forward + backward) on all 7 linears for a sample
     of the tokens, on the host cores; reported in the same unit."""
@@ -344,6 +384,7 @@ def main():
     if not args.no_extras:
         result["gemv"] = bench_gemv(api, workloads)
         result["quantize"] = bench_quantize(api, workloads)
+        result["qtypes"] = bench_qtypes(api, workloads)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(host)

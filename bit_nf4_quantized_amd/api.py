@@ -28,10 +28,12 @@ QLORA_BF16 = 1
 QLORA_BLOCK = 64
 QLORA_DQ_BLOCK = 256
 QLORA_MAX_RANK = 256
+# 4-bit data types (qlora_qtype)
+QTYPES = {"nf4": 0, "int4": 1, "fp4_e2m1": 2, "fp4_e3m0": 3}
 
 # every symbol declared in include/qlora_nf4.h
 EXPORTS = (
-    "qlora_status_str", "qlora_last_error", "qlora_nf4_codebook", "qlora_quant_sizes",
+    "qlora_status_str", "qlora_last_error", "qlora_nf4_codebook", "qlora_codebook", "qlora_quant_sizes",
     "qlora_quantize", "qlora_dequantize", "qlora_linear_workspace", "qlora_linear_fwd",
     "qlora_linear_bwd", "qlora_set_timing",
 )
@@ -52,6 +54,7 @@ class QNF4(ctypes.Structure):
         ("absmax8", ctypes.c_void_p),
         ("scale2", ctypes.c_void_p),
         ("mean", ctypes.c_void_p),
+        ("qtype", ctypes.c_int32),
     ]
 
 
@@ -82,6 +85,8 @@ def _load():
     lib.qlora_last_error.restype = ctypes.c_char_p
     lib.qlora_nf4_codebook.argtypes = [P(ctypes.c_float)]
     lib.qlora_nf4_codebook.restype = ctypes.c_int
+    lib.qlora_codebook.argtypes = [ctypes.c_int, P(ctypes.c_float)]
+    lib.qlora_codebook.restype = ctypes.c_int
     lib.qlora_quant_sizes.argtypes = [i64, i64, P(sz), P(sz), P(sz), P(sz)]
     lib.qlora_quant_sizes.restype = ctypes.c_int
     lib.qlora_quantize.argtypes = [vp, ctypes.c_int, P(QNF4), vp, sz, vp]
@@ -143,6 +148,21 @@ def qlora_nf4_codebook() -> np.ndarray:
     out = (ctypes.c_float * 16)()
     _check(_load().qlora_nf4_codebook(out), "qlora_nf4_codebook")
     return np.frombuffer(bytes(out), dtype=np.float32).copy()
+
+
+def qlora_codebook(qtype: str | int = "nf4") -> np.ndarray:
+    """The 16 ascending fp32 values of a 4-bit data type (name or qlora_qtype)."""
+    out = (ctypes.c_float * 16)()
+    _check(_load().qlora_codebook(_qtype(qtype), out), "qlora_codebook")
+    return np.frombuffer(bytes(out), dtype=np.float32).copy()
+
+
+def _qtype(qtype: str | int) -> int:
+    if isinstance(qtype, str):
+        if qtype not in QTYPES:
+            raise ValueError(f"unknown 4-bit data type {qtype!r}")
+        return QTYPES[qtype]
+    return int(qtype)
 
 
 def qlora_quant_sizes(rows: int, cols: int) -> dict:
@@ -221,13 +241,14 @@ class NF4Tensor:
     absmax8: "torch.Tensor"   # uint8 [nb]
     scale2: "torch.Tensor"    # float32 [ng]
     mean: "torch.Tensor"      # float32 [1]
+    qtype: int = 0            # qlora_qtype of the codes (QTYPES)
 
     def struct(self) -> QNF4:
         return QNF4(self.rows, self.cols, self.codes.data_ptr(), self.absmax8.data_ptr(),
-                    self.scale2.data_ptr(), self.mean.data_ptr())
+                    self.scale2.data_ptr(), self.mean.data_ptr(), self.qtype)
 
     @staticmethod
-    def empty(rows: int, cols: int, device="cuda") -> "NF4Tensor":
+    def empty(rows: int, cols: int, device="cuda", qtype: str | int = "nf4") -> "NF4Tensor":
         import torch
 
         s = qlora_quant_sizes(rows, cols)
@@ -235,7 +256,7 @@ class NF4Tensor:
                          torch.empty(max(s["codes"], 1), dtype=torch.uint8, device=device),
                          torch.empty(max(s["absmax8"], 1), dtype=torch.uint8, device=device),
                          torch.empty(max(s["scale2"] // 4, 1), dtype=torch.float32, device=device),
-                         torch.empty(1, dtype=torch.float32, device=device))
+                         torch.empty(1, dtype=torch.float32, device=device), _qtype(qtype))
 
 
 def _workspace(nbytes: int, device, ws=None):
@@ -248,8 +269,9 @@ def _workspace(nbytes: int, device, ws=None):
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
-def qlora_quantize(W, out: NF4Tensor | None = None, workspace=None, stream=None) -> NF4Tensor:
-    """NF4 + DQ quantisation of a [rows][cols] fp32 or bf16 device tensor."""
+def qlora_quantize(W, out: NF4Tensor | None = None, workspace=None, stream=None, qtype: str | int = "nf4") -> NF4Tensor:
+    """NF4 + DQ quantisation of a [rows][cols] fp32 or bf16 device tensor (or another
+    4-bit data type: ``qtype``; an ``out`` tensor keeps its own qtype)."""
     import torch
 
     if W.dim() != 2:
@@ -262,7 +284,7 @@ def qlora_quantize(W, out: NF4Tensor | None = None, workspace=None, stream=None)
     else:
         raise TypeError("W must be float32 or bfloat16")
     _need(W, W.dtype, (rows, cols), "W")
-    q = out if out is not None else NF4Tensor.empty(rows, cols, W.device)
+    q = out if out is not None else NF4Tensor.empty(rows, cols, W.device, qtype)
     sizes = qlora_quant_sizes(rows, cols)
     ws = _workspace(sizes["workspace"], W.device, workspace)
     st = q.struct()

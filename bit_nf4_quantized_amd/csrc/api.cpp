@@ -55,22 +55,51 @@ struct Tables {
   NF4Thresholds th;
 };
 
-// The NF4 codebook: 7 negative members of S_15 over |min S_15|, an exact 0,
-// and 8 positive members of S_17 over max S_17 (one fp32 rounding each),
-// ascending; plus the decision thresholds between neighbouring codes.
-Tables build_tables() {
-  double s15[15], s17[17];
-  quantile_set(15, s15);
-  quantile_set(17, s17);
+// The 16 ascending table values of a 4-bit data type, in float64 before the
+// one fp32 rounding.
+//   NF4: 7 negative members of S_15 over |min S_15|, an exact 0, and 8
+//     positive members of S_17 over max S_17 (diycv.top, section 方法总览
+//     item 2).
+//   Int4: the Int8 absmax formula of the same section (item 1) with 4-bit
+//     signed integers, levels k/7; entry k + 8 holds k/7 for k = -8..7
+//     (k = -8 is never produced: |x| <= 1).
+//   FP4 E2M1 (1 sign, 2 exponent bits with bias 1, 1 mantissa bit: 0, 0.5,
+//     1, 1.5, 2, 3, 4, 6) and FP4 E3M0 (exponent field 0 = zero, else a
+//     power of two: 0, 2^-6 .. 1 after scaling) scaled so that the largest
+//     magnitude is 1; +-0 are one value, so entry 0 holds an unused -2.
+//   (The pages name Int4, FP4 E2M1 and FP4 E3M0 in section 实验设置与主要结果
+//   item 1 without defining them; these are the plainest readings.)
+void type_values(int qtype, double* v) {
+  if (qtype == QLORA_QTYPE_NF4) {
+    double s15[15], s17[17];
+    quantile_set(15, s15);
+    quantile_set(17, s17);
+    int n = 0;
+    for (int i = 0; i < 7; ++i) v[n++] = s15[i] / (-s15[0]);
+    v[n++] = 0.0;
+    for (int i = 9; i < 17; ++i) v[n++] = s17[i] / s17[16];
+    v[0] = -1.0;
+    v[15] = 1.0;
+  } else if (qtype == QLORA_QTYPE_INT4) {
+    for (int k = -8; k < 8; ++k) v[k + 8] = (double)k / 7.0;
+  } else {
+    const double e2m1[7] = {0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    double mag[7];
+    for (int i = 0; i < 7; ++i) mag[i] = qtype == QLORA_QTYPE_FP4_E2M1 ? e2m1[i] / 6.0 : ldexp(1.0, i - 6);
+    v[0] = -2.0;
+    for (int i = 0; i < 7; ++i) v[1 + i] = -mag[6 - i];
+    v[8] = 0.0;
+    for (int i = 0; i < 7; ++i) v[9 + i] = mag[i];
+  }
+}
+
+// The table of a data type (one fp32 rounding per value), plus the decision
+// thresholds between neighbouring codes.
+Tables build_tables(int qtype) {
   double v[16];
-  int n = 0;
-  for (int i = 0; i < 7; ++i) v[n++] = s15[i] / (-s15[0]);
-  v[n++] = 0.0;
-  for (int i = 9; i < 17; ++i) v[n++] = s17[i] / s17[16];
+  type_values(qtype, v);
   Tables T;
   for (int i = 0; i < 16; ++i) T.tab.q[i] = (float)v[i];
-  T.tab.q[0] = -1.0f;
-  T.tab.q[15] = 1.0f;
   for (int j = 0; j < 15; ++j) {
     // exact midpoint of two fp32 values, then the smallest fp32 strictly above it
     const double m = 0.5 * ((double)T.tab.q[j] + (double)T.tab.q[j + 1]);
@@ -81,13 +110,17 @@ Tables build_tables() {
   return T;
 }
 
-const Tables& tables() {
-  static const Tables T = build_tables();  // thread-safe one-time init
-  return T;
+constexpr int kQTypes = 4;
+
+const Tables& tables(int qtype) {
+  static const Tables T[kQTypes] = {build_tables(0), build_tables(1), build_tables(2), build_tables(3)};  // one-time init
+  return T[qtype];
 }
 
+bool valid_qtype(int qtype) { return qtype >= 0 && qtype < kQTypes; }
+
 bool valid_nf4(const qlora_nf4* q) {
-  return q && q->codes && q->absmax8 && q->scale2 && q->mean;
+  return q && q->codes && q->absmax8 && q->scale2 && q->mean && valid_qtype(q->qtype);
 }
 
 NF4View view_of(const qlora_nf4* q) {
@@ -133,7 +166,13 @@ const char* qlora_last_error(void) { return g_last_error; }
 
 int qlora_nf4_codebook(float* out16) {
   if (!out16) return QLORA_ERR_ARG;
-  memcpy(out16, tables().tab.q, sizeof(float) * 16);
+  memcpy(out16, tables(QLORA_QTYPE_NF4).tab.q, sizeof(float) * 16);
+  return QLORA_OK;
+}
+
+int qlora_codebook(int qtype, float* out16) {
+  if (!out16 || !valid_qtype(qtype)) return QLORA_ERR_ARG;
+  memcpy(out16, tables(qtype).tab.q, sizeof(float) * 16);
   return QLORA_OK;
 }
 
@@ -165,7 +204,7 @@ int qlora_quantize(const void* W, qlora_dtype in_dtype, const qlora_nf4* q, void
   if (!aligned16(W) || !aligned16(q->codes) || !aligned16(ws)) return QLORA_ERR_ALIGN;
   if (ws_bytes < qlora::quant_workspace_layout(numel).total) return QLORA_ERR_WORKSPACE;
   (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
-  const hipError_t e = qlora::launch_quantize(W, in_dtype == QLORA_BF16, numel, tables().th, q->codes,
+  const hipError_t e = qlora::launch_quantize(W, in_dtype == QLORA_BF16, numel, tables(q->qtype).th, q->codes,
                                               q->absmax8, q->scale2, q->mean, ws, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
@@ -180,7 +219,7 @@ int qlora_dequantize(const qlora_nf4* q, uint16_t* out, hipStream_t stream) {
   if (!aligned16(q->codes) || !aligned16(out)) return QLORA_ERR_ALIGN;
   (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
   const hipError_t e =
-      qlora::launch_dequantize(q->codes, q->absmax8, q->scale2, q->mean, tables().tab, numel, out, stream);
+      qlora::launch_dequantize(q->codes, q->absmax8, q->scale2, q->mean, tables(q->qtype).tab, numel, out, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 
@@ -205,7 +244,7 @@ int qlora_linear_fwd(const qlora_nf4* W, const uint16_t* X, int64_t M, const uin
     return QLORA_ERR_ALIGN;
   if (ws_bytes < qlora::linear_workspace_layout(M, W->cols, W->rows, r).total) return QLORA_ERR_WORKSPACE;
   (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
-  const hipError_t e = qlora::linear_forward(view_of(W), tables().tab, X, M, L1, L2, r, scale, Y, T_out, ws, stream);
+  const hipError_t e = qlora::linear_forward(view_of(W), tables(W->qtype).tab, X, M, L1, L2, r, scale, Y, T_out, ws, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 
@@ -223,7 +262,7 @@ int qlora_linear_bwd(const qlora_nf4* W, const uint16_t* X, const uint16_t* dY, 
     return QLORA_ERR_ALIGN;
   if (ws_bytes < qlora::linear_workspace_layout(M, W->cols, W->rows, r).total) return QLORA_ERR_WORKSPACE;
   (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
-  const hipError_t e = qlora::linear_backward(view_of(W), tables().tab, X, dY, M, L1, L2, r, scale, T, dX, dL1,
+  const hipError_t e = qlora::linear_backward(view_of(W), tables(W->qtype).tab, X, dY, M, L1, L2, r, scale, T, dX, dL1,
                                               dL2, grad_dtype == QLORA_BF16, ws, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }

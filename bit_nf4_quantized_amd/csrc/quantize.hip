@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_blocks_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float x = v[i] * r;
-      uint32_t c = zero_block ? 7u : nearest_code(x, tt);
+      uint32_t c = nearest_code(x, tt);         // a zero block has r = 0, x = 0: the table's zero code
       if (e0 + i >= numel) c = 0u;            // padding beyond the tensor
       packed |= c << (4 * i);
     }

@@ -65,10 +65,31 @@ enum {
 };
 
 /*
- * One NF4+DQ quantised tensor: the pages' (c1, c2, W^NF4) triple plus the
- * DQ mean. The struct itself lives in host memory; its buffer pointers are
- * device pointers owned by the caller. Sizes (nb = ceil(rows*cols/64),
- * ng = ceil(nb/256)):
+ * 4-bit data types of the codes. NF4 is the pages' type; the others are the
+ * 4-bit types the pages compare it with (diycv.top, section 实验设置与主要结果
+ * item 1: Int4, FP4 E2M1, FP4 E3M0), which the pages name but do not define.
+ * Every type is a table of 16 ascending fp32 values in [-1, 1] (the FP4
+ * types have 15 distinct values and an unused entry 0 = -2; Int4 has the
+ * unused level -8/7 at entry 0), used with the same blockwise absmax scaling,
+ * nearest-code rounding and double quantisation (qlora_codebook returns the
+ * table):
+ *   QLORA_QTYPE_INT4      entry k + 8 = k/7, k = -8..7 (the Int8 absmax
+ *                         formula of section 方法总览 item 1 at 4 bits)
+ *   QLORA_QTYPE_FP4_E2M1  {0, 0.5, 1, 1.5, 2, 3, 4, 6} / 6 with signs
+ *   QLORA_QTYPE_FP4_E3M0  {0, 2^-6, ..., 2^-1, 1} with signs
+ */
+typedef enum {
+  QLORA_QTYPE_NF4 = 0,
+  QLORA_QTYPE_INT4 = 1,
+  QLORA_QTYPE_FP4_E2M1 = 2,
+  QLORA_QTYPE_FP4_E3M0 = 3
+} qlora_qtype;
+
+/*
+ * One quantised tensor: the pages' (c1, c2, W^NF4) triple plus the DQ mean
+ * and the 4-bit data type of the codes. The struct itself lives in host
+ * memory; its buffer pointers are device pointers owned by the caller.
+ * Sizes (nb = ceil(rows*cols/64), ng = ceil(nb/256)):
  *   codes   [ceil(rows*cols/2)] u8   4-bit codes; element 2j is the low
  *                                    nibble of byte j, element 2j+1 the high
  *                                    nibble; an unused last high nibble is 0.
@@ -86,6 +107,7 @@ typedef struct {
   uint8_t *absmax8;
   float *scale2;
   float *mean;
+  int32_t qtype;  /* qlora_qtype of the codes (QLORA_QTYPE_NF4 = 0); others return QLORA_ERR_ARG */
 } qlora_nf4;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -107,6 +129,14 @@ const char *qlora_last_error(void);
 int qlora_nf4_codebook(float *out16);
 
 /*
+ * qlora_codebook: the 16 ascending fp32 values of a 4-bit data type (host).
+ * qtype = QLORA_QTYPE_NF4 gives the same table as qlora_nf4_codebook.
+ * out16: host array of 16 floats. Returns QLORA_ERR_ARG if NULL or if qtype
+ * is not a qlora_qtype.
+ */
+int qlora_codebook(int qtype, float *out16);
+
+/*
  * qlora_quant_sizes: buffer sizes in bytes for a rows x cols tensor (host
  * only, no device work). Any output pointer may be NULL. workspace_bytes is
  * the scratch that qlora_quantize needs. rows, cols >= 0.
@@ -116,16 +146,17 @@ int qlora_quant_sizes(int64_t rows, int64_t cols, size_t *codes_bytes, size_t *a
 
 /*
  * qlora_quantize: NF4 + DQ quantisation of the weight W (diycv.top, section
- * 方法总览 items 1-3; training step 1-2 of section 训练与推理流程).
+ * 方法总览 items 1-3; training step 1-2 of section 训练与推理流程), or
+ * quantisation to the 4-bit type q->qtype with the same steps.
  *   W         device, rows*cols elements of in_dtype (QLORA_F32 or
  *             QLORA_BF16), row-major [rows][cols].
  *   q         host struct; q->rows, q->cols give the shape; its buffers
  *             receive codes, absmax8, scale2 and mean.
  *   ws        device scratch of at least qlora_quant_sizes(...).workspace
  *             bytes, 16-byte aligned.
- * Per block: a = max|w| (a below 2^-126 makes a zero block, codes 7);
- * x = RN32(w * RN32(1/a)); code = nearest NF4 value, ties to the lower
- * code. DQ: mean = RN32(S/nb) with S the float64 adjacent-pair tree sum of
+ * Per block: a = max|w| (a below 2^-126 makes a zero block: every code is
+ * the table's zero, 7 for NF4); x = RN32(w * RN32(1/a)); code = nearest
+ * table value, ties to the lower code. DQ: mean = RN32(S/nb) with S the float64 adjacent-pair tree sum of
  * the block absmax values; per group sigma = RN32(max|a - mean| / 448);
  * absmax8 = E4M3 round-to-nearest-even of RN32((a - mean)/sigma),
  * saturating at +-448 (0 where sigma is 0). Results are bit-for-bit
@@ -137,7 +168,7 @@ int qlora_quantize(const void *W, qlora_dtype in_dtype, const qlora_nf4 *q, void
 /*
  * qlora_dequantize: doubleDequant to bf16 (diycv.top, section 关键公式):
  *   a'_b = RN32(RN32(e4m3(absmax8_b) * scale2_g) + mean)
- *   out_e = bf16_RNE(RN32(q[code_e] * a'_b))
+ *   out_e = bf16_RNE(RN32(q[code_e] * a'_b)), q = the table of q->qtype
  *   out  device uint16_t[rows*cols] (bf16 bits), 16-byte aligned.
  */
 int qlora_dequantize(const qlora_nf4 *q, uint16_t *out, hipStream_t stream);

@@ -28,8 +28,8 @@ design notes):
   by max S_17, and the 16th code is the exact zero. Ascending order.
 * nearest code, ties to the lower index; element 2j is the low nibble of
   byte j, element 2j+1 the high nibble; an unused high nibble is 0.
-* a block whose absmax is below 2^-126 is a zero block (all codes 7, a := 0).
-  Otherwise x = RN32(w * RN32(1 / a)).
+* a block whose absmax is below 2^-126 is a zero block (every code is the
+  table's exact zero, 7 for NF4; a := 0). Otherwise x = RN32(w * RN32(1 / a)).
 * the DQ mean is one fp32 value per tensor: mu = RN32(S / n) where S is the
   float64 adjacent-pair tree sum of the n block absmax values.
 * the 8-bit float is OCP E4M3 ("E4M3FN": bias 7, no infinities, max 448),
@@ -304,7 +304,10 @@ def quantize(w: np.ndarray, q: np.ndarray | None = None) -> dict:
     for b0 in range(0, nb, step):
         x = (blocks[b0:b0 + step] * r[b0:b0 + step, None]).astype(_F32)  # RN32(w * r)
         codes4[b0:b0 + step] = nearest_codes(x, q)
-    codes4[zero_block, :] = 7                              # exact zero code
+    zeros = np.flatnonzero(q == 0.0)
+    if zeros.size != 1:
+        raise ValueError("quantize: the table needs exactly one zero")
+    codes4[zero_block, :] = zeros[0]                       # exact zero code (7 for NF4)
     codes4 = codes4.reshape(-1)[:numel]
 
     # --- second level: mean-centre, 8-bit float per group of 256 ----------

@@ -25,7 +25,7 @@ def say(msg):
     sys.stdout.flush()
 
 
-def gpu_quantize(api, W: np.ndarray, bf16: bool = False):
+def gpu_quantize(api, W: np.ndarray, bf16: bool = False, qtype: str = "nf4"):
     """Quantise a host weight on the GPU; returns (NF4Tensor, host dict)."""
     import torch
 
@@ -33,7 +33,7 @@ def gpu_quantize(api, W: np.ndarray, bf16: bool = False):
         t = api.to_device_bf16(W)
     else:
         t = torch.from_numpy(np.ascontiguousarray(W, np.float32)).cuda()
-    q = api.qlora_quantize(t)
+    q = api.qlora_quantize(t, qtype=qtype)
     torch.cuda.synchronize()
     return q, nf4_host(q)
 

@@ -38,7 +38,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     assert sorted(api.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -49,6 +49,23 @@ def test_codebook_matches_oracle_bit_exact(lib):
     o = nf4.nf4_codebook()
     assert g.view(np.uint32).tolist() == o.view(np.uint32).tolist()
     assert lib.qlora_nf4_codebook(None) == api.QLORA_ERR_ARG
+
+
+@pytest.mark.parametrize("name", ["nf4", "int4", "fp4_e2m1", "fp4_e3m0"])
+def test_type_tables_match_oracle_bit_exact(lib, name):
+    from oracle import qtypes
+
+    g = api.qlora_codebook(name)
+    assert g.view(np.uint32).tolist() == qtypes.codebook(name).view(np.uint32).tolist()
+
+
+def test_codebook_rejects_bad_type(lib):
+    import ctypes
+
+    out = (ctypes.c_float * 16)()
+    assert lib.qlora_codebook(4, out) == api.QLORA_ERR_ARG
+    assert lib.qlora_codebook(-1, out) == api.QLORA_ERR_ARG
+    assert lib.qlora_codebook(0, None) == api.QLORA_ERR_ARG
 
 
 @pytest.mark.parametrize("rows,cols", [(0, 0), (1, 1), (3, 21), (512, 512), (4096, 11008), (11008, 4096),
@@ -93,6 +110,11 @@ def test_quantize_validation(lib):
     assert lib.qlora_quantize(None, 0, ctypes.byref(empty), None, 0, None) == api.QLORA_OK  # nothing to do
     nullbuf = api.QNF4(64, 64, 0x10000000, None, 0x10200000, 0x10300000)
     assert lib.qlora_quantize(ok_ptr, 0, ctypes.byref(nullbuf), ws, big, None) == api.QLORA_ERR_ARG
+    for bad in (4, -1):  # not a qlora_qtype
+        badt = fake_nf4(64, 64)
+        badt.qtype = bad
+        assert lib.qlora_quantize(ok_ptr, 0, ctypes.byref(badt), ws, big, None) == api.QLORA_ERR_ARG
+        assert lib.qlora_dequantize(ctypes.byref(badt), ctypes.c_void_p(0x20000000), None) == api.QLORA_ERR_ARG
 
 
 def test_dequantize_validation(lib):
