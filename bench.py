@@ -26,8 +26,9 @@ The same run also measures:
     so the 256 MB last-level cache cannot serve the weights;
   * NF4 + DQ quantisation throughput on a LLaMA-65B-shaped tensor;
   * the four 4-bit data types (NF4, Int4, FP4 E2M1, FP4 E3M0, all with DQ)
-    on a 4096 x 11008 weight: relative RMS error of the dequantised weight
-    for normal (0.1 % outliers) and Student-t weights, and quantise GB/s;
+    and NF4 without DQ on a 4096 x 11008 weight: relative RMS error of the
+    dequantised weight for normal (0.1 % outliers) and Student-t weights,
+    storage bits per parameter and quantise GB/s;
   * the CPU oracle on the same step (all 7 linears, 8192 tokens) as a
     baseline.
 Prints one JSON line.
@@ -59,11 +60,11 @@ def linear_flops(M, K, N, r):
     return 4 * M * K * N + 6 * M * r * (K + N)
 
 
-def nf4_bytes(K, N):
+def nf4_bytes(K, N, double_quant=True):
     numel = K * N
     nb = -(-numel // 64)
     ng = -(-nb // 256)
-    return numel // 2 + nb + 4 * ng + 4
+    return numel // 2 + (nb + 4 * ng + 4 if double_quant else 4 * nb)
 
 
 def setup_layer(api, workloads, name, M=None):
@@ -225,9 +226,10 @@ def bench_quantize(api, workloads, reps=5):
 
 
 def bench_qtypes(api, workloads, reps=5):
-    """The four 4-bit data types on a 4096 x 11008 weight: relative RMS error of
-    the dequantised weight (normal with 0.1 % outliers x10, and Student-t
-    df = 4, both std 0.02) and quantise throughput (fp32 input)."""
+    """The four 4-bit data types (with double quantisation) and NF4 without it
+    on a 4096 x 11008 weight: relative RMS error of the dequantised weight
+    (normal with 0.1 % outliers x10, and Student-t df = 4, both std 0.02),
+    storage bits per parameter and quantise throughput (fp32 input)."""
     import numpy as np
     import torch
 
@@ -235,11 +237,12 @@ def bench_qtypes(api, workloads, reps=5):
     rng = np.random.default_rng(2024)
     weights = {"normal+outliers": workloads.draw_weight(rng, 11008, 4096, "normal+outliers", 0.02),
                "student-t4": workloads.draw_weight(rng, 11008, 4096, "student-t4", 0.02)}
-    for name in api.QTYPES:
-        res = {}
+    variants = [(name, name, True) for name in api.QTYPES] + [("nf4_no_dq", "nf4", False)]
+    for label, name, dq in variants:
+        res = {"bits_per_param": 8 * nf4_bytes(4096, 11008, dq) / (4096 * 11008)}
         for kind, Wh in weights.items():
             W = torch.from_numpy(Wh).cuda()
-            q = api.qlora_quantize(W, qtype=name)
+            q = api.qlora_quantize(W, qtype=name, double_quant=dq)
             d = api.qlora_dequantize(q).float()
             err = ((d - W).double().pow(2).mean() / W.double().pow(2).mean()).sqrt().item()
             res[f"rel_rms_err_{kind}"] = err
@@ -254,9 +257,9 @@ def bench_qtypes(api, workloads, reps=5):
                 torch.cuda.synchronize()
                 call_ms = e0.elapsed_time(e1) / reps
                 res["quantize_call_ms"] = call_ms
-                res["quantize_GBps"] = (W.numel() * 4 + nf4_bytes(4096, 11008)) / (call_ms * 1e-3) / 1e9
-        out[name] = res
-        log(f"qtype {name}: rel RMS err normal+outliers {res['rel_rms_err_normal+outliers']:.4f}, "
+                res["quantize_GBps"] = (W.numel() * 4 + nf4_bytes(4096, 11008, dq)) / (call_ms * 1e-3) / 1e9
+        out[label] = res
+        log(f"qtype {label}: rel RMS err normal+outliers {res['rel_rms_err_normal+outliers']:.4f}, "
             f"student-t4 {res['rel_rms_err_student-t4']:.4f}; quantize {res['quantize_GBps']:.0f} GB/s")
     return out
 

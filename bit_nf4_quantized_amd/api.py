@@ -55,6 +55,8 @@ class QNF4(ctypes.Structure):
         ("scale2", ctypes.c_void_p),
         ("mean", ctypes.c_void_p),
         ("qtype", ctypes.c_int32),
+        ("no_dq", ctypes.c_int32),
+        ("absmax32", ctypes.c_void_p),
     ]
 
 
@@ -242,18 +244,29 @@ class NF4Tensor:
     scale2: "torch.Tensor"    # float32 [ng]
     mean: "torch.Tensor"      # float32 [1]
     qtype: int = 0            # qlora_qtype of the codes (QTYPES)
+    absmax32: "torch.Tensor | None" = None  # float32 [nb] when stored without double quantisation
+
+    @property
+    def double_quant(self) -> bool:
+        return self.absmax32 is None
 
     def struct(self) -> QNF4:
-        return QNF4(self.rows, self.cols, self.codes.data_ptr(), self.absmax8.data_ptr(),
-                    self.scale2.data_ptr(), self.mean.data_ptr(), self.qtype)
+        if self.absmax32 is None:
+            return QNF4(self.rows, self.cols, self.codes.data_ptr(), self.absmax8.data_ptr(),
+                        self.scale2.data_ptr(), self.mean.data_ptr(), self.qtype, 0, None)
+        return QNF4(self.rows, self.cols, self.codes.data_ptr(), None, None, None, self.qtype, 1,
+                    self.absmax32.data_ptr())
 
     @staticmethod
-    def empty(rows: int, cols: int, device="cuda", qtype: str | int = "nf4") -> "NF4Tensor":
+    def empty(rows: int, cols: int, device="cuda", qtype: str | int = "nf4", double_quant: bool = True) -> "NF4Tensor":
         import torch
 
         s = qlora_quant_sizes(rows, cols)
-        return NF4Tensor(rows, cols,
-                         torch.empty(max(s["codes"], 1), dtype=torch.uint8, device=device),
+        codes = torch.empty(max(s["codes"], 1), dtype=torch.uint8, device=device)
+        if not double_quant:
+            return NF4Tensor(rows, cols, codes, None, None, None, _qtype(qtype),
+                             torch.empty(max(s["absmax8"], 1), dtype=torch.float32, device=device))
+        return NF4Tensor(rows, cols, codes,
                          torch.empty(max(s["absmax8"], 1), dtype=torch.uint8, device=device),
                          torch.empty(max(s["scale2"] // 4, 1), dtype=torch.float32, device=device),
                          torch.empty(1, dtype=torch.float32, device=device), _qtype(qtype))
@@ -269,9 +282,11 @@ def _workspace(nbytes: int, device, ws=None):
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
-def qlora_quantize(W, out: NF4Tensor | None = None, workspace=None, stream=None, qtype: str | int = "nf4") -> NF4Tensor:
+def qlora_quantize(W, out: NF4Tensor | None = None, workspace=None, stream=None, qtype: str | int = "nf4",
+                   double_quant: bool = True) -> NF4Tensor:
     """NF4 + DQ quantisation of a [rows][cols] fp32 or bf16 device tensor (or another
-    4-bit data type: ``qtype``; an ``out`` tensor keeps its own qtype)."""
+    4-bit data type: ``qtype``; without double quantisation: ``double_quant=False``;
+    an ``out`` tensor keeps its own settings)."""
     import torch
 
     if W.dim() != 2:
@@ -284,7 +299,7 @@ def qlora_quantize(W, out: NF4Tensor | None = None, workspace=None, stream=None,
     else:
         raise TypeError("W must be float32 or bfloat16")
     _need(W, W.dtype, (rows, cols), "W")
-    q = out if out is not None else NF4Tensor.empty(rows, cols, W.device, qtype)
+    q = out if out is not None else NF4Tensor.empty(rows, cols, W.device, qtype, double_quant)
     sizes = qlora_quant_sizes(rows, cols)
     ws = _workspace(sizes["workspace"], W.device, workspace)
     st = q.struct()

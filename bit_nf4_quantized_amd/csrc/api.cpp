@@ -120,7 +120,8 @@ const Tables& tables(int qtype) {
 bool valid_qtype(int qtype) { return qtype >= 0 && qtype < kQTypes; }
 
 bool valid_nf4(const qlora_nf4* q) {
-  return q && q->codes && q->absmax8 && q->scale2 && q->mean && valid_qtype(q->qtype);
+  if (!q || !q->codes || !valid_qtype(q->qtype) || (q->no_dq != 0 && q->no_dq != 1)) return false;
+  return q->no_dq ? q->absmax32 != nullptr : (q->absmax8 && q->scale2 && q->mean);
 }
 
 NF4View view_of(const qlora_nf4* q) {
@@ -131,6 +132,7 @@ NF4View view_of(const qlora_nf4* q) {
   v.mean = q->mean;
   v.rows = q->rows;
   v.cols = q->cols;
+  v.absmax32 = q->no_dq ? q->absmax32 : nullptr;
   return v;
 }
 
@@ -205,7 +207,8 @@ int qlora_quantize(const void* W, qlora_dtype in_dtype, const qlora_nf4* q, void
   if (ws_bytes < qlora::quant_workspace_layout(numel).total) return QLORA_ERR_WORKSPACE;
   (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
   const hipError_t e = qlora::launch_quantize(W, in_dtype == QLORA_BF16, numel, tables(q->qtype).th, q->codes,
-                                              q->absmax8, q->scale2, q->mean, ws, stream);
+                                              q->absmax8, q->scale2, q->mean, q->no_dq ? q->absmax32 : nullptr,
+                                              ws, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 
@@ -219,7 +222,8 @@ int qlora_dequantize(const qlora_nf4* q, uint16_t* out, hipStream_t stream) {
   if (!aligned16(q->codes) || !aligned16(out)) return QLORA_ERR_ALIGN;
   (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
   const hipError_t e =
-      qlora::launch_dequantize(q->codes, q->absmax8, q->scale2, q->mean, tables(q->qtype).tab, numel, out, stream);
+      qlora::launch_dequantize(q->codes, q->absmax8, q->scale2, q->mean, q->no_dq ? q->absmax32 : nullptr,
+                               tables(q->qtype).tab, numel, out, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 

@@ -278,14 +278,14 @@ __global__ __launch_bounds__(256) void dequant_rows_kernel(NF4View W, NF4Table t
   __shared__ float s_q[16];
   if (threadIdx.x < 16) s_q[threadIdx.x] = tab.q[threadIdx.x];
   __syncthreads();
-  const float mu = W.mean[0];
+  const float mu = tensor_mean(W);
   const int64_t numel = W.rows * W.cols;
   const int64_t nunits = numel / 16;  // cols % 64 == 0
   for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < nunits;
        u += (int64_t)gridDim.x * blockDim.x) {
     const int64_t e0 = u * 16;
     const int64_t blk = e0 / kBlock;
-    const float ap = block_scale(W.absmax8[blk], W.scale2[blk / kDqBlock], mu);
+    const float ap = block_const(W, blk, mu);
     const u32x2_t c = *reinterpret_cast<const u32x2_t*>(W.codes + (e0 >> 1));
     uint32_t o[8];
 #pragma unroll
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(256) void dequant_cols_kernel(NF4View W, NF4Table t
   __shared__ uint16_t tile[64][64 + 8];
   if (threadIdx.x < 16) s_q[threadIdx.x] = tab.q[threadIdx.x];
   __syncthreads();
-  const float mu = W.mean[0];
+  const float mu = tensor_mean(W);
   const int64_t K = W.cols, N = W.rows;
   const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
   const int t = threadIdx.x;
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(256) void dequant_cols_kernel(NF4View W, NF4Table t
     if (n < N) {
       const int64_t e0 = n * K + k0 + part * 16;
       const int64_t blk = e0 / kBlock;
-      const float ap = block_scale(W.absmax8[blk], W.scale2[blk / kDqBlock], mu);
+      const float ap = block_const(W, blk, mu);
       const u32x2_t c = *reinterpret_cast<const u32x2_t*>(W.codes + (e0 >> 1));
 #pragma unroll
       for (int i = 0; i < 8; ++i) {

@@ -143,7 +143,7 @@ __device__ __forceinline__ void load_nf4(const NF4View& W, float mu, int64_t n0,
   if (gn < W.rows) {
     R.codes = *reinterpret_cast<const u32x4_t*>(W.codes + gn * (kw >> 1) + (k0 >> 1) + half * 16);
     const int64_t blk = gn * (kw / kBlock) + k0 / kBlock;
-    R.ap = block_scale(W.absmax8[blk], W.scale2[blk / kDqBlock], mu);
+    R.ap = block_const(W, blk, mu);
   } else {
     R.codes = u32x4_t{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
     R.ap = 0.0f;
@@ -187,7 +187,7 @@ __device__ __forceinline__ void load_nf4t(const NF4View& W, float mu, int64_t c0
     if (gn < W.rows && gc < kw) {
       R.code16[i] = *reinterpret_cast<const uint16_t*>(W.codes + gn * (kw >> 1) + (gc >> 1));
       const int64_t blk = gn * (kw / kBlock) + gc / kBlock;
-      R.ap[i] = block_scale(W.absmax8[blk], W.scale2[blk / kDqBlock], mu);
+      R.ap[i] = block_const(W, blk, mu);
     } else {
       R.code16[i] = 0x7777u;
       R.ap[i] = 0.0f;
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
   float mu = 0.0f;
   if constexpr (BMODE == B_NF4 || BMODE == B_NF4T) {
     if (tid < 16) sQ[tid] = p.tab.q[tid];
-    mu = p.W.mean[0];
+    mu = tensor_mean(p.W);
   }
 
   RowRegs ra, rb;

@@ -58,7 +58,12 @@ __global__ __launch_bounds__(64 * kGvWaves) void gemv_ring_kernel(NF4View W, NF4
   const int64_t K = W.cols, N = W.rows;
   const int64_t n0 = (int64_t)blockIdx.x * kGvRows;
 
-  const float mu = W.mean[0];
+  // Without double quantisation the fp32 block absmax is a' itself: the
+  // loads below then read it in place of the DQ scale (the 8-bit load reads
+  // any valid byte, unused), so that no load depends on a branch.
+  const bool dq = W.absmax32 == nullptr;
+  const float mu = *(dq ? W.mean : W.absmax32) * (dq ? 1.0f : 0.0f);
+  const uint8_t* a8p = dq ? W.absmax8 : reinterpret_cast<const uint8_t*>(W.absmax32);
   const int row = lane & 15, grp = lane >> 4;
   int64_t n = n0 + row;
   if (n > N - 1) n = N - 1;  // rows past N are computed on a valid row and never stored
@@ -76,8 +81,8 @@ __global__ __launch_bounds__(64 * kGvWaves) void gemv_ring_kernel(NF4View W, NF4
     const int kc = g.k < K ? g.k : (int)K - 32;
     g.codes = *reinterpret_cast<const u32x4_t*>(crow + (kc >> 1));
     const int64_t blk = blk_row + (kc >> 6);
-    g.a8 = W.absmax8[blk];
-    g.sigma = W.scale2[blk / kDqBlock];
+    g.a8 = a8p[blk];
+    g.sigma = dq ? W.scale2[blk / kDqBlock] : W.absmax32[blk];
     const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(xrow + kc);
 #pragma unroll
     for (int j = 0; j < 4; ++j) g.x[j] = xp[j];
@@ -86,7 +91,7 @@ __global__ __launch_bounds__(64 * kGvWaves) void gemv_ring_kernel(NF4View W, NF4
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
   auto compute = [&](const GvStep& g) {
     const bool valid = g.k < K;
-    const float ap = valid ? block_scale(g.a8, g.sigma, mu) : 0.0f;
+    const float ap = valid ? (dq ? block_scale(g.a8, g.sigma, mu) : g.sigma) : 0.0f;
     const u32x4_t z = {0u, 0u, 0u, 0u};
     const uint32_t words[4] = {g.codes.x, g.codes.y, g.codes.z, g.codes.w};
 #pragma unroll
@@ -499,9 +504,16 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
   }
   // Block constants, one round of D steps ahead: lane l computes a' of row l%16
   // for the wave's steps base + l/16 + 4k (both 64-blocks of the step).
+  // Without double quantisation (Wt.absmax32 set) a' is the fp32 block
+  // absmax: sg0/sg1 then read it for the two blocks and the 16-bit load reads
+  // any valid bytes (unused); with DQ both scale loads read the group's DQ
+  // scale. No load depends on a branch.
   constexpr int kAPairs = D / 4;
+  const bool dq = Wt.absmax32 == nullptr;
+  const void* a8p = dq ? static_cast<const void*>(Wt.absmax8) : static_cast<const void*>(Wt.absmax32);
+  const void* sgp = dq ? static_cast<const void*>(Wt.scale2) : static_cast<const void*>(Wt.absmax32);
   uint32_t a16[kAPairs];
-  float sg[kAPairs];
+  float sg0[kAPairs], sg1[kAPairs];
   const uint32_t arow = __umul24((uint32_t)nrow, (uint32_t)nblk);  // first block of this lane's row
   auto load_a = [&](int base) {
 #pragma unroll
@@ -509,12 +521,14 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
       int s = wave + W * (base + grp + 4 * k);
       if (s >= nsteps) s = 0;                    // past the row: any valid step (not used)
       const uint32_t b = arow + 2u * (uint32_t)s;  // blocks 2s, 2s+1 share a DQ group (256 is even)
-      a16[k] = *reinterpret_cast<const uint16_t*>(Wt.absmax8 + b);
-      sg[k] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(Wt.scale2) + (b >> 8) * 4u);
+      a16[k] = *reinterpret_cast<const uint16_t*>(static_cast<const char*>(a8p) + b);
+      const uint32_t so = dq ? (b >> 8) * 4u : b * 4u;
+      sg0[k] = *reinterpret_cast<const float*>(static_cast<const char*>(sgp) + so);
+      sg1[k] = *reinterpret_cast<const float*>(static_cast<const char*>(sgp) + so + (dq ? 0u : 4u));
     }
   };
   load_a(0);
-  const float mu = Wt.mean[0];
+  const float mu = *reinterpret_cast<const float*>(dq ? static_cast<const void*>(Wt.mean) : sgp) * (dq ? 1.0f : 0.0f);
   // X chunks of 8 (staged path), row-major: chunk c is bytes 16c .. 16c+16 of X
   constexpr int kXPer = 4;                       // the launcher stages X only when M K / 8 <= kXPer threads
   const int xchunks = XL ? M * (K / 8) : 0;
@@ -579,7 +593,7 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
     asm volatile("" : "+v"(lb[c]) :: "memory");
   }
 #pragma unroll
-  for (int k = 0; k < kAPairs; ++k) asm volatile("" : "+v"(a16[k]), "+v"(sg[k]) :: "memory");
+  for (int k = 0; k < kAPairs; ++k) asm volatile("" : "+v"(a16[k]), "+v"(sg0[k]), "+v"(sg1[k]) :: "memory");
   if constexpr (XL) {
 #pragma unroll
     for (int u = 0; u < kXPer; ++u) asm volatile("" : "+v"(xv[u]) :: "memory");
@@ -609,8 +623,8 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
 #pragma unroll
     for (int k = 0; k < kAPairs; ++k) {
       const int slot = grp + 4 * k;
-      aw[(slot * 2 + 0) * 16 + row] = block_scale(a16[k] & 0xFFu, sg[k], mu);
-      aw[(slot * 2 + 1) * 16 + row] = block_scale((a16[k] >> 8) & 0xFFu, sg[k], mu);
+      aw[(slot * 2 + 0) * 16 + row] = dq ? block_scale(a16[k] & 0xFFu, sg0[k], mu) : sg0[k];
+      aw[(slot * 2 + 1) * 16 + row] = dq ? block_scale((a16[k] >> 8) & 0xFFu, sg1[k], mu) : sg1[k];
     }
   };
   store_a();
@@ -865,9 +879,9 @@ hipError_t launch_gemv(const NF4View& W, const NF4Table& tab, const uint16_t* X,
       if (xr.total <= budget) return launch_lut<8, 4, false>(W, tab, X, m, sT, L2, r, Y, tiles, xr.total, stream);
     }
   }
-  // streamed kernel: 4 waves when there are enough row tiles for two or more
-  // workgroups per CU, else 8
-  if (K >= 128 && K <= 32768 && N * K / 2 < ((int64_t)1 << 32)) {
+  // streamed kernel (double quantisation only): 4 waves when there are
+  // enough row tiles for two or more workgroups per CU, else 8
+  if (W.absmax32 == nullptr && K >= 128 && K <= 32768 && N * K / 2 < ((int64_t)1 << 32)) {
     hipError_t e = hipSuccess;
     bool done;
     if (tiles >= 512)

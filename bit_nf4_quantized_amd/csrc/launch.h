@@ -62,13 +62,15 @@ inline QuantWorkspace quant_workspace_layout(int64_t numel) {
   return L;
 }
 
+// absmax32 != nullptr: no double quantisation, the block absmax goes there
+// (absmax8, scale2 and mean are not touched)
 hipError_t launch_quantize(const void* w, bool bf16_in, int64_t numel, const NF4Thresholds& th,
-                           uint8_t* codes, uint8_t* absmax8, float* scale2, float* mean, void* ws,
-                           hipStream_t stream);
+                           uint8_t* codes, uint8_t* absmax8, float* scale2, float* mean, float* absmax32,
+                           void* ws, hipStream_t stream);
 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* absmax8, const float* scale2,
-                             const float* mean, const NF4Table& tab, int64_t numel, uint16_t* out,
-                             hipStream_t stream);
+                             const float* mean, const float* absmax32, const NF4Table& tab, int64_t numel,
+                             uint16_t* out, hipStream_t stream);
 
 // Views of a quantised weight for the GEMM kernels.
 struct NF4View {
@@ -76,8 +78,18 @@ struct NF4View {
   const uint8_t* absmax8;
   const float* scale2;
   const float* mean;
-  int64_t rows, cols;  // stored [rows][cols]
+  int64_t rows, cols;       // stored [rows][cols]
+  const float* absmax32;    // without double quantisation: the fp32 block absmax (else nullptr)
 };
+
+// First-level constant a' of block blk: the fp32 absmax itself without
+// double quantisation, else the doubleDequant of its 8-bit code.
+__device__ __forceinline__ float block_const(const NF4View& W, int64_t blk, float mu) {
+  return W.absmax32 ? W.absmax32[blk] : block_scale(W.absmax8[blk], W.scale2[blk / kDqBlock], mu);
+}
+
+// The DQ mean (unused, 0, without double quantisation).
+__device__ __forceinline__ float tensor_mean(const NF4View& W) { return W.absmax32 ? 0.0f : W.mean[0]; }
 
 // Skinny adapter products (rank <= 64), skinny_gemm.hip.
 struct SkinnySplit {

@@ -237,18 +237,19 @@ __global__ __launch_bounds__(kDqBlock) void dq_encode_kernel(const float* __rest
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ absmax8,
                                                       const float* __restrict__ scale2,
-                                                      const float* __restrict__ mean, NF4Table tab,
+                                                      const float* __restrict__ mean,
+                                                      const float* __restrict__ absmax32, NF4Table tab,
                                                       int64_t numel, uint16_t* __restrict__ out) {
   __shared__ float s_q[16];
   if (threadIdx.x < 16) s_q[threadIdx.x] = tab.q[threadIdx.x];
   __syncthreads();
-  const float mu = mean[0];
+  const float mu = absmax32 ? 0.0f : mean[0];
   const int64_t nunits = (numel + 15) / 16;
   for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < nunits;
        u += (int64_t)gridDim.x * blockDim.x) {
     const int64_t e0 = u * 16;
     const int64_t blk = e0 / kBlock;
-    const float ap = block_scale(absmax8[blk], scale2[blk / kDqBlock], mu);
+    const float ap = absmax32 ? absmax32[blk] : block_scale(absmax8[blk], scale2[blk / kDqBlock], mu);
     if (e0 + 16 <= numel) {
       const u32x2_t c = *reinterpret_cast<const u32x2_t*>(codes + (e0 >> 1));
       uint32_t o[8];
@@ -276,13 +277,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 }  // namespace
 
 hipError_t launch_quantize(const void* w, bool bf16_in, int64_t numel, const NF4Thresholds& th,
-                           uint8_t* codes, uint8_t* absmax8, float* scale2, float* mean, void* ws,
-                           hipStream_t stream) {
+                           uint8_t* codes, uint8_t* absmax8, float* scale2, float* mean, float* absmax32,
+                           void* ws, hipStream_t stream) {
   const int64_t nb = (numel + kBlock - 1) / kBlock;
   const int64_t ng = (nb + kDqBlock - 1) / kDqBlock;
   QuantWorkspace L = quant_workspace_layout(numel);
   char* base = static_cast<char*>(ws);
-  float* absmax = reinterpret_cast<float*>(base + L.absmax_off);
+  float* absmax = absmax32 ? absmax32 : reinterpret_cast<float*>(base + L.absmax_off);
   double* sum_a = reinterpret_cast<double*>(base + L.sum_a_off);
   double* sum_b = reinterpret_cast<double*>(base + L.sum_b_off);
   hipError_t e = timed(kTimeQuant, stream, [&] {
@@ -295,6 +296,7 @@ hipError_t launch_quantize(const void* w, bool bf16_in, int64_t numel, const NF4
     return hipGetLastError();
   });
   if (e != hipSuccess) return e;
+  if (absmax32) return hipSuccess;  // no double quantisation: the fp32 absmax is the stored constant
   hipLaunchKernelGGL(tree_fold_kernel, dim3(1), dim3(1024), 0, stream, sum_a, sum_b, ng, nb, mean);
   hipLaunchKernelGGL(dq_encode_kernel, dim3((unsigned)ng), dim3(kDqBlock), 0, stream, absmax, nb, mean,
                      absmax8, scale2);
@@ -302,15 +304,15 @@ hipError_t launch_quantize(const void* w, bool bf16_in, int64_t numel, const NF4
 }
 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* absmax8, const float* scale2,
-                             const float* mean, const NF4Table& tab, int64_t numel, uint16_t* out,
-                             hipStream_t stream) {
+                             const float* mean, const float* absmax32, const NF4Table& tab, int64_t numel,
+                             uint16_t* out, hipStream_t stream) {
   const int64_t nunits = (numel + 15) / 16;
   int64_t blocks = (nunits + 255) / 256;
   if (blocks > 256 * 64) blocks = 256 * 64;
   if (blocks < 1) blocks = 1;
   return timed(kTimeDequant, stream, [&] {
     hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, codes, absmax8, scale2,
-                       mean, tab, numel, out);
+                       mean, absmax32, tab, numel, out);
     return hipGetLastError();
   });
 }

@@ -87,7 +87,9 @@ typedef enum {
 
 /*
  * One quantised tensor: the pages' (c1, c2, W^NF4) triple plus the DQ mean
- * and the 4-bit data type of the codes. The struct itself lives in host
+ * and the 4-bit data type of the codes. Double quantisation is on by
+ * default (no_dq = 0); with no_dq = 1 the first-level constants stay fp32
+ * (the blockwise quantisation of section 方法总览 item 1 without item 3). The struct itself lives in host
  * memory; its buffer pointers are device pointers owned by the caller.
  * Sizes (nb = ceil(rows*cols/64), ng = ceil(nb/256)):
  *   codes   [ceil(rows*cols/2)] u8   4-bit codes; element 2j is the low
@@ -108,6 +110,9 @@ typedef struct {
   float *scale2;
   float *mean;
   int32_t qtype;  /* qlora_qtype of the codes (QLORA_QTYPE_NF4 = 0); others return QLORA_ERR_ARG */
+  int32_t no_dq;  /* 0: double quantisation (absmax8, scale2, mean); 1: none, absmax32 holds the
+                     fp32 block absmax and absmax8, scale2, mean are not used (may be NULL) */
+  float *absmax32; /* [nb] f32 (no_dq = 1 only; 4 * absmax8_bytes of qlora_quant_sizes) */
 } qlora_nf4;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -151,7 +156,8 @@ int qlora_quant_sizes(int64_t rows, int64_t cols, size_t *codes_bytes, size_t *a
  *   W         device, rows*cols elements of in_dtype (QLORA_F32 or
  *             QLORA_BF16), row-major [rows][cols].
  *   q         host struct; q->rows, q->cols give the shape; its buffers
- *             receive codes, absmax8, scale2 and mean.
+ *             receive codes, absmax8, scale2 and mean (codes and absmax32
+ *             when q->no_dq = 1: the block absmax a, no DQ steps).
  *   ws        device scratch of at least qlora_quant_sizes(...).workspace
  *             bytes, 16-byte aligned.
  * Per block: a = max|w| (a below 2^-126 makes a zero block: every code is
@@ -167,7 +173,7 @@ int qlora_quantize(const void *W, qlora_dtype in_dtype, const qlora_nf4 *q, void
 
 /*
  * qlora_dequantize: doubleDequant to bf16 (diycv.top, section 关键公式):
- *   a'_b = RN32(RN32(e4m3(absmax8_b) * scale2_g) + mean)
+ *   a'_b = RN32(RN32(e4m3(absmax8_b) * scale2_g) + mean)   (absmax32_b when no_dq)
  *   out_e = bf16_RNE(RN32(q[code_e] * a'_b)), q = the table of q->qtype
  *   out  device uint16_t[rows*cols] (bf16 bits), 16-byte aligned.
  */

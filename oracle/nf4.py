@@ -272,8 +272,13 @@ def unpack_nibbles(packed: np.ndarray, numel: int) -> np.ndarray:
     return out[:numel]
 
 
-def quantize(w: np.ndarray, q: np.ndarray | None = None) -> dict:
+def quantize(w: np.ndarray, q: np.ndarray | None = None, double_quant: bool = True) -> dict:
     """NF4 blockwise quantisation (B = 64) with double quantisation (B = 256).
+
+    With ``double_quant=False`` the first-level constants are kept as the
+    fp32 block absmax (``absmax32``), which is the blockwise quantisation of
+    the pages' section 方法总览 item 1 without item 3; the DQ buffers are
+    absent.
 
     ``w`` is the weight in its stored layout (any shape; it is flattened in
     row-major order). fp32 input, or bf16 already widened exactly to fp32.
@@ -309,6 +314,8 @@ def quantize(w: np.ndarray, q: np.ndarray | None = None) -> dict:
         raise ValueError("quantize: the table needs exactly one zero")
     codes4[zero_block, :] = zeros[0]                       # exact zero code (7 for NF4)
     codes4 = codes4.reshape(-1)[:numel]
+    if not double_quant:
+        return {"numel": numel, "codes": pack_nibbles(codes4), "absmax32": a, "absmax": a, "codes4": codes4}
 
     # --- second level: mean-centre, 8-bit float per group of 256 ----------
     mu = _F32(tree_sum_f64(a.astype(_F64)) / nb) if nb else _F32(0.0)
@@ -353,7 +360,10 @@ def dequantize_f32(qt: dict, q: np.ndarray | None = None) -> np.ndarray:
         q = nf4_codebook()
     numel = qt["numel"]
     codes4 = unpack_nibbles(qt["codes"], numel)
-    ap = dequant_constants(qt["absmax8"], qt["scale2"], qt["mean"])
+    if "absmax32" in qt:                       # no double quantisation: a' is the block absmax
+        ap = np.asarray(qt["absmax32"], dtype=_F32)
+    else:
+        ap = dequant_constants(qt["absmax8"], qt["scale2"], qt["mean"])
     out = np.empty(numel, dtype=_F32)
     for i in range(0, numel, CHUNK):               # CHUNK is a multiple of BLOCK
         c = codes4[i:i + CHUNK]

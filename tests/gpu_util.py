@@ -25,7 +25,7 @@ def say(msg):
     sys.stdout.flush()
 
 
-def gpu_quantize(api, W: np.ndarray, bf16: bool = False, qtype: str = "nf4"):
+def gpu_quantize(api, W: np.ndarray, bf16: bool = False, qtype: str = "nf4", double_quant: bool = True):
     """Quantise a host weight on the GPU; returns (NF4Tensor, host dict)."""
     import torch
 
@@ -33,7 +33,7 @@ def gpu_quantize(api, W: np.ndarray, bf16: bool = False, qtype: str = "nf4"):
         t = api.to_device_bf16(W)
     else:
         t = torch.from_numpy(np.ascontiguousarray(W, np.float32)).cuda()
-    q = api.qlora_quantize(t, qtype=qtype)
+    q = api.qlora_quantize(t, qtype=qtype, double_quant=double_quant)
     torch.cuda.synchronize()
     return q, nf4_host(q)
 
@@ -45,6 +45,8 @@ def nf4_host(q):
     numel = q.rows * q.cols
     nb = -(-numel // 64)
     ng = -(-nb // 256)
+    if not q.double_quant:
+        return {"codes": q.codes.cpu().numpy()[: (numel + 1) // 2], "absmax32": q.absmax32.cpu().numpy()[:nb]}
     return {
         "codes": q.codes.cpu().numpy()[: (numel + 1) // 2],
         "absmax8": q.absmax8.cpu().numpy()[:nb],

@@ -115,6 +115,13 @@ def test_quantize_validation(lib):
         badt.qtype = bad
         assert lib.qlora_quantize(ok_ptr, 0, ctypes.byref(badt), ws, big, None) == api.QLORA_ERR_ARG
         assert lib.qlora_dequantize(ctypes.byref(badt), ctypes.c_void_p(0x20000000), None) == api.QLORA_ERR_ARG
+    nodq = fake_nf4(64, 64)
+    nodq.no_dq = 1                        # without double quantisation absmax32 is required
+    assert lib.qlora_quantize(ok_ptr, 0, ctypes.byref(nodq), ws, big, None) == api.QLORA_ERR_ARG
+    nodq.no_dq = 2                        # the flag is 0 or 1
+    nodq.absmax32 = 0x10400000
+    assert lib.qlora_quantize(ok_ptr, 0, ctypes.byref(nodq), ws, big, None) == api.QLORA_ERR_ARG
+    assert lib.qlora_dequantize(ctypes.byref(nodq), ctypes.c_void_p(0x20000000), None) == api.QLORA_ERR_ARG
 
 
 def test_dequantize_validation(lib):

@@ -104,3 +104,62 @@ def test_gemv(api, name, M):
     rng = np.random.default_rng(51 + M + len(name))
     inp = workloads.draw_linear(rng, workloads.LinearShape("t", 1024, 520), M, 64, 0.25, "normal", 0.02, False)
     compare(run_linear(api, inp, name, need_bwd=False), oracle_linear(inp, name, need_bwd=False), f"{name} gemv")
+
+
+# ---- without double quantisation --------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["nf4", "int4"])
+def test_no_dq_quantize_dequantize_bit_exact(api, name):
+    import torch
+
+    say(f"{name} without DQ: quantize 300x211")
+    rng = np.random.default_rng(61 + len(name))
+    W = workloads.random_weight(rng, 300 * 211, "normal").reshape(300, 211)
+    W[:1, :] = 0.0
+    q, got = gpu_quantize(api, W, qtype=name, double_quant=False)
+    tab = qtypes.codebook(name)
+    qt = nf4.quantize(W, tab, double_quant=False)
+    np.testing.assert_array_equal(got["codes"], qt["codes"])
+    np.testing.assert_array_equal(got["absmax32"].view(np.uint32), qt["absmax32"].view(np.uint32))
+    deq = api.to_host_bits(api.qlora_dequantize(q))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(deq.reshape(300, 211), nf4.dequantize(qt, (300, 211), tab))
+
+
+def run_linear_nodq(api, inp, name, need_bwd):
+    import torch
+
+    q, _ = gpu_quantize(api, inp.W, qtype=name, double_quant=False)
+    X, L1, L2 = api.to_device_bf16(inp.X), api.to_device_bf16(inp.L1), api.to_device_bf16(inp.L2)
+    Y, T = api.qlora_linear_fwd(q, X, L1, L2, inp.s, want_T=need_bwd)
+    out = {"Y": api.to_host_bits(Y)}
+    if need_bwd:
+        dY = api.to_device_bf16(inp.dY)
+        dX, dL1, dL2 = api.qlora_linear_bwd(q, X, dY, L1, L2, inp.s, T=T)
+        torch.cuda.synchronize()
+        out.update(dX=api.to_host_bits(dX), dL1=dL1.cpu().numpy(), dL2=dL2.cpu().numpy())
+    return out
+
+
+def oracle_linear_nodq(inp, name, need_bwd):
+    tab = qtypes.codebook(name)
+    Wd = nf4.dequantize(nf4.quantize(inp.W, tab, double_quant=False), inp.W.shape, tab)
+    Y, _ = linear.linear_fwd(inp.X, Wd, inp.L1, inp.L2, inp.s)
+    ref = {"Y": Y}
+    if need_bwd:
+        dX, dL1, dL2 = linear.linear_bwd(inp.X, Wd, inp.L1, inp.L2, inp.s, inp.dY)
+        ref.update(dX=dX, dL1=dL1, dL2=dL2)
+    return ref
+
+
+@pytest.mark.parametrize("M,K,N,r", [
+    (200, 320, 136, 16),     # large-M path (dequantise + GEMM)
+    (1, 1024, 520, 64),      # byte-table GEMV
+    (4, 64 * 9, 264, 8),     # register-ring GEMV (K % 128 == 64)
+])
+def test_no_dq_linear(api, M, K, N, r):
+    say(f"nf4 without DQ: linear {M}x{K}x{N} r={r}")
+    need_bwd = M > 16
+    rng = np.random.default_rng(71 + M + K)
+    inp = workloads.draw_linear(rng, workloads.LinearShape("t", K, N), M, r, 0.5, "normal", 0.02, need_bwd)
+    compare(run_linear_nodq(api, inp, "nf4", need_bwd), oracle_linear_nodq(inp, "nf4", need_bwd), f"no-DQ {M}x{K}x{N}")

@@ -103,3 +103,35 @@ def test_nf4_has_the_smallest_error_on_normal_weights():
         d = nf4.dequantize_f32(nf4.quantize(w, q), q).astype(np.float64)
         err[name] = np.sqrt(np.mean((d - w) ** 2) / np.mean(w.astype(np.float64) ** 2))
     assert min(err, key=err.get) == "nf4", err
+
+
+# ---- without double quantisation --------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["nf4", "int4"])
+def test_no_dq_keeps_the_exact_block_absmax(name):
+    q = qtypes.codebook(name)
+    rng = np.random.default_rng(21)
+    w = workloads.random_weight(rng, 64 * 37 + 9, "normal")
+    qt = nf4.quantize(w, q, double_quant=False)
+    pad = np.zeros(64 * 38, np.float32)
+    pad[: w.size] = w
+    a = np.abs(pad.reshape(38, 64)).max(axis=1)
+    np.testing.assert_array_equal(qt["absmax32"], a)
+    assert "absmax8" not in qt
+    codes = nf4.unpack_nibbles(qt["codes"], w.size)
+    want = (q[codes] * np.repeat(a, 64)[: w.size]).astype(np.float32)
+    np.testing.assert_array_equal(nf4.dequantize_f32(qt, q), want)
+    # the codes are those of the DQ path (the first level is the same)
+    np.testing.assert_array_equal(qt["codes"], nf4.quantize(w, q)["codes"])
+
+
+def test_dq_constant_error_is_within_the_e4m3_step():
+    # a' - a comes from one E4M3 rounding of (a - mu) / sigma (3 mantissa bits:
+    # relative error <= 2^-4) plus fp32 roundings
+    rng = np.random.default_rng(22)
+    w = workloads.random_weight(rng, 64 * 4096, "student-t4")
+    qt = nf4.quantize(w)
+    a = qt["absmax"].astype(np.float64)
+    ap = nf4.dequant_constants(qt["absmax8"], qt["scale2"], qt["mean"]).astype(np.float64)
+    mu = float(qt["mean"][0])
+    assert np.all(np.abs(ap - a) <= 2.0 ** -4 * np.abs(a - mu) + 2.0 ** -20 * np.abs(a)), np.max(np.abs(ap - a))
