@@ -29,6 +29,8 @@ The same run also measures:
     and NF4 without DQ on a 4096 x 11008 weight: relative RMS error of the
     dequantised weight for normal (0.1 % outliers) and Student-t weights,
     storage bits per parameter and quantise GB/s;
+  * the blockwise Int8 absmax codec: quantise and dequantise GB/s on the
+    LLaMA-65B gate-shaped tensor, and the error by block size (64 .. 4096);
   * the CPU oracle on the same step (all 7 linears, 8192 tokens) as a
     baseline.
 Prints one JSON line.
@@ -225,6 +227,56 @@ def bench_quantize(api, workloads, reps=5):
     return res
 
 
+def bench_int8(api, workloads, reps=5):
+    """Blockwise Int8 absmax codec: quantise (fp32 in) and dequantise (fp32 and
+    bf16 out) throughput on a LLaMA-65B gate-shaped tensor (22016 x 8192,
+    block 64), and the relative RMS error by block size on a 4096 x 11008
+    normal weight with 0.1 % outliers x10 (std 0.02)."""
+    import numpy as np
+    import torch
+
+    shp = workloads.LLAMA65B[4]
+    numel = shp.N * shp.K
+    X = torch.from_numpy(workloads.quantize_weight(shp, 4, 4)).cuda().reshape(-1)
+    res = {"shape": [shp.N, shp.K], "block": 64}
+
+    def timed(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    codes, absmax = api.qlora_int8_quantize(X, 64)
+    y32 = torch.empty(numel, dtype=torch.float32, device="cuda")
+    y16 = torch.empty(numel, dtype=torch.bfloat16, device="cuda")
+    cb = numel + 4 * (numel // 64)
+    for name, fn, nbytes in (
+            ("quantize_f32", lambda: api.qlora_int8_quantize(X, 64, codes=codes, absmax=absmax), 4 * numel + cb),
+            ("dequantize_f32", lambda: api.qlora_int8_dequantize(codes, absmax, 64, out=y32), cb + 4 * numel),
+            ("dequantize_bf16", lambda: api.qlora_int8_dequantize(codes, absmax, 64, dtype=torch.bfloat16, out=y16),
+             cb + 2 * numel)):
+        ms = timed(fn)
+        res[name] = {"call_ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9,
+                     "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+        log(f"int8 {name}: {ms:.3f} ms, {res[name]['GBps']:.0f} GB/s")
+    del X, codes, absmax, y32, y16
+    rng = np.random.default_rng(2024)
+    W = torch.from_numpy(workloads.draw_weight(rng, 11008, 4096, "normal+outliers", 0.02)).cuda().reshape(-1)
+    err = {}
+    for block in api.INT8_BLOCKS:
+        c, a = api.qlora_int8_quantize(W, block)
+        d = api.qlora_int8_dequantize(c, a, block)
+        err[str(block)] = ((d - W).double().pow(2).mean() / W.double().pow(2).mean()).sqrt().item()
+    res["rel_rms_err_by_block"] = err
+    log("int8 rel RMS err by block: " + ", ".join(f"{b}: {e:.5f}" for b, e in err.items()))
+    return res
+
+
 def bench_qtypes(api, workloads, reps=5):
     """The four 4-bit data types (with double quantisation) and NF4 without it
     on a 4096 x 11008 weight: relative RMS error of the dequantised weight
@@ -388,6 +440,7 @@ def main():
         result["gemv"] = bench_gemv(api, workloads)
         result["quantize"] = bench_quantize(api, workloads)
         result["qtypes"] = bench_qtypes(api, workloads)
+        result["int8"] = bench_int8(api, workloads)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(host)

@@ -35,8 +35,9 @@ QTYPES = {"nf4": 0, "int4": 1, "fp4_e2m1": 2, "fp4_e3m0": 3}
 EXPORTS = (
     "qlora_status_str", "qlora_last_error", "qlora_nf4_codebook", "qlora_codebook", "qlora_quant_sizes",
     "qlora_quantize", "qlora_dequantize", "qlora_linear_workspace", "qlora_linear_fwd",
-    "qlora_linear_bwd", "qlora_set_timing",
+    "qlora_linear_bwd", "qlora_set_timing", "qlora_int8_quantize", "qlora_int8_dequantize",
 )
+INT8_BLOCKS = (64, 128, 256, 512, 1024, 2048, 4096)
 QLORA_TIMING_FWD_GEMM = 0
 QLORA_TIMING_DX_GEMM = 1
 QLORA_TIMING_GEMV = 2
@@ -104,6 +105,10 @@ def _load():
     lib.qlora_linear_bwd.restype = ctypes.c_int
     lib.qlora_set_timing.argtypes = [ctypes.c_int, vp, vp, ctypes.c_int, P(ctypes.c_int)]
     lib.qlora_set_timing.restype = ctypes.c_int
+    lib.qlora_int8_quantize.argtypes = [vp, ctypes.c_int, i64, ctypes.c_int, vp, vp, vp]
+    lib.qlora_int8_quantize.restype = ctypes.c_int
+    lib.qlora_int8_dequantize.argtypes = [vp, vp, i64, ctypes.c_int, vp, ctypes.c_int, vp]
+    lib.qlora_int8_dequantize.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -316,6 +321,47 @@ def qlora_dequantize(q: NF4Tensor, out=None, stream=None):
     _need(y, torch.bfloat16, (q.rows, q.cols), "out")
     st = q.struct()
     _check(_load().qlora_dequantize(ctypes.byref(st), _ptr(y), _stream(stream)), "qlora_dequantize")
+    return y
+
+
+def qlora_int8_quantize(X, block: int = 64, codes=None, absmax=None, stream=None):
+    """Blockwise Int8 absmax codes of a contiguous fp32 or bf16 device tensor
+    (flattened); returns (codes int8 [numel], absmax float32 [ceil(numel/block)])."""
+    import torch
+
+    if X.dtype == torch.float32:
+        dt = QLORA_F32
+    elif X.dtype == torch.bfloat16:
+        dt = QLORA_BF16
+    else:
+        raise TypeError("X must be float32 or bfloat16")
+    numel = X.numel()
+    _need(X, X.dtype, tuple(X.shape), "X")
+    nb = -(-numel // block) if block > 0 else 0
+    codes = codes if codes is not None else torch.empty(numel, dtype=torch.int8, device=X.device)
+    absmax = absmax if absmax is not None else torch.empty(nb, dtype=torch.float32, device=X.device)
+    _need(codes, torch.int8, (numel,), "codes")
+    _need(absmax, torch.float32, (nb,), "absmax")
+    _check(_load().qlora_int8_quantize(_ptr(X), dt, numel, block, _ptr(codes), _ptr(absmax), _stream(stream)),
+           "qlora_int8_quantize")
+    return codes, absmax
+
+
+def qlora_int8_dequantize(codes, absmax, block: int = 64, dtype=None, out=None, stream=None):
+    """x' = code * RN32(absmax / 127) as a flat float32 (default) or bfloat16 device tensor."""
+    import torch
+
+    dtype = torch.float32 if dtype is None else dtype
+    if dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("dtype must be float32 or bfloat16")
+    numel = codes.numel()
+    _need(codes, torch.int8, (numel,), "codes")
+    _need(absmax, torch.float32, (-(-numel // block) if block > 0 else 0,), "absmax")
+    y = out if out is not None else torch.empty(numel, dtype=dtype, device=codes.device)
+    _need(y, dtype, (numel,), "out")
+    dt = QLORA_F32 if dtype == torch.float32 else QLORA_BF16
+    _check(_load().qlora_int8_dequantize(_ptr(codes), _ptr(absmax), numel, block, _ptr(y), dt, _stream(stream)),
+           "qlora_int8_dequantize")
     return y
 
 

@@ -148,6 +148,13 @@ int check_linear(const qlora_nf4* W, int64_t M, int r, float scale) {
   return QLORA_OK;
 }
 
+// log2 of an Int8 codec block size (a power of two in [64, 4096]), or -1.
+int int8_block_log2(int block) {
+  for (int lg = 6; lg <= 12; ++lg)
+    if (block == (1 << lg)) return lg;
+  return -1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -224,6 +231,33 @@ int qlora_dequantize(const qlora_nf4* q, uint16_t* out, hipStream_t stream) {
   const hipError_t e =
       qlora::launch_dequantize(q->codes, q->absmax8, q->scale2, q->mean, q->no_dq ? q->absmax32 : nullptr,
                                tables(q->qtype).tab, numel, out, stream);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
+
+int qlora_int8_quantize(const void* X, qlora_dtype in_dtype, int64_t numel, int block, int8_t* codes,
+                        float* absmax, hipStream_t stream) {
+  const int lg = int8_block_log2(block);
+  if (lg < 0 || (in_dtype != QLORA_F32 && in_dtype != QLORA_BF16)) return QLORA_ERR_ARG;
+  if (numel < 0 || numel > QLORA_INT8_MAX_NUMEL) return QLORA_ERR_SHAPE;
+  if (numel == 0) return QLORA_OK;
+  if (!X || !codes || !absmax) return QLORA_ERR_ARG;
+  if (!aligned16(X) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(absmax) & 3u)) return QLORA_ERR_ALIGN;
+  (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
+  const hipError_t e = qlora::launch_int8_quantize(X, in_dtype == QLORA_BF16, numel, lg, codes, absmax, stream);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
+
+int qlora_int8_dequantize(const int8_t* codes, const float* absmax, int64_t numel, int block, void* out,
+                          qlora_dtype out_dtype, hipStream_t stream) {
+  const int lg = int8_block_log2(block);
+  if (lg < 0 || (out_dtype != QLORA_F32 && out_dtype != QLORA_BF16)) return QLORA_ERR_ARG;
+  if (numel < 0 || numel > QLORA_INT8_MAX_NUMEL) return QLORA_ERR_SHAPE;
+  if (numel == 0) return QLORA_OK;
+  if (!codes || !absmax || !out) return QLORA_ERR_ARG;
+  if (!aligned16(codes) || !aligned16(out) || (reinterpret_cast<uintptr_t>(absmax) & 3u)) return QLORA_ERR_ALIGN;
+  (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
+  const hipError_t e =
+      qlora::launch_int8_dequantize(codes, absmax, numel, lg, out, out_dtype == QLORA_BF16, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 

@@ -72,6 +72,13 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* absmax8, const
                              const float* mean, const float* absmax32, const NF4Table& tab, int64_t numel,
                              uint16_t* out, hipStream_t stream);
 
+// Blockwise Int8 absmax codec (int8.hip); blocks of 2^block_log2 elements,
+// block_log2 in [6, 12].
+hipError_t launch_int8_quantize(const void* x, bool bf16_in, int64_t numel, int block_log2, int8_t* codes,
+                                float* absmax, hipStream_t stream);
+hipError_t launch_int8_dequantize(const int8_t* codes, const float* absmax, int64_t numel, int block_log2,
+                                  void* out, bool bf16_out, hipStream_t stream);
+
 // Views of a quantised weight for the GEMM kernels.
 struct NF4View {
   const uint8_t* codes;

@@ -180,6 +180,40 @@ int qlora_quantize(const void *W, qlora_dtype in_dtype, const qlora_nf4 *q, void
 int qlora_dequantize(const qlora_nf4 *q, uint16_t *out, hipStream_t stream);
 
 /*
+ * qlora_int8_quantize: blockwise Int8 absmax quantisation (diycv.top,
+ * section 方法总览 item 1: X_int8 = round(127 / absmax(X) * X), one constant
+ * per block of the flattened tensor).
+ *   X       device, numel elements of in_dtype (QLORA_F32 or QLORA_BF16),
+ *           16-byte aligned.
+ *   numel   0 .. QLORA_INT8_MAX_NUMEL (0 enqueues nothing).
+ *   block   elements per block: 64, 128, 256, 512, 1024, 2048 or 4096.
+ *   codes   device int8[numel], 16-byte aligned.
+ *   absmax  device f32[ceil(numel / block)] receiving each block's absmax a.
+ * Per block: c = RN32(127 / a) (IEEE division); code = round(RN32(x * c)),
+ * to nearest with ties to even, clamped to [-127, 127]. A block with a below
+ * 2^-120 (zeros, or too small for the factor to be finite) gets code 0
+ * everywhere. The last block may be short. Deterministic.
+ * Returns QLORA_ERR_ARG for a bad block, dtype or NULL pointer,
+ * QLORA_ERR_SHAPE for numel out of range, QLORA_ERR_ALIGN for misaligned
+ * pointers.
+ */
+enum { QLORA_INT8_MAX_NUMEL_LOG2 = 40 };
+#define QLORA_INT8_MAX_NUMEL (((int64_t)1) << QLORA_INT8_MAX_NUMEL_LOG2)
+int qlora_int8_quantize(const void *X, qlora_dtype in_dtype, int64_t numel, int block, int8_t *codes,
+                        float *absmax, hipStream_t stream);
+
+/*
+ * qlora_int8_dequantize: out_e = RN32(code_e * RN32(a_b / 127)) for every
+ * element e of block b, written as fp32 (out_dtype QLORA_F32) or rounded to
+ * bf16 with round-to-nearest-even (QLORA_BF16, uint16_t bits).
+ *   codes, absmax, numel, block   as written by qlora_int8_quantize.
+ *   out     device [numel] of out_dtype, 16-byte aligned.
+ * Errors as for qlora_int8_quantize.
+ */
+int qlora_int8_dequantize(const int8_t *codes, const float *absmax, int64_t numel, int block, void *out,
+                          qlora_dtype out_dtype, hipStream_t stream);
+
+/*
  * qlora_linear_workspace: bytes of device workspace that qlora_linear_fwd
  * and qlora_linear_bwd need for M tokens, in_features K, out_features N and
  * rank r (host only). One workspace of this size serves both calls.

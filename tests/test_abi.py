@@ -38,7 +38,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     assert sorted(api.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -131,6 +131,29 @@ def test_dequantize_validation(lib):
     assert lib.qlora_dequantize(ctypes.byref(q), ctypes.c_void_p(0x20000002), None) == api.QLORA_ERR_ALIGN
     mis = api.QNF4(64, 64, 0x10000001, 0x10100000, 0x10200000, 0x10300000)
     assert lib.qlora_dequantize(ctypes.byref(mis), ctypes.c_void_p(0x20000000), None) == api.QLORA_ERR_ALIGN
+
+
+def test_int8_validation(lib):
+    p = lambda a: ctypes.c_void_p(a)
+    X, C, A, O = p(0x21000000), p(0x22000000), p(0x23000000), p(0x24000000)
+    q, d = lib.qlora_int8_quantize, lib.qlora_int8_dequantize
+    for bad_block in (0, 32, 96, 8192, -64):
+        assert q(X, 0, 1000, bad_block, C, A, None) == api.QLORA_ERR_ARG
+        assert d(C, A, 1000, bad_block, O, 0, None) == api.QLORA_ERR_ARG
+    assert q(X, 2, 1000, 64, C, A, None) == api.QLORA_ERR_ARG            # not a qlora_dtype
+    assert d(C, A, 1000, 64, O, 7, None) == api.QLORA_ERR_ARG
+    assert q(X, 0, -1, 64, C, A, None) == api.QLORA_ERR_SHAPE
+    assert q(X, 0, (1 << 40) + 1, 64, C, A, None) == api.QLORA_ERR_SHAPE
+    assert q(None, 0, 0, 64, None, None, None) == api.QLORA_OK          # empty: nothing to do
+    assert d(None, None, 0, 4096, None, 1, None) == api.QLORA_OK
+    assert q(None, 0, 64, 64, C, A, None) == api.QLORA_ERR_ARG
+    assert q(X, 0, 64, 64, C, None, None) == api.QLORA_ERR_ARG
+    assert d(C, A, 64, 64, None, 0, None) == api.QLORA_ERR_ARG
+    assert q(p(0x21000008), 0, 64, 64, C, A, None) == api.QLORA_ERR_ALIGN
+    assert q(X, 1, 64, 64, p(0x22000004), A, None) == api.QLORA_ERR_ALIGN
+    assert q(X, 0, 64, 64, C, p(0x23000002), None) == api.QLORA_ERR_ALIGN
+    assert d(C, A, 64, 64, p(0x24000008), 0, None) == api.QLORA_ERR_ALIGN
+    assert api.INT8_BLOCKS == (64, 128, 256, 512, 1024, 2048, 4096)
 
 
 def test_linear_workspace_rules():
