@@ -31,6 +31,8 @@ The same run also measures:
     storage bits per parameter and quantise GB/s;
   * the blockwise Int8 absmax codec: quantise and dequantise GB/s on the
     LLaMA-65B gate-shaped tensor, and the error by block size (64 .. 4096);
+  * the adapter merge (bf16 dequantised base + s L1 L2, r = 64) in GB/s on
+    the LLaMA-7B linear shapes;
   * the CPU oracle on the same step (all 7 linears, 8192 tokens) as a
     baseline.
 Prints one JSON line.
@@ -277,6 +279,43 @@ def bench_int8(api, workloads, reps=5):
     return res
 
 
+def bench_merge(api, workloads, reps=10):
+    """Adapter merge (bf16 dequantised base + s L1 L2) for the LLaMA-7B
+    linear shapes at r = 64: GB/s of the weight's algorithmic bytes (the
+    quantised weight read once, the bf16 result written once, the adapters
+    read once) against 8 TB/s; distinct weight copies so the caches cannot
+    hold them."""
+    import numpy as np
+    import torch
+
+    out = []
+    for K, N in ((4096, 4096), (4096, 11008), (11008, 4096)):
+        rng = np.random.default_rng(K + N)
+        q0 = api.qlora_quantize(torch.from_numpy(workloads.draw_weight(rng, N, K, "normal", 0.02)).cuda())
+        copies = 8
+        qs = [api.NF4Tensor(q0.rows, q0.cols, q0.codes.clone(), q0.absmax8.clone(), q0.scale2.clone(),
+                            q0.mean.clone()) for _ in range(copies)]
+        L1 = (0.01 * torch.randn(K, 64, device="cuda")).to(torch.bfloat16)
+        L2 = (0.01 * torch.randn(64, N, device="cuda")).to(torch.bfloat16)
+        outs = [torch.empty((N, K), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+        for i in range(copies):
+            api.qlora_merge_adapters(qs[i], L1, L2, 0.25, out=outs[i % 2])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(reps * copies):
+            api.qlora_merge_adapters(qs[i % copies], L1, L2, 0.25, out=outs[i % 2])
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (reps * copies)
+        nbytes = nf4_bytes(K, N) + 2 * N * K + 2 * 64 * (K + N)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        out.append({"K": K, "N": N, "r": 64, "call_us": ms * 1e3, "GBps": gbps, "frac_of_hbm_peak": gbps / PEAK_HBM_GBPS})
+        log(f"merge {K}->{N} r=64: {ms * 1e3:.1f} us, {gbps:.0f} GB/s")
+        del qs, outs
+    return out
+
+
 def bench_qtypes(api, workloads, reps=5):
     """The four 4-bit data types (with double quantisation) and NF4 without it
     on a 4096 x 11008 weight: relative RMS error of the dequantised weight
@@ -441,6 +480,7 @@ def main():
         result["quantize"] = bench_quantize(api, workloads)
         result["qtypes"] = bench_qtypes(api, workloads)
         result["int8"] = bench_int8(api, workloads)
+        result["merge"] = bench_merge(api, workloads)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(host)

@@ -36,6 +36,7 @@ EXPORTS = (
     "qlora_status_str", "qlora_last_error", "qlora_nf4_codebook", "qlora_codebook", "qlora_quant_sizes",
     "qlora_quantize", "qlora_dequantize", "qlora_linear_workspace", "qlora_linear_fwd",
     "qlora_linear_bwd", "qlora_set_timing", "qlora_int8_quantize", "qlora_int8_dequantize",
+    "qlora_merge_adapters",
 )
 INT8_BLOCKS = (64, 128, 256, 512, 1024, 2048, 4096)
 QLORA_TIMING_FWD_GEMM = 0
@@ -105,6 +106,8 @@ def _load():
     lib.qlora_linear_bwd.restype = ctypes.c_int
     lib.qlora_set_timing.argtypes = [ctypes.c_int, vp, vp, ctypes.c_int, P(ctypes.c_int)]
     lib.qlora_set_timing.restype = ctypes.c_int
+    lib.qlora_merge_adapters.argtypes = [P(QNF4), vp, vp, ctypes.c_int, ctypes.c_float, vp, vp]
+    lib.qlora_merge_adapters.restype = ctypes.c_int
     lib.qlora_int8_quantize.argtypes = [vp, ctypes.c_int, i64, ctypes.c_int, vp, vp, vp]
     lib.qlora_int8_quantize.restype = ctypes.c_int
     lib.qlora_int8_dequantize.argtypes = [vp, vp, i64, ctypes.c_int, vp, ctypes.c_int, vp]
@@ -321,6 +324,21 @@ def qlora_dequantize(q: NF4Tensor, out=None, stream=None):
     _need(y, torch.bfloat16, (q.rows, q.cols), "out")
     st = q.struct()
     _check(_load().qlora_dequantize(ctypes.byref(st), _ptr(y), _stream(stream)), "qlora_dequantize")
+    return y
+
+
+def qlora_merge_adapters(q: NF4Tensor, L1, L2, scale: float, out=None, stream=None):
+    """bf16 [N][K] = dequant(Wt) + s (L1 L2)^T, rounded once to bf16."""
+    import torch
+
+    K, r = L1.shape
+    _need(L1, torch.bfloat16, (q.cols, r), "L1")
+    _need(L2, torch.bfloat16, (r, q.rows), "L2")
+    y = out if out is not None else torch.empty((q.rows, q.cols), dtype=torch.bfloat16, device=q.codes.device)
+    _need(y, torch.bfloat16, (q.rows, q.cols), "out")
+    st = q.struct()
+    _check(_load().qlora_merge_adapters(ctypes.byref(st), _ptr(L1), _ptr(L2), r, float(scale), _ptr(y),
+                                        _stream(stream)), "qlora_merge_adapters")
     return y
 
 

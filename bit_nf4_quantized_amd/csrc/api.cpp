@@ -261,6 +261,17 @@ int qlora_int8_dequantize(const int8_t* codes, const float* absmax, int64_t nume
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 
+int qlora_merge_adapters(const qlora_nf4* W, const uint16_t* L1, const uint16_t* L2, int r, float scale,
+                         uint16_t* out, hipStream_t stream) {
+  const int st = check_linear(W, 0, r, scale);
+  if (st != QLORA_OK) return st;
+  if (!L1 || !L2 || !out) return QLORA_ERR_ARG;
+  if (!aligned16(L1) || !aligned16(L2) || !aligned16(out)) return QLORA_ERR_ALIGN;
+  (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
+  const hipError_t e = qlora::launch_merge(view_of(W), tables(W->qtype).tab, L1, L2, r, scale, out, stream);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
+
 int qlora_linear_workspace(int64_t M, int64_t K, int64_t N, int r, size_t* bytes) {
   if (!bytes) return QLORA_ERR_ARG;
   if (r < 8 || r > QLORA_MAX_RANK || (r % 8) != 0) return QLORA_ERR_ARG;

@@ -98,6 +98,24 @@ __device__ __forceinline__ float block_const(const NF4View& W, int64_t blk, floa
 // The DQ mean (unused, 0, without double quantisation).
 __device__ __forceinline__ float tensor_mean(const NF4View& W) { return W.absmax32 ? 0.0f : W.mean[0]; }
 
+// Compute units of the current device, queried once (every device this
+// library runs on is the same part); 256 if the query fails.
+inline int device_cu_count() {
+  static int cus = 0;
+  if (cus <= 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      cus = n;
+    (void)hipGetLastError();
+    if (cus <= 0) cus = 256;
+  }
+  return cus;
+}
+
+// Adapter merge into the bf16 dequantised base (merge.hip).
+hipError_t launch_merge(const NF4View& W, const NF4Table& tab, const uint16_t* L1, const uint16_t* L2, int r,
+                        float s, uint16_t* out, hipStream_t stream);
+
 // Skinny adapter products (rank <= 64), skinny_gemm.hip.
 struct SkinnySplit {
   int Z;        // reduction slices

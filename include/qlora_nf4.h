@@ -263,6 +263,25 @@ int qlora_linear_bwd(const qlora_nf4 *W, const uint16_t *X, const uint16_t *dY, 
                      qlora_dtype grad_dtype, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * qlora_merge_adapters: the trained adapters merged into the bf16
+ * dequantised base, for inference without the adapter branch (neura.market
+ * "QLoRA", pitfalls list: merge into the 16-bit dequantised base, never back
+ * into the 4-bit one; diycv.top, section 关键公式 for the dequant):
+ *   out[n][k] = bf16_RNE(RN32(Wd[n][k] + RN32(s * D[k][n]))),
+ *   Wd = bf16(RN32(q[code] * a')) as in qlora_dequantize,
+ *   D  = L1 L2 with bf16 operands and fp32 accumulation,
+ * so that X out^T is the layer of qlora_linear_fwd up to rounding.
+ *   W      host struct of the quantised weight [N][K].
+ *   L1     device bf16 [K][r];  L2 device bf16 [r][N].
+ *   scale  the LoRA scale s (finite).
+ *   out    device bf16 [N][K] (uint16_t bits), 16-byte aligned.
+ * Shape rules as for qlora_linear_fwd (K a multiple of 64, N of 8, r a
+ * multiple of 8 in [8, 256]). The 4-bit weight is left unchanged.
+ */
+int qlora_merge_adapters(const qlora_nf4 *W, const uint16_t *L1, const uint16_t *L2, int r, float scale,
+                         uint16_t *out, hipStream_t stream);
+
+/*
  * qlora_set_timing: measurement hook; it changes no result. While set on the
  * calling thread for a kernel class, each launch of that class by the
  * entry points above is bracketed by hipEventRecord(start[i]) and

@@ -38,7 +38,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     assert sorted(api.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -193,6 +193,23 @@ def test_linear_validation(lib):
     assert b(ctypes.byref(W), X, dY, 64, L1, L2, 8, 2.0, None, p(0x27000004), g1, g2, 0, ws, big,
              None) == api.QLORA_ERR_ALIGN
     assert b(ctypes.byref(W), X, dY, 64, L1, L2, 8, 2.0, None, dX, g1, g2, 0, ws, 100, None) == api.QLORA_ERR_WORKSPACE
+
+
+def test_merge_validation(lib):
+    W = fake_nf4(512, 512)
+    p = lambda a: ctypes.c_void_p(a)
+    L1, L2, O = p(0x22000000), p(0x23000000), p(0x24000000)
+    m = lib.qlora_merge_adapters
+    assert m(None, L1, L2, 8, 1.0, O, None) == api.QLORA_ERR_ARG
+    assert m(ctypes.byref(W), L1, L2, 12, 1.0, O, None) == api.QLORA_ERR_ARG       # r not a multiple of 8
+    assert m(ctypes.byref(W), L1, L2, 264, 1.0, O, None) == api.QLORA_ERR_ARG      # r above the maximum
+    assert m(ctypes.byref(W), L1, L2, 8, float("inf"), O, None) == api.QLORA_ERR_ARG
+    assert m(ctypes.byref(fake_nf4(512, 500)), L1, L2, 8, 1.0, O, None) == api.QLORA_ERR_SHAPE
+    assert m(ctypes.byref(fake_nf4(20, 512)), L1, L2, 8, 1.0, O, None) == api.QLORA_ERR_SHAPE
+    assert m(ctypes.byref(W), None, L2, 8, 1.0, O, None) == api.QLORA_ERR_ARG
+    assert m(ctypes.byref(W), L1, L2, 8, 1.0, None, None) == api.QLORA_ERR_ARG
+    assert m(ctypes.byref(W), L1, p(0x23000008), 8, 1.0, O, None) == api.QLORA_ERR_ALIGN
+    assert m(ctypes.byref(W), L1, L2, 8, 1.0, p(0x24000002), None) == api.QLORA_ERR_ALIGN
 
 
 def test_binding_refuses_host_tensors():
