@@ -44,6 +44,7 @@ QLORA_TIMING_DX_GEMM = 1
 QLORA_TIMING_GEMV = 2
 QLORA_TIMING_QUANT = 3
 QLORA_TIMING_DEQUANT = 4
+QLORA_TIMING_MID_GEMM = 5
 
 
 class QNF4(ctypes.Structure):

@@ -14,7 +14,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Optional per-thread event brackets around one kernel class (measurement
 // only; see qlora_set_timing). Classes match the QLORA_TIMING_* constants.
 enum TimingClass { kTimeFwdGemm = 0, kTimeDxGemm = 1, kTimeGemv = 2, kTimeQuant = 3, kTimeDequant = 4,
-                   kTimeClasses = 5 };
+                   kTimeMidGemm = 5, kTimeClasses = 6 };
 
 struct TimingSlot {
   hipEvent_t* start = nullptr;
@@ -111,6 +111,14 @@ inline int device_cu_count() {
   }
   return cus;
 }
+
+// Forward for 16 < M <= kMidMaxM (midm.hip): fused dequant-GEMM over K-slices
+// plus a fixed-order reduction; sT = bf16(s X L1) [M][rp] and l2t = L2^T
+// [N][rp], both zero past r; part holds midm_partial_bytes.
+constexpr int kMidMaxM = 128;
+size_t midm_partial_bytes(int64_t M, int64_t K, int64_t N);
+hipError_t launch_midm(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M, const uint16_t* sT,
+                       const uint16_t* l2t, int rp, float* part, uint16_t* Y, hipStream_t stream);
 
 // Adapter merge into the bf16 dequantised base (merge.hip).
 hipError_t launch_merge(const NF4View& W, const NF4Table& tab, const uint16_t* L1, const uint16_t* L2, int r,

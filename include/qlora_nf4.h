@@ -235,7 +235,8 @@ int qlora_linear_workspace(int64_t M, int64_t K, int64_t N, int r, size_t *bytes
  *   ws     device workspace of qlora_linear_workspace(M, K, N, r) bytes.
  * Shapes: M >= 0; K a positive multiple of 64; N a positive multiple of 8;
  * r a multiple of 8 in [8, 256]. M <= 16 takes the bandwidth-bound GEMV
- * kernel, larger M the MFMA GEMM; both return the same layer.
+ * kernel, 16 < M <= 128 a one-pass fused dequant-GEMM over K-slices with a
+ * fixed-order reduction, larger M the MFMA GEMM; all return the same layer.
  */
 int qlora_linear_fwd(const qlora_nf4 *W, const uint16_t *X, int64_t M, const uint16_t *L1,
                      const uint16_t *L2, int r, float scale, uint16_t *Y, uint16_t *T_out,
@@ -291,11 +292,13 @@ int qlora_merge_adapters(const qlora_nf4 *W, const uint16_t *L1, const uint16_t 
  * hook for that class. The event arrays and count are host memory owned by
  * the caller and must stay valid while the hook is set; the events must
  * have been created by the caller (hipEventCreate).
- *   kernel  QLORA_TIMING_FWD_GEMM  fused dequant-GEMM producing Y (M > 16)
+ *   kernel  QLORA_TIMING_FWD_GEMM  fused dequant-GEMM producing Y (M > 128)
  *           QLORA_TIMING_DX_GEMM   fused transposed-dequant GEMM producing dX
  *           QLORA_TIMING_GEMV      small-M dequant-GEMV producing Y (M <= 16)
  *           QLORA_TIMING_QUANT     first quantisation pass (codes + absmax)
  *           QLORA_TIMING_DEQUANT   standalone dequant kernel
+ *           QLORA_TIMING_MID_GEMM  forward for 16 < M <= 128: the fused
+ *                                  dequant-GEMM and its K-slice reduction
  * Returns QLORA_ERR_ARG for an unknown class or negative n.
  */
 enum {
@@ -304,7 +307,8 @@ enum {
   QLORA_TIMING_GEMV = 2,
   QLORA_TIMING_QUANT = 3,
   QLORA_TIMING_DEQUANT = 4,
-  QLORA_TIMING_CLASSES = 5
+  QLORA_TIMING_MID_GEMM = 5,
+  QLORA_TIMING_CLASSES = 6
 };
 int qlora_set_timing(int kernel, hipEvent_t *start, hipEvent_t *stop, int n, int *count);
 

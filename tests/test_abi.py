@@ -223,6 +223,7 @@ def test_binding_refuses_host_tensors():
 def test_set_timing_validation(lib):
     cnt = ctypes.c_int(0)
     assert lib.qlora_set_timing(-1, None, None, 0, None) == api.QLORA_ERR_ARG
-    assert lib.qlora_set_timing(5, None, None, 0, None) == api.QLORA_ERR_ARG
+    assert lib.qlora_set_timing(6, None, None, 0, None) == api.QLORA_ERR_ARG
+    assert lib.qlora_set_timing(5, None, None, 0, None) == api.QLORA_OK
     assert lib.qlora_set_timing(0, None, None, -2, ctypes.byref(cnt)) == api.QLORA_ERR_ARG
     assert lib.qlora_set_timing(0, None, None, 0, None) == api.QLORA_OK       # clearing is always fine

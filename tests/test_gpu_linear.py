@@ -78,7 +78,7 @@ def test_tiny_512(api):
 @pytest.mark.parametrize("M,K,N,r,s,kind", [
     (200, 320, 136, 16, 0.5, "normal"),          # ragged M and N tiles
     (384, 1024, 768, 64, 0.25, "normal"),        # several tiles each way
-    (17, 256, 264, 8, 1.0, "student-t4"),        # smallest GEMM-path M
+    (17, 256, 264, 8, 1.0, "student-t4"),        # smallest M above the GEMV (fused one-pass forward)
     (130, 64 * 7, 8 * 41, 256, 0.125, "normal"),  # largest rank, ragged everything
 ])
 def test_shapes(api, M, K, N, r, s, kind):
@@ -121,6 +121,45 @@ def test_gemv_paths(api, M, K, N, r):
     inp = case(M, K, N, r, 0.25, 300 + M + K + N, with_grad=False)
     ref, _ = oracle_case(inp)
     compare(run_case(api, inp, need_bwd=False), ref, f"gemv {M}x{K}x{N} r={r}")
+
+
+@pytest.mark.parametrize("M,K,N,r", [
+    (24, 64 * 9, 8 * 13, 24),     # ragged 64-row tile, odd number of k-steps, r not a multiple of 64
+    (32, 1024, 520, 64),
+    (33, 2048, 1000, 72),         # X tile of 64 rows; two LoRA steps
+    (64, 4096, 200, 256),         # largest rank: four LoRA steps
+    (100, 512, 8 * 300, 16),      # X tile of 128 rows, padded
+    (128, 4096, 4096, 64),        # several K-slices per tile
+    (128, 64, 64, 8),             # one k-step: a single slice, no reduction
+])
+def test_mid_m_forward(api, M, K, N, r):
+    say(f"mid-M forward M={M} K={K} N={N} r={r}")
+    inp = case(M, K, N, r, 0.5, 300 + M + K, with_grad=False)
+    ref, _ = oracle_case(inp)
+    compare(run_case(api, inp, need_bwd=False), ref, f"mid-M {M}x{K}x{N} r={r}")
+
+
+@pytest.mark.parametrize("M", [40, 128])
+def test_mid_m_one_hot_reproduces_dequant(api, M):
+    """Rows of X that are unit vectors with L2 = 0 give rows of the dequantised
+    weight exactly, through the K-slices and their reduction."""
+    import torch
+
+    say(f"mid-M one-hot rows M={M}")
+    K, N = 2048, 200
+    rng = np.random.default_rng(12 + M)
+    W = workloads.random_weight(rng, N * K, "normal").reshape(N, K)
+    q, _ = gpu_quantize(api, W)
+    Wd = nf4.bf16_bits_to_f32(nf4.dequantize(nf4.quantize(W), (N, K)))
+    ks = rng.choice(K, M, replace=False)
+    Xh = np.zeros((M, K), np.float32)
+    Xh[np.arange(M), ks] = 1.0
+    L1 = workloads.to_bf16_bits(rng.standard_normal((K, 8)).astype(np.float32))
+    Y, T = api.qlora_linear_fwd(q, dev(api, workloads.to_bf16_bits(Xh)), dev(api, L1),
+                                dev(api, np.zeros((8, N), np.uint16)), 1.0, want_T=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(nf4.bf16_bits_to_f32(api.to_host_bits(Y)), Wd[:, ks].T)
+    np.testing.assert_array_equal(api.to_host_bits(T), L1[ks])      # T = X L1 picks rows of L1
 
 
 def test_lora_only_and_zero_adapter(api):
