@@ -31,6 +31,7 @@ The same run also measures:
     storage bits per parameter and quantise GB/s;
   * the blockwise Int8 absmax codec: quantise and dequantise GB/s on the
     LLaMA-65B gate-shaped tensor, and the error by block size (64 .. 4096);
+  * the batched-decode forward at M in {32, 64, 128};
   * the adapter merge (bf16 dequantised base + s L1 L2, r = 64) in GB/s on
     the LLaMA-7B linear shapes;
   * the CPU oracle on the same step (all 7 linears, 8192 tokens) as a
@@ -316,6 +317,50 @@ def bench_merge(api, workloads, reps=10):
     return out
 
 
+def bench_mid_m(api, workloads, reps=5):
+    """Batched decode forward, M in {32, 64, 128}, on the LLaMA-7B linear
+    shapes (r = 64): whole call and the fused dequant-GEMM + reduction
+    (HIP events on the call's stream), weights cycled over 8 copies."""
+    import numpy as np
+    import torch
+
+    out = []
+    for K, N in ((4096, 4096), (4096, 11008), (11008, 4096)):
+        rng = np.random.default_rng(K + 2 * N)
+        q0 = api.qlora_quantize(torch.from_numpy(workloads.draw_weight(rng, N, K, "normal", 0.02)).cuda())
+        copies = 8
+        qs = [api.NF4Tensor(q0.rows, q0.cols, q0.codes.clone(), q0.absmax8.clone(), q0.scale2.clone(),
+                            q0.mean.clone()) for _ in range(copies)]
+        L1 = (0.01 * torch.randn(K, 64, device="cuda")).to(torch.bfloat16)
+        L2 = (0.01 * torch.randn(64, N, device="cuda")).to(torch.bfloat16)
+        for M in (32, 64, 128):
+            X = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+            Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+            ws = torch.empty(api.qlora_linear_workspace(M, K, N, 64), dtype=torch.uint8, device="cuda")
+            for i in range(copies):
+                api.qlora_linear_fwd(qs[i], X, L1, L2, 0.25, Y=Y, workspace=ws)
+            n = copies * reps
+            timer = api.KernelTimer(api.QLORA_TIMING_MID_GEMM, capacity=n)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            with timer:
+                e0.record()
+                for i in range(n):
+                    api.qlora_linear_fwd(qs[i % copies], X, L1, L2, 0.25, Y=Y, workspace=ws)
+                e1.record()
+            torch.cuda.synchronize()
+            call_us = e0.elapsed_time(e1) / n * 1e3
+            d = timer.durations_ms()
+            k_us = sum(d) / len(d) * 1e3
+            flops = 2 * M * N * K + 2 * M * 64 * (K + N)
+            out.append({"K": K, "N": N, "M": M, "call_us": call_us, "kernel_us": k_us,
+                        "kernel_weight_GBps": nf4_bytes(K, N) / (k_us * 1e-6) / 1e9,
+                        "call_tflops": flops / (call_us * 1e-6) / 1e12})
+            log(f"mid-M {K}->{N} M={M}: call {call_us:.1f} us, fused kernel + reduce {k_us:.1f} us")
+        del qs
+    return out
+
+
 def bench_qtypes(api, workloads, reps=5):
     """The four 4-bit data types (with double quantisation) and NF4 without it
     on a 4096 x 11008 weight: relative RMS error of the dequantised weight
@@ -481,6 +526,7 @@ def main():
         result["qtypes"] = bench_qtypes(api, workloads)
         result["int8"] = bench_int8(api, workloads)
         result["merge"] = bench_merge(api, workloads)
+        result["mid_m"] = bench_mid_m(api, workloads)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(host)
