@@ -31,6 +31,7 @@ The same run also measures:
     storage bits per parameter and quantise GB/s;
   * the blockwise Int8 absmax codec: quantise and dequantise GB/s on the
     LLaMA-65B gate-shaped tensor, and the error by block size (64 .. 4096);
+  * the same step with LoRA dropout 0.1 on every adapter;
   * the batched-decode forward at M in {32, 64, 128};
   * the adapter merge (bf16 dequantised base + s L1 L2, r = 64) in GB/s on
     the LLaMA-7B linear shapes;
@@ -107,6 +108,37 @@ def run_step(api, layers, ws):
         api.qlora_linear_fwd(d["q"], d["X"], d["L1"], d["L2"], d["s"], Y=d["Y"], T_out=d["T"], workspace=ws)
         api.qlora_linear_bwd(d["q"], d["X"], d["dY"], d["L1"], d["L2"], d["s"], T=d["T"], dX=d["dX"],
                              dL1=d["dL1"], dL2=d["dL2"], workspace=ws)
+
+
+def bench_dropout_step(api, layers, flops_step, plain_ms, steps=5, warmup=2, p=0.1, seed=2024):
+    """The same fwd+bwd step with LoRA dropout p = 0.1 on every adapter
+    (the 7B/13B Guanaco setting): ms per step and the cost over the plain step."""
+    import torch
+
+    ws_bytes = max(api.qlora_linear_workspace_dropout(d["M"], d["shape"].K, d["shape"].N, d["r"]) for d in layers)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        for d in layers:
+            api.qlora_linear_fwd(d["q"], d["X"], d["L1"], d["L2"], d["s"], Y=d["Y"], T_out=d["T"], workspace=ws,
+                                 dropout=(p, seed + i))
+            api.qlora_linear_bwd(d["q"], d["X"], d["dY"], d["L1"], d["L2"], d["s"], T=d["T"], dX=d["dX"],
+                                 dL1=d["dL1"], dL2=d["dL2"], workspace=ws, dropout=(p, seed + i))
+
+    for i in range(warmup):
+        step(i)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    log(f"dropout step (p = {p}): {ms:.3f} ms, {flops_step / (ms * 1e-3) / 1e12:.1f} TFLOP/s, "
+        f"{100 * (ms / plain_ms - 1):.1f} % over the plain step")
+    del ws
+    return {"p": p, "ms_per_step": ms, "tflops": flops_step / (ms * 1e-3) / 1e12, "overhead_vs_plain": ms / plain_ms - 1}
 
 
 def gemm_traffic():
@@ -518,7 +550,13 @@ def main():
         "roofline": roofline,
         "kernels": {"fwd_gemm": kf, "dx_gemm": kd},
     }
-    del layers, ws
+    if not args.no_extras:
+        del ws
+        torch.cuda.empty_cache()
+        result["dropout_step"] = bench_dropout_step(api, layers, flops_step, ms_step)
+        del layers
+    else:
+        del layers, ws
     torch.cuda.empty_cache()
     if not args.no_extras:
         result["gemv"] = bench_gemv(api, workloads)

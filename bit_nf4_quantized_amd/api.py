@@ -36,7 +36,8 @@ EXPORTS = (
     "qlora_status_str", "qlora_last_error", "qlora_nf4_codebook", "qlora_codebook", "qlora_quant_sizes",
     "qlora_quantize", "qlora_dequantize", "qlora_linear_workspace", "qlora_linear_fwd",
     "qlora_linear_bwd", "qlora_set_timing", "qlora_int8_quantize", "qlora_int8_dequantize",
-    "qlora_merge_adapters",
+    "qlora_merge_adapters", "qlora_linear_workspace_dropout", "qlora_linear_fwd_dropout",
+    "qlora_linear_bwd_dropout", "qlora_lora_dropout",
 )
 INT8_BLOCKS = (64, 128, 256, 512, 1024, 2048, 4096)
 QLORA_TIMING_FWD_GEMM = 0
@@ -107,6 +108,17 @@ def _load():
     lib.qlora_linear_bwd.restype = ctypes.c_int
     lib.qlora_set_timing.argtypes = [ctypes.c_int, vp, vp, ctypes.c_int, P(ctypes.c_int)]
     lib.qlora_set_timing.restype = ctypes.c_int
+    u64 = ctypes.c_uint64
+    lib.qlora_linear_workspace_dropout.argtypes = [i64, i64, i64, ctypes.c_int, P(sz)]
+    lib.qlora_linear_workspace_dropout.restype = ctypes.c_int
+    lib.qlora_linear_fwd_dropout.argtypes = [P(QNF4), vp, i64, vp, vp, ctypes.c_int, ctypes.c_float, ctypes.c_float,
+                                             u64, vp, vp, vp, sz, vp]
+    lib.qlora_linear_fwd_dropout.restype = ctypes.c_int
+    lib.qlora_linear_bwd_dropout.argtypes = [P(QNF4), vp, vp, i64, vp, vp, ctypes.c_int, ctypes.c_float,
+                                             ctypes.c_float, u64, vp, vp, vp, vp, ctypes.c_int, vp, sz, vp]
+    lib.qlora_linear_bwd_dropout.restype = ctypes.c_int
+    lib.qlora_lora_dropout.argtypes = [vp, i64, ctypes.c_float, u64, vp, vp]
+    lib.qlora_lora_dropout.restype = ctypes.c_int
     lib.qlora_merge_adapters.argtypes = [P(QNF4), vp, vp, ctypes.c_int, ctypes.c_float, vp, vp]
     lib.qlora_merge_adapters.restype = ctypes.c_int
     lib.qlora_int8_quantize.argtypes = [vp, ctypes.c_int, i64, ctypes.c_int, vp, vp, vp]
@@ -187,6 +199,24 @@ def qlora_linear_workspace(M: int, K: int, N: int, r: int) -> int:
     out = ctypes.c_size_t()
     _check(_load().qlora_linear_workspace(M, K, N, r, ctypes.byref(out)), "qlora_linear_workspace")
     return out.value
+
+
+def qlora_linear_workspace_dropout(M: int, K: int, N: int, r: int) -> int:
+    out = ctypes.c_size_t()
+    _check(_load().qlora_linear_workspace_dropout(M, K, N, r, ctypes.byref(out)), "qlora_linear_workspace_dropout")
+    return out.value
+
+
+def qlora_lora_dropout(X, p: float, seed: int, out=None, stream=None):
+    """The dropped adapter input Xd of a bf16 device tensor (same shape)."""
+    import torch
+
+    _need(X, torch.bfloat16, tuple(X.shape), "X")
+    y = out if out is not None else torch.empty_like(X)
+    _need(y, torch.bfloat16, tuple(X.shape), "out")
+    _check(_load().qlora_lora_dropout(_ptr(X), X.numel(), float(p), int(seed), _ptr(y), _stream(stream)),
+           "qlora_lora_dropout")
+    return y
 
 
 class KernelTimer:
@@ -385,8 +415,9 @@ def qlora_int8_dequantize(codes, absmax, block: int = 64, dtype=None, out=None, 
 
 
 def qlora_linear_fwd(q: NF4Tensor, X, L1, L2, scale: float, want_T: bool = False, Y=None, T_out=None,
-                     workspace=None, stream=None):
-    """Y = X dequant(Wt)^T + s (X L1) L2; returns (Y, T) with T = bf16(X L1) or None."""
+                     workspace=None, stream=None, dropout=None):
+    """Y = X dequant(Wt)^T + s (X L1) L2; returns (Y, T) with T = bf16(X L1) or None.
+    ``dropout=(p, seed)`` applies LoRA dropout to the adapter branch's input."""
     import torch
 
     M, K = X.shape
@@ -403,17 +434,26 @@ def qlora_linear_fwd(q: NF4Tensor, X, L1, L2, scale: float, want_T: bool = False
         T_out = torch.empty((M, r), dtype=torch.bfloat16, device=X.device)
     if T_out is not None:
         _need(T_out, torch.bfloat16, (M, r), "T_out")
-    ws = _workspace(qlora_linear_workspace(M, K, N, r), X.device, workspace)
     st = q.struct()
-    _check(_load().qlora_linear_fwd(ctypes.byref(st), _ptr(X), M, _ptr(L1), _ptr(L2), r, float(scale), _ptr(Y),
-                                    _ptr(T_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
-           "qlora_linear_fwd")
+    if dropout is None:
+        ws = _workspace(qlora_linear_workspace(M, K, N, r), X.device, workspace)
+        _check(_load().qlora_linear_fwd(ctypes.byref(st), _ptr(X), M, _ptr(L1), _ptr(L2), r, float(scale), _ptr(Y),
+                                        _ptr(T_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+               "qlora_linear_fwd")
+    else:
+        p, seed = dropout
+        ws = _workspace(qlora_linear_workspace_dropout(M, K, N, r), X.device, workspace)
+        _check(_load().qlora_linear_fwd_dropout(ctypes.byref(st), _ptr(X), M, _ptr(L1), _ptr(L2), r, float(scale),
+                                                float(p), int(seed), _ptr(Y), _ptr(T_out), _ptr(ws),
+                                                ws.numel() * ws.element_size(), _stream(stream)),
+               "qlora_linear_fwd_dropout")
     return Y, T_out
 
 
 def qlora_linear_bwd(q: NF4Tensor, X, dY, L1, L2, scale: float, T=None, need_dX: bool = True,
-                     grad_dtype=None, dX=None, dL1=None, dL2=None, workspace=None, stream=None):
-    """Returns (dX or None, dL1, dL2) of the QLoRA linear for upstream gradient dY."""
+                     grad_dtype=None, dX=None, dL1=None, dL2=None, workspace=None, stream=None, dropout=None):
+    """Returns (dX or None, dL1, dL2) of the QLoRA linear for upstream gradient dY
+    (``dropout=(p, seed)``: the same LoRA dropout as the forward)."""
     import torch
 
     grad_dtype = torch.float32 if grad_dtype is None else grad_dtype
@@ -437,12 +477,20 @@ def qlora_linear_bwd(q: NF4Tensor, X, dY, L1, L2, scale: float, T=None, need_dX:
     dL2 = dL2 if dL2 is not None else torch.empty((r, N), dtype=grad_dtype, device=X.device)
     _need(dL1, grad_dtype, (K, r), "dL1")
     _need(dL2, grad_dtype, (r, N), "dL2")
-    ws = _workspace(qlora_linear_workspace(M, K, N, r), X.device, workspace)
     st = q.struct()
     gd = QLORA_F32 if grad_dtype == torch.float32 else QLORA_BF16
-    _check(_load().qlora_linear_bwd(ctypes.byref(st), _ptr(X), _ptr(dY), M, _ptr(L1), _ptr(L2), r, float(scale),
-                                    _ptr(T), _ptr(dX), _ptr(dL1), _ptr(dL2), gd, _ptr(ws),
-                                    ws.numel() * ws.element_size(), _stream(stream)), "qlora_linear_bwd")
+    if dropout is None:
+        ws = _workspace(qlora_linear_workspace(M, K, N, r), X.device, workspace)
+        _check(_load().qlora_linear_bwd(ctypes.byref(st), _ptr(X), _ptr(dY), M, _ptr(L1), _ptr(L2), r,
+                                        float(scale), _ptr(T), _ptr(dX), _ptr(dL1), _ptr(dL2), gd, _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream)), "qlora_linear_bwd")
+    else:
+        p, seed = dropout
+        ws = _workspace(qlora_linear_workspace_dropout(M, K, N, r), X.device, workspace)
+        _check(_load().qlora_linear_bwd_dropout(ctypes.byref(st), _ptr(X), _ptr(dY), M, _ptr(L1), _ptr(L2), r,
+                                                float(scale), float(p), int(seed), _ptr(T), _ptr(dX), _ptr(dL1),
+                                                _ptr(dL2), gd, _ptr(ws), ws.numel() * ws.element_size(),
+                                                _stream(stream)), "qlora_linear_bwd_dropout")
     return dX, dL1, dL2
 
 

@@ -281,9 +281,20 @@ int qlora_linear_workspace(int64_t M, int64_t K, int64_t N, int r, size_t* bytes
   return QLORA_OK;
 }
 
-int qlora_linear_fwd(const qlora_nf4* W, const uint16_t* X, int64_t M, const uint16_t* L1, const uint16_t* L2,
-                     int r, float scale, uint16_t* Y, uint16_t* T_out, void* ws, size_t ws_bytes,
-                     hipStream_t stream) {
+int qlora_linear_workspace_dropout(int64_t M, int64_t K, int64_t N, int r, size_t* bytes) {
+  const int st = qlora_linear_workspace(M, K, N, r, bytes);
+  if (st != QLORA_OK) return st;
+  *bytes = qlora::linear_workspace_layout(M, K, N, r, true).total;
+  return QLORA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+int linear_fwd_impl(const qlora_nf4* W, const uint16_t* X, int64_t M, const uint16_t* L1, const uint16_t* L2, int r,
+                    float scale, uint16_t* Y, uint16_t* T_out, void* ws, size_t ws_bytes, hipStream_t stream,
+                    const qlora::DropoutParams* dr) {
   int st = check_linear(W, M, r, scale);
   if (st != QLORA_OK) return st;
   if (!L1 || !L2) return QLORA_ERR_ARG;
@@ -291,15 +302,18 @@ int qlora_linear_fwd(const qlora_nf4* W, const uint16_t* X, int64_t M, const uin
   if (!ws) return QLORA_ERR_WORKSPACE;
   if (!aligned16(X) || !aligned16(L1) || !aligned16(L2) || !aligned16(Y) || !aligned16(T_out) || !aligned16(ws))
     return QLORA_ERR_ALIGN;
-  if (ws_bytes < qlora::linear_workspace_layout(M, W->cols, W->rows, r).total) return QLORA_ERR_WORKSPACE;
+  if (ws_bytes < qlora::linear_workspace_layout(M, W->cols, W->rows, r, dr != nullptr).total)
+    return QLORA_ERR_WORKSPACE;
   (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
-  const hipError_t e = qlora::linear_forward(view_of(W), tables(W->qtype).tab, X, M, L1, L2, r, scale, Y, T_out, ws, stream);
+  const hipError_t e = qlora::linear_forward(view_of(W), tables(W->qtype).tab, X, M, L1, L2, r, scale, Y, T_out, ws,
+                                             stream, dr);
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 
-int qlora_linear_bwd(const qlora_nf4* W, const uint16_t* X, const uint16_t* dY, int64_t M, const uint16_t* L1,
-                     const uint16_t* L2, int r, float scale, const uint16_t* T, uint16_t* dX, void* dL1,
-                     void* dL2, qlora_dtype grad_dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
+int linear_bwd_impl(const qlora_nf4* W, const uint16_t* X, const uint16_t* dY, int64_t M, const uint16_t* L1,
+                    const uint16_t* L2, int r, float scale, const uint16_t* T, uint16_t* dX, void* dL1, void* dL2,
+                    qlora_dtype grad_dtype, void* ws, size_t ws_bytes, hipStream_t stream,
+                    const qlora::DropoutParams* dr) {
   int st = check_linear(W, M, r, scale);
   if (st != QLORA_OK) return st;
   if (grad_dtype != QLORA_F32 && grad_dtype != QLORA_BF16) return QLORA_ERR_ARG;
@@ -309,10 +323,57 @@ int qlora_linear_bwd(const qlora_nf4* W, const uint16_t* X, const uint16_t* dY, 
   if (!aligned16(X) || !aligned16(dY) || !aligned16(L1) || !aligned16(L2) || !aligned16(T) || !aligned16(dX) ||
       !aligned16(dL1) || !aligned16(dL2) || !aligned16(ws))
     return QLORA_ERR_ALIGN;
-  if (ws_bytes < qlora::linear_workspace_layout(M, W->cols, W->rows, r).total) return QLORA_ERR_WORKSPACE;
+  if (ws_bytes < qlora::linear_workspace_layout(M, W->cols, W->rows, r, dr != nullptr).total)
+    return QLORA_ERR_WORKSPACE;
   (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
   const hipError_t e = qlora::linear_backward(view_of(W), tables(W->qtype).tab, X, dY, M, L1, L2, r, scale, T, dX, dL1,
-                                              dL2, grad_dtype == QLORA_BF16, ws, stream);
+                                              dL2, grad_dtype == QLORA_BF16, ws, stream, dr);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
+
+bool valid_dropout(float p) { return isfinite(p) && p >= 0.0f && p < 1.0f; }
+
+}  // namespace
+
+extern "C" {
+
+int qlora_linear_fwd(const qlora_nf4* W, const uint16_t* X, int64_t M, const uint16_t* L1, const uint16_t* L2,
+                     int r, float scale, uint16_t* Y, uint16_t* T_out, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  return linear_fwd_impl(W, X, M, L1, L2, r, scale, Y, T_out, ws, ws_bytes, stream, nullptr);
+}
+
+int qlora_linear_bwd(const qlora_nf4* W, const uint16_t* X, const uint16_t* dY, int64_t M, const uint16_t* L1,
+                     const uint16_t* L2, int r, float scale, const uint16_t* T, uint16_t* dX, void* dL1,
+                     void* dL2, qlora_dtype grad_dtype, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return linear_bwd_impl(W, X, dY, M, L1, L2, r, scale, T, dX, dL1, dL2, grad_dtype, ws, ws_bytes, stream, nullptr);
+}
+
+int qlora_linear_fwd_dropout(const qlora_nf4* W, const uint16_t* X, int64_t M, const uint16_t* L1,
+                             const uint16_t* L2, int r, float scale, float p, uint64_t seed, uint16_t* Y,
+                             uint16_t* T_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dropout(p)) return QLORA_ERR_ARG;
+  const qlora::DropoutParams d = qlora::dropout_params(p, seed);
+  return linear_fwd_impl(W, X, M, L1, L2, r, scale, Y, T_out, ws, ws_bytes, stream, &d);
+}
+
+int qlora_linear_bwd_dropout(const qlora_nf4* W, const uint16_t* X, const uint16_t* dY, int64_t M,
+                             const uint16_t* L1, const uint16_t* L2, int r, float scale, float p, uint64_t seed,
+                             const uint16_t* T, uint16_t* dX, void* dL1, void* dL2, qlora_dtype grad_dtype,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!valid_dropout(p)) return QLORA_ERR_ARG;
+  const qlora::DropoutParams d = qlora::dropout_params(p, seed);
+  return linear_bwd_impl(W, X, dY, M, L1, L2, r, scale, T, dX, dL1, dL2, grad_dtype, ws, ws_bytes, stream, &d);
+}
+
+int qlora_lora_dropout(const uint16_t* X, int64_t numel, float p, uint64_t seed, uint16_t* Xd, hipStream_t stream) {
+  if (!valid_dropout(p)) return QLORA_ERR_ARG;
+  if (numel < 0 || (numel % 8) != 0 || numel > ((int64_t)1 << 40)) return QLORA_ERR_SHAPE;
+  if (numel == 0) return QLORA_OK;
+  if (!X || !Xd) return QLORA_ERR_ARG;
+  if (!aligned16(X) || !aligned16(Xd)) return QLORA_ERR_ALIGN;
+  (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
+  const hipError_t e = qlora::launch_dropout_input(X, numel, qlora::dropout_params(p, seed), Xd, stream);
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 

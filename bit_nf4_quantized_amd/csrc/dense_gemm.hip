@@ -75,6 +75,8 @@ struct DenseArgs {
   int64_t K2;       // slab reduction, multiple of TK (0 = no slab)
   float alpha;
   int tiles_m, tiles_n;
+  const float* E;   // ADD: fp32 addend [M][N] (row stride lde), C = bf16(alpha acc + E)
+  int64_t lde;
 };
 
 // One stage of one operand: rows [row0, row0+256) x columns [k0, k0+64).
@@ -123,6 +125,7 @@ __device__ __forceinline__ void stage_load(const uint16_t* __restrict__ P, const
 
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * TK + ((chunk ^ swz(row)) << 3); }
 
+template <bool ADD>
 __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(DenseArgs p) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[2][2][kStageElems];  // [buffer][A, B]
 
@@ -231,6 +234,43 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(DenseArgs p) {
   for (; st + 2 < nk; ++st) stage(st, true, true);
   if (st + 1 < nk) stage(st++, false, true);
   if (st < nk) stage(st, false, false);
+
+  if constexpr (ADD) {
+    // Epilogue with an fp32 addend: each wave stages a quarter of its 128 x 64
+    // sub-tile (32 rows, one accumulator row-block) as fp32 in its own padded
+    // LDS slice; then each lane takes 8 consecutive columns of a row, adds the
+    // matching 32 bytes of E and stores 16 bytes of bf16.
+    constexpr int kAddStride = WTN + 4;  // fp32 per padded row
+    __syncthreads();
+    float* ef = reinterpret_cast<float*>(&smem[0][0][0]) + wave * (32 * kAddStride);
+    const int64_t row_base = m0 + wm * WTM, col_base = n0 + wn * WTN;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          ef[((v & 3) + 4 * (lane >> 5) + 8 * (v >> 2)) * kAddStride + j * 32 + (lane & 31)] = p.alpha * acc[i][j][v];
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done (wave-private slice)
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int r = it * 8 + (lane >> 3);
+        const int cc = (lane & 7) * 8;
+        const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(ef + r * kAddStride + cc);
+        const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(ef + r * kAddStride + cc + 4);
+        const int64_t row = row_base + i * 32 + r, col = col_base + cc;
+        const bool in = row < p.M && col < p.N;
+        const float* ep = p.E + (in ? row * p.lde + col : 0);
+        const f32x4_t e0 = *reinterpret_cast<const f32x4_t*>(ep);
+        const f32x4_t e1 = *reinterpret_cast<const f32x4_t*>(ep + 4);
+        const u32x4_t val = {pack_bf16x2(a0.x + e0.x, a0.y + e0.y), pack_bf16x2(a0.z + e0.z, a0.w + e0.w),
+                             pack_bf16x2(a1.x + e1.x, a1.y + e1.y), pack_bf16x2(a1.z + e1.z, a1.w + e1.w)};
+        if (in) *reinterpret_cast<u32x4_t*>(p.C + row * p.ldc + col) = val;
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // reads of this quarter done before the next overwrites it
+    }
+    return;
+  }
 
   // Epilogue through LDS (the stage buffers are free now): each wave writes
   // half of its 128 x 64 sub-tile (64 rows) as bf16 into its own padded LDS
@@ -375,15 +415,20 @@ hipError_t launch_dequant_cols(const NF4View& W, const NF4Table& tab, uint16_t* 
 
 hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
                           int64_t M, int64_t N, int64_t K, const uint16_t* A2, const uint16_t* B2, int64_t ld2,
-                          int64_t K2, uint16_t* C, int64_t ldc, float alpha, hipStream_t stream) {
+                          int64_t K2, uint16_t* C, int64_t ldc, float alpha, hipStream_t stream, const float* E,
+                          int64_t lde) {
   DenseArgs p;
   p.A = A; p.B = B; p.A2 = A2; p.B2 = B2; p.C = C;
   p.lda = lda; p.ldb = ldb; p.ld2 = ld2; p.ldc = ldc;
   p.M = M; p.N = N; p.K = K; p.K2 = K2; p.alpha = alpha;
   p.tiles_m = (int)((M + TM - 1) / TM);
   p.tiles_n = (int)((N + TN - 1) / TN);
+  p.E = E; p.lde = lde;
   const int ntiles = p.tiles_m * p.tiles_n;
-  hipLaunchKernelGGL(gemm_nt_kernel, dim3((unsigned)ntiles), dim3(kThreads), 0, stream, p);
+  if (E)
+    hipLaunchKernelGGL(gemm_nt_kernel<true>, dim3((unsigned)ntiles), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(gemm_nt_kernel<false>, dim3((unsigned)ntiles), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -457,7 +457,7 @@ hipError_t launch_small_lora_down(const uint16_t* X, int64_t M, int64_t K, const
 hipError_t launch_gemv(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M,
                        const uint16_t* sT, const uint16_t* L2, int r, uint16_t* Y, hipStream_t stream);
 
-LinearWorkspace linear_workspace_layout(int64_t M, int64_t K, int64_t N, int r) {
+LinearWorkspace linear_workspace_layout(int64_t M, int64_t K, int64_t N, int r, bool dropout) {
   LinearWorkspace L;
   const int64_t mtiles = cdiv(M, BM);
   const int64_t rp = cdiv(r, 64) * 64;  // LoRA slab width, zero-padded to the GEMM K-stage
@@ -488,6 +488,11 @@ LinearWorkspace linear_workspace_layout(int64_t M, int64_t K, int64_t N, int r) 
   L.wd_off = off;
   L.wd_bytes = M > 16 ? align_up((size_t)K * (size_t)(np > N ? np : N) * 2, 256) : 0;
   off += L.wd_bytes;
+  L.xd_off = L.dd_off = off;
+  if (dropout) {
+    L.xd_off = off; off += align_up((size_t)M * K * 2, 256);
+    L.dd_off = off; off += align_up((size_t)M * K * 4, 256);
+  }
   L.total = off > 0 ? off : 256;
   return L;
 }
@@ -544,10 +549,18 @@ static hipError_t lora_down(const uint16_t* X, int64_t M, int64_t K, const uint1
 
 hipError_t linear_forward(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M,
                           const uint16_t* L1, const uint16_t* L2, int r, float s, uint16_t* Y,
-                          uint16_t* T_out, void* ws, hipStream_t stream) {
+                          uint16_t* T_out, void* ws, hipStream_t stream, const DropoutParams* dr) {
   const int64_t K = W.cols, N = W.rows;
   if (M == 0) return hipSuccess;
-  const LinearWorkspace L = linear_workspace_layout(M, K, N, r);
+  const LinearWorkspace L = linear_workspace_layout(M, K, N, r, dr != nullptr);
+  // the adapter branch's input: X, or its dropped copy
+  const uint16_t* Xa = X;
+  if (dr) {
+    uint16_t* xd = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + L.xd_off);
+    hipError_t e = launch_dropout_input(X, M * K, *dr, xd, stream);
+    if (e != hipSuccess) return e;
+    Xa = xd;
+  }
   const int64_t rp = cdiv(r, 64) * 64;
   char* base = static_cast<char*>(ws);
   uint16_t* l2t = reinterpret_cast<uint16_t*>(base + L.l2t_off);
@@ -556,13 +569,13 @@ hipError_t linear_forward(const NF4View& W, const NF4Table& tab, const uint16_t*
 
   uint16_t* l1t = reinterpret_cast<uint16_t*>(base + L.l1t_off);
   if (M <= 16) {
-    hipError_t e = launch_small_lora_down(X, M, K, L1, r, s, sT, r, T_out, part, stream);
+    hipError_t e = launch_small_lora_down(Xa, M, K, L1, r, s, sT, r, T_out, part, stream);
     if (e != hipSuccess) return e;
     return timed(kTimeGemv, stream, [&] { return launch_gemv(W, tab, X, M, sT, L2, r, Y, stream); });
   }
 
   if (M <= kMidMaxM) {   // batched decode: one pass over the 4-bit weight
-    hipError_t e = lora_down(X, M, K, L1, r, s, sT, rp, T_out, part, l1t, stream);
+    hipError_t e = lora_down(Xa, M, K, L1, r, s, sT, rp, T_out, part, l1t, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)cdiv(N, 32), (unsigned)cdiv(rp, 32)), dim3(256), 0,
                        stream, L2, (int64_t)r, N, l2t, rp);
@@ -573,7 +586,7 @@ hipError_t linear_forward(const NF4View& W, const NF4Table& tab, const uint16_t*
 
   const bool dense = fits_dense({M * K * 2, N * K * 2, M * rp * 2, N * rp * 2});
   const int64_t ldst = dense ? rp : r;
-  hipError_t e = lora_down(X, M, K, L1, r, s, sT, ldst, T_out, part, l1t, stream);
+  hipError_t e = lora_down(Xa, M, K, L1, r, s, sT, ldst, T_out, part, l1t, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)cdiv(N, 32), (unsigned)cdiv(ldst, 32)), dim3(256), 0,
                      stream, L2, (int64_t)r, N, l2t, ldst);
@@ -600,9 +613,9 @@ hipError_t linear_forward(const NF4View& W, const NF4Table& tab, const uint16_t*
 hipError_t linear_backward(const NF4View& W, const NF4Table& tab, const uint16_t* X, const uint16_t* dY,
                            int64_t M, const uint16_t* L1, const uint16_t* L2, int r, float s,
                            const uint16_t* T, uint16_t* dX, void* dL1, void* dL2, bool grad_bf16,
-                           void* ws, hipStream_t stream) {
+                           void* ws, hipStream_t stream, const DropoutParams* dr) {
   const int64_t K = W.cols, N = W.rows;
-  const LinearWorkspace L = linear_workspace_layout(M, K, N, r);
+  const LinearWorkspace L = linear_workspace_layout(M, K, N, r, dr != nullptr);
   const int64_t rp = cdiv(r, 64) * 64;
   char* base = static_cast<char*>(ws);
   uint16_t* tbuf = reinterpret_cast<uint16_t*>(base + L.t_off);
@@ -623,6 +636,15 @@ hipError_t linear_backward(const NF4View& W, const NF4Table& tab, const uint16_t
 
   const bool dense = dX && M > 16 && (N % 64) == 0 && fits_dense({M * N * 2, K * N * 2, M * rp * 2, K * rp * 2});
   const int64_t ldsu = dense ? rp : r;
+  // the adapter branch's input: X, or its dropped copy (the same mask as the forward)
+  const uint16_t* Xa = X;
+  float* dd = reinterpret_cast<float*>(base + L.dd_off);
+  if (dr) {
+    uint16_t* xd = reinterpret_cast<uint16_t*>(base + L.xd_off);
+    e = launch_dropout_input(X, M * K, *dr, xd, stream);
+    if (e != hipSuccess) return e;
+    Xa = xd;
+  }
 
   uint16_t* l1t = reinterpret_cast<uint16_t*>(base + L.l1t_off);
   uint16_t* l2p = reinterpret_cast<uint16_t*>(base + L.l2p_off);
@@ -664,9 +686,29 @@ hipError_t linear_backward(const NF4View& W, const NF4Table& tab, const uint16_t
     uint16_t* wdt = reinterpret_cast<uint16_t*>(base + L.wd_off);
     e = launch_dequant_cols(W, tab, wdt, N, stream);
     if (e != hipSuccess) return e;
-    e = timed(kTimeDxGemm, stream, [&] {
-      return launch_gemm_nt(dY, N, wdt, N, M, K, N, sU, l1s, rp, rp, dX, K, 1.0f, stream);
-    });
+    if (dr) {
+      // dropout: the masked LoRA term D in fp32, added in the GEMM's epilogue
+      e = launch_masked_lora(sU, ldsu, L1, r, M, K, *dr, nullptr, dd, nullptr, stream);
+      if (e != hipSuccess) return e;
+      e = timed(kTimeDxGemm, stream, [&] {
+        return launch_gemm_nt(dY, N, wdt, N, M, K, N, sU, l1s, rp, 0, dX, K, 1.0f, stream, dd, K);
+      });
+    } else {
+      e = timed(kTimeDxGemm, stream, [&] {
+        return launch_gemm_nt(dY, N, wdt, N, M, K, N, sU, l1s, rp, rp, dX, K, 1.0f, stream);
+      });
+    }
+    if (e != hipSuccess) return e;
+  } else if (dX && dr) {
+    // dropout, small M or ragged N: the main product in fp32, then dX = bf16(main + D)
+    GemmArgs a = base_args();
+    a.M = M; a.N = K; a.K = N; a.k_split = N;
+    a.A = dY; a.lda = N;
+    a.W = W; a.tab = tab;
+    a.C = dd; a.ldc = K;
+    e = timed(kTimeDxGemm, stream, [&] { return run_gemm<A_ROW, B_NF4T, EPI_F32, false>(a, 1, stream); });
+    if (e != hipSuccess) return e;
+    e = launch_masked_lora(sU, ldsu, L1, r, M, K, *dr, dd, nullptr, dX, stream);
     if (e != hipSuccess) return e;
   } else if (dX) {
     GemmArgs a = base_args();
@@ -680,13 +722,13 @@ hipError_t linear_backward(const NF4View& W, const NF4Table& tab, const uint16_t
   }
   // T = bf16(X L1) unless the caller kept it from the forward pass
   if (!T) {
-    e = lora_down(X, M, K, L1, r, 1.0f, tbuf, r, nullptr, part, l1t, stream);
+    e = lora_down(Xa, M, K, L1, r, 1.0f, tbuf, r, nullptr, part, l1t, stream);
     if (e != hipSuccess) return e;
     T = tbuf;
   }
   if (skinny_ok(r, M, K) && skinny_ok(r, M, N)) {
     // dL1 = X^T sU  ([K][r]);  dL2 = s (dY^T T)^T  ([r][N])
-    e = skinny_tn(X, K, K, sU, ldsu, M, r, part, 1.0f, false, grad_bf16, dL1, stream);
+    e = skinny_tn(Xa, K, K, sU, ldsu, M, r, part, 1.0f, false, grad_bf16, dL1, stream);
     if (e != hipSuccess) return e;
     return skinny_tn(dY, N, N, T, r, M, r, part, s, true, grad_bf16, dL2, stream);
   }
@@ -694,7 +736,7 @@ hipError_t linear_backward(const NF4View& W, const NF4Table& tab, const uint16_t
   {
     GemmArgs a = base_args();
     a.M = K; a.N = r; a.K = M;
-    a.A = X; a.lda = K;
+    a.A = Xa; a.lda = K;
     a.B = sU; a.ldb = ldsu;
     const Split sp = choose_split(cdiv(K, BM) * cdiv(r, BN), M);
     a.k_split = sp.k_split;

@@ -150,25 +150,46 @@ struct LinearWorkspace {
   size_t part_bytes;
   size_t wd_off;     // bf16 dequantised weight for the dense GEMM path
   size_t wd_bytes;
+  size_t xd_off;     // dropout: bf16 [M][K] dropped adapter input
+  size_t dd_off;     // dropout: fp32 [M][K] masked LoRA term of dX (or the main product)
   size_t total;
 };
 
-LinearWorkspace linear_workspace_layout(int64_t M, int64_t K, int64_t N, int r);
+LinearWorkspace linear_workspace_layout(int64_t M, int64_t K, int64_t N, int r, bool dropout = false);
 
 hipError_t launch_dequant_rows(const NF4View& W, const NF4Table& tab, uint16_t* out, hipStream_t stream);
 hipError_t launch_dequant_cols(const NF4View& W, const NF4Table& tab, uint16_t* out, int64_t ldo,
                                hipStream_t stream);
+// E (optional): fp32 addend [M][N] with row stride lde; C = bf16(alpha acc + E).
 hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M, int64_t N,
                           int64_t K, const uint16_t* A2, const uint16_t* B2, int64_t ld2, int64_t K2, uint16_t* C,
-                          int64_t ldc, float alpha, hipStream_t stream);
+                          int64_t ldc, float alpha, hipStream_t stream, const float* E = nullptr,
+                          int64_t lde = 0);
 
+// LoRA dropout (dropout.hip): keep iff the element's Philox word >= thr,
+// kept values scaled by c.
+struct DropoutParams {
+  uint32_t thr;    // floor(p 2^32)
+  float c;         // RN32(1 / (1 - p))
+  uint64_t seed;
+};
+DropoutParams dropout_params(float p, uint64_t seed);
+hipError_t launch_dropout_input(const uint16_t* X, int64_t numel, const DropoutParams& d, uint16_t* Xd,
+                                hipStream_t stream);
+// D[m][k] = keep c sum_j sU[m][j] L1[k][j] (fp32); with F, dX = bf16(F + D) instead.
+hipError_t launch_masked_lora(const uint16_t* sU, int64_t ldsu, const uint16_t* L1, int r, int64_t M, int64_t K,
+                              const DropoutParams& d, const float* F, float* D, uint16_t* dX, hipStream_t stream);
+
+// With dr, the adapter branch reads the dropped input (regenerated from
+// dr's seed in both passes) and the workspace is linear_workspace_layout(...,
+// true).
 hipError_t linear_forward(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M,
                           const uint16_t* L1, const uint16_t* L2, int r, float s, uint16_t* Y,
-                          uint16_t* T_out, void* ws, hipStream_t stream);
+                          uint16_t* T_out, void* ws, hipStream_t stream, const DropoutParams* dr = nullptr);
 
 hipError_t linear_backward(const NF4View& W, const NF4Table& tab, const uint16_t* X, const uint16_t* dY,
                            int64_t M, const uint16_t* L1, const uint16_t* L2, int r, float s,
                            const uint16_t* T, uint16_t* dX, void* dL1, void* dL2, bool grad_bf16,
-                           void* ws, hipStream_t stream);
+                           void* ws, hipStream_t stream, const DropoutParams* dr = nullptr);
 
 }  // namespace qlora

@@ -264,6 +264,41 @@ int qlora_linear_bwd(const qlora_nf4 *W, const uint16_t *X, const uint16_t *dY, 
                      qlora_dtype grad_dtype, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * LoRA dropout on the adapter branch (diycv.top, section 训练与推理流程: the
+ * Guanaco runs use LoRA dropout 0.1 for 7B/13B and 0.05 for 33B/65B). The
+ * adapter branch reads Xd instead of X:
+ *   Xd[m][k] = keep(m, k) ? bf16_RNE(RN32(X[m][k] * c)) : +0,  c = RN32(1 / (1 - p)),
+ *   keep(m, k) = u >= floor(p 2^32), u = word e % 4 of Philox4x32-10 (Salmon
+ *   et al., SC 2011) with counter (lo(e/4), hi(e/4), 0, 0) and key
+ *   (lo(seed), hi(seed)), e = m K + k.
+ * The forward is Y = X Wd^T + s (Xd L1) L2 (T_out = bf16(Xd L1)); the
+ * backward, given the same (p, seed), is
+ *   dX  = dY Wd + keep * c * (bf16(s dY L2^T) L1^T)   (fp32, one bf16 rounding)
+ *   dL1 = s Xd^T (dY L2^T),  dL2 = s (Xd L1)^T dY.
+ * Nothing is stored between the passes: the mask is regenerated from
+ * (p, seed). p must be finite, 0 <= p < 1 (else QLORA_ERR_ARG); other
+ * arguments, shapes and errors as for qlora_linear_fwd / qlora_linear_bwd,
+ * except that the workspace is qlora_linear_workspace_dropout bytes (it adds
+ * 6 M K bytes for Xd and the fp32 masked LoRA term of dX).
+ */
+int qlora_linear_workspace_dropout(int64_t M, int64_t K, int64_t N, int r, size_t *bytes);
+int qlora_linear_fwd_dropout(const qlora_nf4 *W, const uint16_t *X, int64_t M, const uint16_t *L1,
+                             const uint16_t *L2, int r, float scale, float p, uint64_t seed, uint16_t *Y,
+                             uint16_t *T_out, void *ws, size_t ws_bytes, hipStream_t stream);
+int qlora_linear_bwd_dropout(const qlora_nf4 *W, const uint16_t *X, const uint16_t *dY, int64_t M,
+                             const uint16_t *L1, const uint16_t *L2, int r, float scale, float p, uint64_t seed,
+                             const uint16_t *T, uint16_t *dX, void *dL1, void *dL2, qlora_dtype grad_dtype,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * qlora_lora_dropout: the dropped adapter input Xd alone (as above, element
+ * e of a row-major tensor of numel bf16 values; numel a multiple of 8, at
+ * most 2^40). X, Xd: device, 16-byte aligned. Errors: QLORA_ERR_ARG (p, NULL),
+ * QLORA_ERR_SHAPE (numel), QLORA_ERR_ALIGN.
+ */
+int qlora_lora_dropout(const uint16_t *X, int64_t numel, float p, uint64_t seed, uint16_t *Xd, hipStream_t stream);
+
+/*
  * qlora_merge_adapters: the trained adapters merged into the bf16
  * dequantised base, for inference without the adapter branch (neura.market
  * "QLoRA", pitfalls list: merge into the 16-bit dequantised base, never back

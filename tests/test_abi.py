@@ -38,7 +38,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 18, names
     assert sorted(api.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -193,6 +193,31 @@ def test_linear_validation(lib):
     assert b(ctypes.byref(W), X, dY, 64, L1, L2, 8, 2.0, None, p(0x27000004), g1, g2, 0, ws, big,
              None) == api.QLORA_ERR_ALIGN
     assert b(ctypes.byref(W), X, dY, 64, L1, L2, 8, 2.0, None, dX, g1, g2, 0, ws, 100, None) == api.QLORA_ERR_WORKSPACE
+
+
+def test_dropout_validation(lib):
+    W = fake_nf4(512, 512)
+    p = lambda a: ctypes.c_void_p(a)
+    X, L1, L2, Y, ws = p(0x21000000), p(0x22000000), p(0x23000000), p(0x24000000), p(0x25000000)
+    big = 1 << 34
+    f = lib.qlora_linear_fwd_dropout
+    for bad_p in (-0.1, 1.0, 1.5, float("nan"), float("inf")):
+        assert f(ctypes.byref(W), X, 64, L1, L2, 8, 2.0, bad_p, 1, Y, None, ws, big, None) == api.QLORA_ERR_ARG
+        assert lib.qlora_lora_dropout(X, 64, bad_p, 1, Y, None) == api.QLORA_ERR_ARG
+    need = ctypes.c_size_t()
+    plain = api.qlora_linear_workspace(64, 512, 512, 8)
+    assert lib.qlora_linear_workspace_dropout(64, 512, 512, 8, ctypes.byref(need)) == api.QLORA_OK
+    assert need.value >= plain + 6 * 64 * 512
+    # the plain workspace is too small for the dropout variant
+    assert f(ctypes.byref(W), X, 64, L1, L2, 8, 2.0, 0.1, 1, Y, None, ws, plain, None) == api.QLORA_ERR_WORKSPACE
+    b = lib.qlora_linear_bwd_dropout
+    g1, g2 = p(0x28000000), p(0x29000000)
+    assert b(ctypes.byref(W), X, p(0x26000000), 64, L1, L2, 8, 2.0, 1.0, 1, None, None, g1, g2, 0, ws, big,
+             None) == api.QLORA_ERR_ARG
+    assert lib.qlora_lora_dropout(X, 12, 0.1, 1, Y, None) == api.QLORA_ERR_SHAPE       # numel % 8
+    assert lib.qlora_lora_dropout(X, -8, 0.1, 1, Y, None) == api.QLORA_ERR_SHAPE
+    assert lib.qlora_lora_dropout(None, 0, 0.1, 1, None, None) == api.QLORA_OK         # empty
+    assert lib.qlora_lora_dropout(p(0x21000008), 64, 0.1, 1, Y, None) == api.QLORA_ERR_ALIGN
 
 
 def test_merge_validation(lib):
