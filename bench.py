@@ -33,6 +33,8 @@ The same run also measures:
     LLaMA-65B gate-shaped tensor, and the error by block size (64 .. 4096);
   * the same step with LoRA dropout 0.1 on every adapter;
   * the batched-decode forward at M in {32, 64, 128};
+  * the optimiser step (clip + Adam) at the size of all LLaMA-7B adapters,
+    with 0-100 % of the Adam state paged out to pinned host memory;
   * the adapter merge (bf16 dequantised base + s L1 L2, r = 64) in GB/s on
     the LLaMA-7B linear shapes;
   * the CPU oracle on the same step (all 7 linears, 8192 tokens) as a
@@ -393,6 +395,66 @@ def bench_mid_m(api, workloads, reps=5):
     return out
 
 
+def bench_optim(api, reps=3):
+    """The adapters' optimiser step at the size of all LLaMA-7B adapters
+    (r = 64 on the 7 linears of 32 layers, 159.9 M fp32 values): the clip
+    norm, and Adam with the first (1 - f) of the state (m, v) in HBM and the
+    last f in pinned host memory, for f in {0, 0.25, 0.5, 0.75, 1} (one call
+    per placement). The difference to f = 0 is the cost of paged-out state."""
+    import torch
+
+    n = 32 * 64 * (4 * (4096 + 4096) + 2 * (4096 + 11008) + (11008 + 4096))
+    gen = torch.Generator(device="cuda").manual_seed(1)
+    theta = 0.02 * torch.randn(n, device="cuda", generator=gen)
+    g = 1e-4 * torch.randn(n, device="cuda", generator=gen)
+    tb = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    m_d = torch.zeros(n, device="cuda")
+    v_d = torch.zeros(n, device="cuda")
+    m_h = torch.zeros(n, dtype=torch.float32).pin_memory()
+    v_h = torch.zeros(n, dtype=torch.float32).pin_memory()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    coef, _ = api.qlora_clip_grad_norm(g, 0.3)
+    clip_ms = timed(lambda: api.qlora_clip_grad_norm(g, 0.3, coef=coef))
+    out = {"params": n, "clip_ms": clip_ms, "clip_GBps": 4 * n / (clip_ms * 1e-3) / 1e9, "adam": []}
+    log(f"optimiser: clip norm over {n} values {clip_ms:.3f} ms")
+    state = [0]
+
+    def step(frac):
+        split = (int(n * (1 - frac)) // 4) * 4
+        state[0] += 1
+        t = state[0]
+        if split > 0:
+            api.qlora_adam_step(theta[:split], g[:split], m_d[:split], v_d[:split], t, lr=2e-4, coef=coef,
+                                theta_bf16=tb[:split])
+        if split < n:
+            api.qlora_adam_step(theta[split:], g[split:], m_h[split:], v_h[split:], t, lr=2e-4, coef=coef,
+                                theta_bf16=tb[split:])
+
+    base = None
+    for frac in (0.0, 0.25, 0.5, 0.75, 1.0):
+        ms = timed(lambda: step(frac))
+        base = ms if base is None else base
+        host_bytes = 16 * (n - (int(n * (1 - frac)) // 4) * 4)
+        row = {"host_fraction": frac, "ms": ms, "hbm_GBps_equiv": 30 * n / (ms * 1e-3) / 1e9,
+               "host_link_GBps": host_bytes / (ms * 1e-3) / 1e9 if host_bytes else None, "vs_hbm_state": ms / base}
+        out["adam"].append(row)
+        log(f"optimiser: Adam with {int(100 * frac)} % of the state in host memory: {ms:.2f} ms "
+            f"({ms / base:.1f}x the HBM-resident step)")
+    del theta, g, tb, m_d, v_d, m_h, v_h
+    return out
+
+
 def bench_qtypes(api, workloads, reps=5):
     """The four 4-bit data types (with double quantisation) and NF4 without it
     on a 4096 x 11008 weight: relative RMS error of the dequantised weight
@@ -565,6 +627,7 @@ def main():
         result["int8"] = bench_int8(api, workloads)
         result["merge"] = bench_merge(api, workloads)
         result["mid_m"] = bench_mid_m(api, workloads)
+        result["optimiser"] = bench_optim(api)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(host)

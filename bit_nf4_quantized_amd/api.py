@@ -37,8 +37,16 @@ EXPORTS = (
     "qlora_quantize", "qlora_dequantize", "qlora_linear_workspace", "qlora_linear_fwd",
     "qlora_linear_bwd", "qlora_set_timing", "qlora_int8_quantize", "qlora_int8_dequantize",
     "qlora_merge_adapters", "qlora_linear_workspace_dropout", "qlora_linear_fwd_dropout",
-    "qlora_linear_bwd_dropout", "qlora_lora_dropout",
+    "qlora_linear_bwd_dropout", "qlora_lora_dropout", "qlora_clip_grad_norm", "qlora_adam_step",
 )
+QLORA_CLIP_WORKSPACE_BYTES = 8192
+
+
+class AdamParams(ctypes.Structure):
+    """Mirror of the C struct qlora_adam_params."""
+
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int64)]
 INT8_BLOCKS = (64, 128, 256, 512, 1024, 2048, 4096)
 QLORA_TIMING_FWD_GEMM = 0
 QLORA_TIMING_DX_GEMM = 1
@@ -109,6 +117,10 @@ def _load():
     lib.qlora_set_timing.argtypes = [ctypes.c_int, vp, vp, ctypes.c_int, P(ctypes.c_int)]
     lib.qlora_set_timing.restype = ctypes.c_int
     u64 = ctypes.c_uint64
+    lib.qlora_clip_grad_norm.argtypes = [vp, i64, ctypes.c_float, vp, vp, vp, sz, vp]
+    lib.qlora_clip_grad_norm.restype = ctypes.c_int
+    lib.qlora_adam_step.argtypes = [vp, vp, vp, vp, i64, ctypes.c_void_p, vp, vp, vp]
+    lib.qlora_adam_step.restype = ctypes.c_int
     lib.qlora_linear_workspace_dropout.argtypes = [i64, i64, i64, ctypes.c_int, P(sz)]
     lib.qlora_linear_workspace_dropout.restype = ctypes.c_int
     lib.qlora_linear_fwd_dropout.argtypes = [P(QNF4), vp, i64, vp, vp, ctypes.c_int, ctypes.c_float, ctypes.c_float,
@@ -205,6 +217,53 @@ def qlora_linear_workspace_dropout(M: int, K: int, N: int, r: int) -> int:
     out = ctypes.c_size_t()
     _check(_load().qlora_linear_workspace_dropout(M, K, N, r, ctypes.byref(out)), "qlora_linear_workspace_dropout")
     return out.value
+
+
+def _need_mem(t, dtype, shape, name):
+    """A device tensor, or a pinned host tensor (the kernels reach it over the host link)."""
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{name} must be a device tensor or pinned host memory")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def qlora_clip_grad_norm(g, max_norm: float, coef=None, norm=None, workspace=None, stream=None):
+    """coef = min(1, max_norm / (||g|| + 1e-6)) and the norm (float64), as 1-element device tensors."""
+    import torch
+
+    n = g.numel()
+    _need_mem(g, torch.float32, tuple(g.shape), "g")
+    dev = g.device if g.is_cuda else torch.device("cuda")
+    coef = coef if coef is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    norm = norm if norm is not None else torch.empty(1, dtype=torch.float64, device=dev)
+    ws = _workspace(QLORA_CLIP_WORKSPACE_BYTES, dev, workspace)
+    _check(_load().qlora_clip_grad_norm(_ptr(g), n, float(max_norm), _ptr(coef), _ptr(norm), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream)), "qlora_clip_grad_norm")
+    return coef, norm
+
+
+def qlora_adam_step(theta, g, m, v, step: int, lr: float, beta1: float = 0.9, beta2: float = 0.999,
+                    eps: float = 1e-8, weight_decay: float = 0.0, coef=None, theta_bf16=None, stream=None):
+    """One Adam step in place on flat fp32 theta, m, v (each a device tensor or
+    pinned host memory) for gradient g, clipped by ``coef`` (1-element tensor)."""
+    import torch
+
+    n = theta.numel()
+    for t, name in ((theta, "theta"), (g, "g"), (m, "m"), (v, "v")):
+        _need_mem(t, torch.float32, (n,), name)
+    if theta_bf16 is not None:
+        _need_mem(theta_bf16, torch.bfloat16, (n,), "theta_bf16")
+    hp = AdamParams(lr, beta1, beta2, eps, weight_decay, step)
+    _check(_load().qlora_adam_step(_ptr(theta), _ptr(g), _ptr(m), _ptr(v), n, ctypes.byref(hp), _ptr(coef),
+                                   _ptr(theta_bf16), _stream(stream)), "qlora_adam_step")
 
 
 def qlora_lora_dropout(X, p: float, seed: int, out=None, stream=None):

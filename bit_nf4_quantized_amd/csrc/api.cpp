@@ -333,6 +333,21 @@ int linear_bwd_impl(const qlora_nf4* W, const uint16_t* X, const uint16_t* dY, i
 
 bool valid_dropout(float p) { return isfinite(p) && p >= 0.0f && p < 1.0f; }
 
+// The device-side address of p: device memory as it is, pinned host memory
+// through its device mapping; nullptr for anything else (pageable host
+// memory, managed memory, or an address HIP does not know).
+void* device_view(const void* p) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (a.type == hipMemoryTypeDevice && !a.isManaged) return const_cast<void*>(p);
+  if (a.type == hipMemoryTypeHost && a.devicePointer && a.hostPointer && !a.isManaged)
+    return static_cast<char*>(a.devicePointer) + (static_cast<const char*>(p) - static_cast<const char*>(a.hostPointer));
+  return nullptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -364,6 +379,53 @@ int qlora_linear_bwd_dropout(const qlora_nf4* W, const uint16_t* X, const uint16
   if (!valid_dropout(p)) return QLORA_ERR_ARG;
   const qlora::DropoutParams d = qlora::dropout_params(p, seed);
   return linear_bwd_impl(W, X, dY, M, L1, L2, r, scale, T, dX, dL1, dL2, grad_dtype, ws, ws_bytes, stream, &d);
+}
+
+int qlora_clip_grad_norm(const float* g, int64_t n, float max_norm, float* coef, double* norm, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  if (n < 0) return QLORA_ERR_SHAPE;
+  if (!(max_norm > 0.0f) || isnan(max_norm)) return QLORA_ERR_ARG;
+  if ((n > 0 && !g) || (!coef && !norm)) return QLORA_ERR_ARG;
+  if (!ws || ws_bytes < QLORA_CLIP_WORKSPACE_BYTES) return QLORA_ERR_WORKSPACE;
+  if (!aligned16(g) || !aligned16(ws) || (reinterpret_cast<uintptr_t>(coef) & 3u) ||
+      (reinterpret_cast<uintptr_t>(norm) & 7u))
+    return QLORA_ERR_ALIGN;
+  const float* gd = n > 0 ? static_cast<const float*>(device_view(g)) : g;
+  float* cd = coef ? static_cast<float*>(device_view(coef)) : nullptr;
+  double* nd = norm ? static_cast<double*>(device_view(norm)) : nullptr;
+  double* wd = static_cast<double*>(device_view(ws));
+  if ((n > 0 && !gd) || (coef && !cd) || (norm && !nd) || !wd) return QLORA_ERR_ARG;
+  (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
+  const hipError_t e = qlora::launch_clip_norm(gd, n, (double)max_norm, cd, nd, wd, stream);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
+
+int qlora_adam_step(float* theta, const float* g, float* m, float* v, int64_t n, const qlora_adam_params* hp,
+                    const float* coef, uint16_t* theta_bf16, hipStream_t stream) {
+  if (!hp) return QLORA_ERR_ARG;
+  if (n < 0) return QLORA_ERR_SHAPE;
+  if (hp->step < 1 || !(hp->lr >= 0.0f) || !isfinite(hp->lr) || !(hp->eps >= 0.0f) || !isfinite(hp->eps) ||
+      !(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f) ||
+      !isfinite(hp->weight_decay))
+    return QLORA_ERR_ARG;
+  if (n == 0) return QLORA_OK;
+  if (!theta || !g || !m || !v) return QLORA_ERR_ARG;
+  if (!aligned16(theta) || !aligned16(g) || !aligned16(m) || !aligned16(v) || !aligned16(theta_bf16) ||
+      (reinterpret_cast<uintptr_t>(coef) & 3u))
+    return QLORA_ERR_ALIGN;
+  float* td = static_cast<float*>(device_view(theta));
+  const float* gd = static_cast<const float*>(device_view(g));
+  float* md = static_cast<float*>(device_view(m));
+  float* vd = static_cast<float*>(device_view(v));
+  const float* cd = coef ? static_cast<const float*>(device_view(coef)) : nullptr;
+  uint16_t* bd = theta_bf16 ? static_cast<uint16_t*>(device_view(theta_bf16)) : nullptr;
+  if (!td || !gd || !md || !vd || (coef && !cd) || (theta_bf16 && !bd)) return QLORA_ERR_ARG;
+  qlora::AdamHyper h;
+  h.lr = hp->lr; h.beta1 = hp->beta1; h.beta2 = hp->beta2; h.eps = hp->eps; h.wd = hp->weight_decay;
+  h.step = hp->step;
+  (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
+  const hipError_t e = qlora::launch_adam(td, gd, md, vd, n, h, cd, bd, stream);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 
 int qlora_lora_dropout(const uint16_t* X, int64_t numel, float p, uint64_t seed, uint16_t* Xd, hipStream_t stream) {

@@ -120,6 +120,16 @@ size_t midm_partial_bytes(int64_t M, int64_t K, int64_t N);
 hipError_t launch_midm(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M, const uint16_t* sT,
                        const uint16_t* l2t, int rp, float* part, uint16_t* Y, hipStream_t stream);
 
+// Optimiser step (optim.hip). part: 1024 doubles of workspace.
+struct AdamHyper {
+  float lr, beta1, beta2, eps, wd;
+  int64_t step;
+};
+hipError_t launch_clip_norm(const float* g, int64_t n, double max_norm, float* coef, double* norm, double* part,
+                            hipStream_t stream);
+hipError_t launch_adam(float* theta, const float* g, float* m, float* v, int64_t n, const AdamHyper& h,
+                       const float* coef, uint16_t* theta_bf16, hipStream_t stream);
+
 // Adapter merge into the bf16 dequantised base (merge.hip).
 hipError_t launch_merge(const NF4View& W, const NF4Table& tab, const uint16_t* L1, const uint16_t* L2, int r,
                         float s, uint16_t* out, hipStream_t stream);

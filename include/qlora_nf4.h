@@ -299,6 +299,50 @@ int qlora_linear_bwd_dropout(const qlora_nf4 *W, const uint16_t *X, const uint16
 int qlora_lora_dropout(const uint16_t *X, int64_t numel, float p, uint64_t seed, uint16_t *Xd, hipStream_t stream);
 
 /*
+ * The adapters' optimiser step (diycv.top, section 训练与推理流程: Adam with
+ * beta2 = 0.999, max grad norm 0.3, constant learning rate; section 方法总览
+ * item 4: the optimiser state is paged between GPU and CPU memory). The
+ * adapter parameters, gradients and state are flat fp32 vectors of n
+ * elements (the caller lays all adapters out in one buffer). Every pointer
+ * may be device memory or pinned host memory (hipHostMalloc / a pinned torch
+ * tensor): pinned host memory is read and written in place by the kernels
+ * over the host link, which keeps that state out of HBM ("paged out");
+ * anything else (pageable or managed memory) is rejected with QLORA_ERR_ARG.
+ * Both calls are deterministic and enqueue on `stream`.
+ *
+ * qlora_clip_grad_norm: norm = sqrt(sum g^2) (float64, fixed order) and
+ * coef = min(1, max_norm / (norm + 1e-6)) (float64, stored as fp32).
+ *   g       [n] fp32, 16-byte aligned.   max_norm > 0 (may be +inf: coef = 1).
+ *   coef    device/pinned fp32 [1] or NULL;  norm: fp64 [1] or NULL (not both NULL).
+ *   ws      QLORA_CLIP_WORKSPACE_BYTES of device memory, 16-byte aligned.
+ */
+enum { QLORA_CLIP_WORKSPACE_BYTES = 8192 };
+int qlora_clip_grad_norm(const float *g, int64_t n, float max_norm, float *coef, double *norm, void *ws,
+                         size_t ws_bytes, hipStream_t stream);
+
+/*
+ * qlora_adam_step: one Adam step (Kingma and Ba, ICLR 2015) on the clipped
+ * gradient, in fp32, element by element:
+ *   g' = coef g;  m = b1 m + (1-b1) g';  v = b2 v + (1-b2) g'^2;
+ *   theta -= lr ( (m / bc1) / (sqrt(v / bc2) + eps) + weight_decay theta ),
+ *   bc1 = 1 - b1^step, bc2 = 1 - b2^step (float64, rounded to fp32);
+ *   theta_bf16 (optional) receives bf16_RNE(theta), the adapters the layer reads.
+ *   theta, m, v updated in place; g read; all [n] and 16-byte aligned.
+ *   coef    fp32 [1] from qlora_clip_grad_norm, or NULL for 1.
+ *   hp      step >= 1; 0 <= beta1, beta2 < 1; lr, eps >= 0; finite values.
+ */
+typedef struct {
+  float lr;
+  float beta1;
+  float beta2;
+  float eps;
+  float weight_decay;
+  int64_t step;
+} qlora_adam_params;
+int qlora_adam_step(float *theta, const float *g, float *m, float *v, int64_t n, const qlora_adam_params *hp,
+                    const float *coef, uint16_t *theta_bf16, hipStream_t stream);
+
+/*
  * qlora_merge_adapters: the trained adapters merged into the bf16
  * dequantised base, for inference without the adapter branch (neura.market
  * "QLoRA", pitfalls list: merge into the 16-bit dequantised base, never back

@@ -38,7 +38,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     assert sorted(api.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -218,6 +218,39 @@ def test_dropout_validation(lib):
     assert lib.qlora_lora_dropout(X, -8, 0.1, 1, Y, None) == api.QLORA_ERR_SHAPE
     assert lib.qlora_lora_dropout(None, 0, 0.1, 1, None, None) == api.QLORA_OK         # empty
     assert lib.qlora_lora_dropout(p(0x21000008), 64, 0.1, 1, Y, None) == api.QLORA_ERR_ALIGN
+
+
+def test_optimiser_validation(lib):
+    p = lambda a: ctypes.c_void_p(a)
+    th, g, m, v, c = p(0x21000000), p(0x22000000), p(0x23000000), p(0x24000000), p(0x25000000)
+    ok = api.AdamParams(1e-4, 0.9, 0.999, 1e-8, 0.0, 1)
+    a = lib.qlora_adam_step
+    assert a(th, g, m, v, 100, None, None, None, None) == api.QLORA_ERR_ARG
+    for bad in (api.AdamParams(1e-4, 0.9, 0.999, 1e-8, 0.0, 0),          # step starts at 1
+                api.AdamParams(1e-4, 1.0, 0.999, 1e-8, 0.0, 1),          # beta1 < 1
+                api.AdamParams(1e-4, 0.9, -0.1, 1e-8, 0.0, 1),
+                api.AdamParams(float("nan"), 0.9, 0.999, 1e-8, 0.0, 1),
+                api.AdamParams(1e-4, 0.9, 0.999, -1.0, 0.0, 1),
+                api.AdamParams(1e-4, 0.9, 0.999, 1e-8, float("inf"), 1)):
+        assert a(th, g, m, v, 100, ctypes.byref(bad), None, None, None) == api.QLORA_ERR_ARG
+    assert a(th, g, m, v, -1, ctypes.byref(ok), None, None, None) == api.QLORA_ERR_SHAPE
+    assert a(None, None, None, None, 0, ctypes.byref(ok), None, None, None) == api.QLORA_OK
+    assert a(th, None, m, v, 100, ctypes.byref(ok), None, None, None) == api.QLORA_ERR_ARG
+    assert a(p(0x21000004), g, m, v, 100, ctypes.byref(ok), None, None, None) == api.QLORA_ERR_ALIGN
+    # pageable host memory is never handed to a kernel
+    arrs = [np.zeros(64, np.float32) for _ in range(4)]
+    ptrs = [p(x.ctypes.data) for x in arrs]
+    if all(x.value % 16 == 0 for x in ptrs):
+        assert a(*ptrs, 64, ctypes.byref(ok), None, None, None) == api.QLORA_ERR_ARG
+    cl = lib.qlora_clip_grad_norm
+    ws = p(0x26000000)
+    assert cl(g, 100, 0.0, c, None, ws, 8192, None) == api.QLORA_ERR_ARG        # max_norm > 0
+    assert cl(g, 100, float("nan"), c, None, ws, 8192, None) == api.QLORA_ERR_ARG
+    assert cl(g, -1, 0.3, c, None, ws, 8192, None) == api.QLORA_ERR_SHAPE
+    assert cl(g, 100, 0.3, None, None, ws, 8192, None) == api.QLORA_ERR_ARG      # nothing to write
+    assert cl(g, 100, 0.3, c, None, ws, 100, None) == api.QLORA_ERR_WORKSPACE
+    assert cl(g, 100, 0.3, c, None, None, 8192, None) == api.QLORA_ERR_WORKSPACE
+    assert cl(p(0x22000004), 100, 0.3, c, None, ws, 8192, None) == api.QLORA_ERR_ALIGN
 
 
 def test_merge_validation(lib):
