@@ -17,10 +17,12 @@ The same run also measures:
   * roofline of the dominant kernel, the bf16 MFMA GEMM (gemm_nt_kernel) that
     computes both Y = X Wd^T + (s X L1) L2 and dX = dY Wd + (s dY L2^T) L1^T,
     from HIP events that the library records around each of its launches on
-    the call's stream; its HBM traffic comes from rocprofv3 FETCH_SIZE /
-    WRITE_SIZE counters stored under profiles/ (scaled by the same counters
-    on a plain device copy, see --copy-probe) and is reported only while the
-    kernel source still has the hash recorded with them;
+    the call's stream, in a second pass of the same steps (the timed steps
+    themselves run without those brackets, which cost about 14 us each);
+    its HBM traffic comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counters
+    stored under profiles/ (scaled by the same counters on a plain device
+    copy, see --copy-probe) and is reported only while the kernel source
+    still has the hash recorded with them;
   * the small-M dequant-GEMV (M in {1, 4, 16}; 4096->11008 and 11008->4096)
     in GB/s against 8 TB/s, cycling >= 24 distinct weight copies (> 512 MB)
     so the 256 MB last-level cache cannot serve the weights;
@@ -559,22 +561,30 @@ def main():
     for _ in range(args.warmup):
         run_step(api, layers, ws)
     torch.cuda.synchronize()
-    n_l = len(layers)
-    t_fwd = api.KernelTimer(api.QLORA_TIMING_FWD_GEMM, capacity=n_l * args.steps)
-    t_dx = api.KernelTimer(api.QLORA_TIMING_DX_GEMM, capacity=n_l * args.steps)
+    # the timed steps, uninstrumented
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    with t_fwd, t_dx:
-        e0.record()
-        for _ in range(args.steps):
-            run_step(api, layers, ws)
-        e1.record()
+    e0.record()
+    for _ in range(args.steps):
+        run_step(api, layers, ws)
+    e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = e0.elapsed_time(e1) / args.steps
     value = flops_step / (ms_step * 1e-3) / 1e12
     log(f"step {ms_step:.3f} ms, {value:.1f} TFLOP/s (wall {wall / args.steps * 1e3:.3f} ms/step)")
+    # the same number of steps again with HIP events around every GEMM launch
+    # (the per-kernel durations of the roofline; the brackets cost some time,
+    # which is why the step itself is timed without them)
+    n_l = len(layers)
+    t_fwd = api.KernelTimer(api.QLORA_TIMING_FWD_GEMM, capacity=n_l * args.steps)
+    t_dx = api.KernelTimer(api.QLORA_TIMING_DX_GEMM, capacity=n_l * args.steps)
+    torch.cuda.synchronize()
+    with t_fwd, t_dx:
+        for _ in range(args.steps):
+            run_step(api, layers, ws)
+    torch.cuda.synchronize()
 
     dfwd, ddx = t_fwd.durations_ms(), t_dx.durations_ms()
     kf = kernel_summary(dfwd, fwd_flops * args.steps)

@@ -481,7 +481,7 @@ LinearWorkspace linear_workspace_layout(int64_t M, int64_t K, int64_t N, int r, 
   L.l1t_off = off; off += align_up((size_t)64 * K * 2, 256);
   L.l2p_off = off; off += align_up((size_t)64 * N * 2, 256);
   if (r <= 64) upd(skinny_partial_bytes(M, K, N));
-  if (M <= 16) upd(small_t_partial_bytes(M, K, r));
+  if (M <= kMidMaxM) upd(small_t_partial_bytes(M, K, r));
   upd(midm_partial_bytes(M, K, N));
   L.part_off = off; L.part_bytes = align_up(part, 256); off += L.part_bytes;
   // dense path: the dequantised weight (forward [N][K], backward [K][np])
@@ -575,13 +575,9 @@ hipError_t linear_forward(const NF4View& W, const NF4Table& tab, const uint16_t*
   }
 
   if (M <= kMidMaxM) {   // batched decode: one pass over the 4-bit weight
-    hipError_t e = lora_down(Xa, M, K, L1, r, s, sT, rp, T_out, part, l1t, stream);
+    hipError_t e = launch_small_lora_down(Xa, M, K, L1, r, s, sT, rp, T_out, part, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)cdiv(N, 32), (unsigned)cdiv(rp, 32)), dim3(256), 0,
-                       stream, L2, (int64_t)r, N, l2t, rp);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return timed(kTimeMidGemm, stream, [&] { return launch_midm(W, tab, X, M, sT, l2t, (int)rp, part, Y, stream); });
+    return timed(kTimeMidGemm, stream, [&] { return launch_midm(W, tab, X, M, sT, L2, r, (int)rp, part, Y, stream); });
   }
 
   const bool dense = fits_dense({M * K * 2, N * K * 2, M * rp * 2, N * rp * 2});

@@ -745,9 +745,9 @@ hipError_t launch_lut(const NF4View& Wt, const NF4Table& tab, const uint16_t* X,
 
 // ---- small-M LoRA down projection -------------------------------------------
 //
-// T = X L1 for M <= 16 rows, in two short kernels:
-//   * partial sums over k-slices of 512: one workgroup of 16 waves per slice
-//     and 64 columns; wave w multiplies its 32 rows of the slice with
+// T = X L1 for M <= 128 rows, in two short kernels:
+//   * partial sums over k-slices of 512: one workgroup of 16 waves per slice,
+//     64 columns and 16 rows of X (blockIdx.z); wave w multiplies its 32 rows of the slice with
 //     v_mfma_f32_16x16x32_bf16 (A = the rows of X, B = the columns of L1,
 //     zero rows beyond M), and the 16 waves' sums are added in a fixed order
 //     through LDS;
@@ -769,8 +769,9 @@ __global__ __launch_bounds__(64 * kTsWaves) void small_t_partial_kernel(const ui
   const int64_t kw = (int64_t)blockIdx.x * kTsK + wave * kTsRows + 8 * (lane >> 4);
   const int row = lane & 15;
   const int j0 = blockIdx.y * 64;
+  const int mb = blockIdx.z * 16;   // this workgroup's 16 rows of X
   u32x4_t xa = {0u, 0u, 0u, 0u};
-  if (row < M && kw < K) xa = *reinterpret_cast<const u32x4_t*>(X + (int64_t)row * K + kw);  // K % 64 == 0
+  if (mb + row < M && kw < K) xa = *reinterpret_cast<const u32x4_t*>(X + (int64_t)(mb + row) * K + kw);  // K % 64 == 0
   uint32_t h[4][8];  // all 32 loads first (one round trip)
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt) {
@@ -793,7 +794,7 @@ __global__ __launch_bounds__(64 * kTsWaves) void small_t_partial_kernel(const ui
     acc[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, xa), __builtin_bit_cast(bf16x8_t, b),
                                                        zero, 0, 0, 0);
   }
-  // acc[jt] register i of lane l: T[m = 4 (l/16) + i][j = j0 + 16 jt + l%16]
+  // acc[jt] register i of lane l: T[m = mb + 4 (l/16) + i][j = j0 + 16 jt + l%16]
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt)
 #pragma unroll
@@ -803,7 +804,7 @@ __global__ __launch_bounds__(64 * kTsWaves) void small_t_partial_kernel(const ui
   float v = 0.0f;
 #pragma unroll
   for (int w = 0; w < kTsWaves; ++w) v += red[w][m][lane];
-  if (m < M && j0 + lane < r) P[((int64_t)blockIdx.x * M + m) * r + j0 + lane] = v;
+  if (mb + m < M && j0 + lane < r) P[((int64_t)blockIdx.x * M + mb + m) * r + j0 + lane] = v;
 }
 
 __global__ __launch_bounds__(256) void small_t_reduce_kernel(const float* __restrict__ P, int Z, int M, int r, float s,
@@ -834,10 +835,10 @@ size_t small_t_partial_bytes(int64_t M, int64_t K, int r) {
 
 hipError_t launch_small_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* L1, int r, float s,
                                   uint16_t* sT, int64_t ldst, uint16_t* T_out, float* part, hipStream_t stream) {
-  if (M < 1 || M > 16) return hipErrorInvalidValue;
+  if (M < 1 || M > 128) return hipErrorInvalidValue;
   const int Z = (int)((K + kTsK - 1) / kTsK);
-  hipLaunchKernelGGL(small_t_partial_kernel, dim3((unsigned)Z, (unsigned)((r + 63) / 64)), dim3(64 * kTsWaves), 0,
-                     stream, X, (int)M, K, L1, r, part);
+  hipLaunchKernelGGL(small_t_partial_kernel, dim3((unsigned)Z, (unsigned)((r + 63) / 64), (unsigned)((M + 15) / 16)),
+                     dim3(64 * kTsWaves), 0, stream, X, (int)M, K, L1, r, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(small_t_reduce_kernel, dim3((unsigned)((M * r + 255) / 256)), dim3(256), 0, stream, part, Z,

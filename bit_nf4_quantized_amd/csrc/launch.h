@@ -113,12 +113,12 @@ inline int device_cu_count() {
 }
 
 // Forward for 16 < M <= kMidMaxM (midm.hip): fused dequant-GEMM over K-slices
-// plus a fixed-order reduction; sT = bf16(s X L1) [M][rp] and l2t = L2^T
-// [N][rp], both zero past r; part holds midm_partial_bytes.
+// plus a fixed-order reduction; sT = bf16(s X L1) [M][rp] (columns < r
+// used), L2 [r][N]; part holds midm_partial_bytes.
 constexpr int kMidMaxM = 128;
 size_t midm_partial_bytes(int64_t M, int64_t K, int64_t N);
 hipError_t launch_midm(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M, const uint16_t* sT,
-                       const uint16_t* l2t, int rp, float* part, uint16_t* Y, hipStream_t stream);
+                       const uint16_t* L2, int r, int rp, float* part, uint16_t* Y, hipStream_t stream);
 
 // Optimiser step (optim.hip). part: 1024 doubles of workspace.
 struct AdamHyper {

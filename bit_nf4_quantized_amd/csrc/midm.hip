@@ -23,7 +23,11 @@
 //   - The X tile of the step (MT x 64 bf16) is staged in LDS, double
 //     buffered, and shared by the 4 waves.
 //   - The LoRA term is one more step per 64 adapter ranks in slice 0, with
-//     the transposed L2 [n][j] as the A operand and bf16(s X L1) [m][j] as X.
+//     L2's column n (16 ranks per lane, read strided) as the A operand and
+//     bf16(s X L1) [m][j] as X.
+//   - The codes of a step are loaded two steps ahead and its X tile three
+//     steps ahead (staged into LDS one step ahead), each in three register
+//     sets used in rotation.
 //   - Every global load is unconditional, from a clamped address, zeroed by a
 //     select afterwards (a load under a branch makes the compiler wait for it
 //     where the branches join).
@@ -42,18 +46,21 @@ constexpr int kMidTN = 64;   // weight rows per workgroup
 // over the banks
 __device__ __forceinline__ int mid_swz(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
 
-template <int MT>
-struct MidStep {
+struct MidCodes {
   u32x2_t codes;      // 16 codes of this lane's row, k = 16 quad .. 16 quad + 16
-  uint32_t c8;        // E4M3 byte of the row's block (DQ)
+  uint8_t c8;         // E4M3 byte of the row's block (DQ); widened where it is used, not at the load
   float fv;           // group scale (DQ) or block absmax (no DQ)
-  u32x4_t x[MT / 32]; // this thread's 16-byte chunks of the X tile
+};
+
+template <int MT>
+struct MidX {
+  u32x4_t x[MT / 32]; // this thread's 16-byte chunks of the step's X tile
 };
 
 template <int MT>
 __global__ __launch_bounds__(kMidThreads) void midm_kernel(NF4View W, NF4Table tab, const uint16_t* __restrict__ X,
                                                            int M, const uint16_t* __restrict__ sT,
-                                                           const uint16_t* __restrict__ l2t, int rp,
+                                                           const uint16_t* __restrict__ L2, int r, int rp,
                                                            int64_t kslice, float* __restrict__ part,
                                                            uint16_t* __restrict__ Y) {
   constexpr int kXPer = MT / 32;           // 16-byte X chunks per thread per step (MT * 8 / 256)
@@ -85,23 +92,27 @@ __global__ __launch_bounds__(kMidThreads) void midm_kernel(NF4View W, NF4Table t
   const float mraw = *(dq ? W.mean : W.absmax32);
   const float mu = dq ? mraw : 0.0f;
 
-  auto load_step = [&](int st, MidStep<MT>& d) {
+  auto load_codes = [&](int st, MidCodes& d) {
     const int64_t k0 = kb + (int64_t)st * 64;
     const int64_t e = nrow_c * K + k0 + quad * 16;     // 16 codes, inside one 64-block
     d.codes = *reinterpret_cast<const u32x2_t*>(W.codes + (e >> 1));
     const int64_t blk = e / kBlock;
     d.c8 = bp[dq ? blk : 0];
     d.fv = fp[dq ? blk / kDqBlock : blk];
+  };
+  // rows m >= M of the X tile read row 0 (finite values) and only feed
+  // output columns m >= M, which are never stored: no select is needed (a
+  // select after the load would make the compiler wait for it where it sinks)
+  auto load_x = [&](int st, MidX<MT>& d) {
+    const int64_t k0 = kb + (int64_t)st * 64;
 #pragma unroll
     for (int u = 0; u < kXPer; ++u) {
       const int idx = tid + u * kMidThreads;
       const int m = idx >> 3, ch = idx & 7;
-      const bool ok = m < M;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(X + (ok ? (int64_t)m * K + k0 + ch * 8 : 0));
-      d.x[u] = ok ? v : zero4;
+      d.x[u] = *reinterpret_cast<const u32x4_t*>(X + (m < M ? (int64_t)m * K : 0) + k0 + ch * 8);
     }
   };
-  auto store_x = [&](const MidStep<MT>& d, int buf) {
+  auto store_x = [&](const MidX<MT>& d, int buf) {
 #pragma unroll
     for (int u = 0; u < kXPer; ++u) {
       const int idx = tid + u * kMidThreads;
@@ -128,48 +139,83 @@ __global__ __launch_bounds__(kMidThreads) void midm_kernel(NF4View W, NF4Table t
   };
 
   __syncthreads();  // s_q
-  if (nmain > 0) {
-    MidStep<MT> cur, nxt;
-    load_step(0, cur);
-    store_x(cur, 0);
-    __syncthreads();
-    for (int st = 0; st < nmain; ++st) {
-      const int buf = st & 1;
-      load_step(st + 1 < nmain ? st + 1 : st, nxt);   // the last step loads itself again
-      // dequantise this lane's 16 weights: bf16(RN32(q[c] * a'))
-      const float ap = dq ? block_scale(cur.c8, cur.fv, mu) : cur.fv;
-      uint32_t w[8];
+  // one 64-k step st: start the loads of the codes of step st+2 and of the X
+  // tile of step st+3, dequantise this lane's 16 weights (bf16(RN32(q[c]
+  // a'))) and multiply them with the X tile in LDS, then stage the X tile of
+  // step st+1 (loaded two steps ago) into the other LDS buffer. Loads past
+  // the last step repeat the last step.
+  auto clampst = [&](int st) { return st < nmain ? st : nmain - 1; };
+  auto step = [&](int st, const MidCodes& cur, MidCodes& c2, MidX<MT>& x3, const MidX<MT>& x1) {
+    const int buf = st & 1;
+    // nothing moves across step boundaries: the scheduler would otherwise
+    // hoist arithmetic on a later step's loads, and wait for them early
+    __builtin_amdgcn_sched_barrier(0);
+    load_codes(clampst(st + 2), c2);
+    load_x(clampst(st + 3), x3);
+    const float ap = dq ? block_scale(cur.c8, cur.fv, mu) : cur.fv;
+    uint32_t w[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t word = i < 4 ? cur.codes.x : cur.codes.y;
-        const uint32_t byte = (word >> (8 * (i & 3))) & 0xFFu;
-        w[i] = pack_bf16x2(s_q[byte & 15u] * ap, s_q[byte >> 4] * ap);
-      }
-      const u32x4_t a0 = row_ok ? u32x4_t{w[0], w[1], w[2], w[3]} : zero4;
-      const u32x4_t a1 = row_ok ? u32x4_t{w[4], w[5], w[6], w[7]} : zero4;
-      mma(a0, a1, buf);
-      store_x(nxt, buf ^ 1);
-      __syncthreads();
-      cur = nxt;
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t word = i < 4 ? cur.codes.x : cur.codes.y;
+      const uint32_t byte = (word >> (8 * (i & 3))) & 0xFFu;
+      w[i] = pack_bf16x2(s_q[byte & 15u] * ap, s_q[byte >> 4] * ap);
     }
+    // rows n >= N dequantise row 0 and only feed outputs n >= N, never stored
+    mma(u32x4_t{w[0], w[1], w[2], w[3]}, u32x4_t{w[4], w[5], w[6], w[7]}, buf);
+    store_x(x1, buf ^ 1);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if (nmain > 0) {
+    // three register sets each for the codes and the X tiles, in rotation
+    // (no copies between steps: a copy would wait for the loads in flight)
+    MidCodes c0, c1, c2;
+    MidX<MT> x0, x1, x2;
+    load_codes(0, c0);
+    load_codes(clampst(1), c1);
+    load_x(0, x0);
+    load_x(clampst(1), x1);
+    load_x(clampst(2), x2);
+    store_x(x0, 0);
+    __syncthreads();
+    // whole rounds of three steps, then the last one or two (a loop with
+    // exits between its steps makes the compiler wait for every load in
+    // flight at the loop head)
+    int st = 0;
+    for (; st + 3 <= nmain; st += 3) {
+      step(st, c0, c2, x0, x1);
+      step(st + 1, c1, c0, x1, x2);
+      step(st + 2, c2, c1, x2, x0);
+    }
+    if (st < nmain) step(st, c0, c2, x0, x1);
+    if (st + 1 < nmain) step(st + 1, c1, c0, x1, x2);
   }
 
-  // the LoRA slab in slice 0: A = l2t[n][j .. j + 16) (transposed L2, rp
-  // columns, zero past r), X = bf16(s X L1)[m][j .. ] (rp columns)
+  // the LoRA slab in slice 0: A = L2[j .. j + 16)[n] (16 ranks of this
+  // lane's column of L2, zero past r), X = bf16(s X L1)[m][j .. ] (row
+  // stride rp, zero past r)
   if (z == 0) {
     for (int j0 = 0; j0 < rp; j0 += 64) {
-      const u32x4_t* ap = reinterpret_cast<const u32x4_t*>(l2t + nrow_c * rp + j0 + quad * 16);
-      const u32x4_t a0v = ap[0], a1v = ap[1];
+      uint32_t lw[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int ja = j0 + quad * 16 + 2 * i;   // r even: ranks ja and ja+1 are both inside or both outside
+        const bool ok = ja < r;
+        const uint32_t lo = L2[(int64_t)(ok ? ja : 0) * N + nrow_c];
+        const uint32_t hi = L2[(int64_t)(ok ? ja + 1 : 0) * N + nrow_c];
+        lw[i] = ok ? (lo | (hi << 16)) : 0u;
+      }
+      const u32x4_t a0v = {lw[0], lw[1], lw[2], lw[3]}, a1v = {lw[4], lw[5], lw[6], lw[7]};
 #pragma unroll
       for (int u = 0; u < kXPer; ++u) {
         const int idx = tid + u * kMidThreads;
         const int m = idx >> 3, ch = idx & 7;
-        const bool ok = m < M;
+        const bool ok = m < M && j0 + ch * 8 < r;   // r % 8 == 0: a chunk is wholly inside or outside
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(sT + (ok ? (int64_t)m * rp + j0 + ch * 8 : 0));
         *reinterpret_cast<u32x4_t*>(&sX[0][mid_swz(m, ch)]) = ok ? v : zero4;
       }
       __syncthreads();
-      mma(row_ok ? a0v : zero4, row_ok ? a1v : zero4, 0);
+      mma(a0v, a1v, 0);
       __syncthreads();
     }
   }
@@ -230,7 +276,7 @@ size_t midm_partial_bytes(int64_t M, int64_t K, int64_t N) {
 }
 
 hipError_t launch_midm(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M, const uint16_t* sT,
-                       const uint16_t* l2t, int rp, float* part, uint16_t* Y, hipStream_t stream) {
+                       const uint16_t* L2, int r, int rp, float* part, uint16_t* Y, hipStream_t stream) {
   if (M <= 16 || M > kMidMaxM || (W.cols % 64) != 0 || (W.rows % 8) != 0 || (rp % 64) != 0)
     return hipErrorInvalidValue;
   const MidSplit p = mid_split(W.cols, W.rows);
@@ -238,11 +284,11 @@ hipError_t launch_midm(const NF4View& W, const NF4Table& tab, const uint16_t* X,
   const dim3 grid((unsigned)p.tiles, (unsigned)p.S), block(kMidThreads);
   const int m = (int)M;
   if (M <= 32)
-    hipLaunchKernelGGL(midm_kernel<32>, grid, block, 0, stream, W, tab, X, m, sT, l2t, rp, p.kslice, pp, Y);
+    hipLaunchKernelGGL(midm_kernel<32>, grid, block, 0, stream, W, tab, X, m, sT, L2, r, rp, p.kslice, pp, Y);
   else if (M <= 64)
-    hipLaunchKernelGGL(midm_kernel<64>, grid, block, 0, stream, W, tab, X, m, sT, l2t, rp, p.kslice, pp, Y);
+    hipLaunchKernelGGL(midm_kernel<64>, grid, block, 0, stream, W, tab, X, m, sT, L2, r, rp, p.kslice, pp, Y);
   else
-    hipLaunchKernelGGL(midm_kernel<128>, grid, block, 0, stream, W, tab, X, m, sT, l2t, rp, p.kslice, pp, Y);
+    hipLaunchKernelGGL(midm_kernel<128>, grid, block, 0, stream, W, tab, X, m, sT, L2, r, rp, p.kslice, pp, Y);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
   const int64_t MN = M * W.rows;
