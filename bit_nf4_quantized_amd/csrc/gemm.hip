@@ -574,7 +574,7 @@ hipError_t linear_forward(const NF4View& W, const NF4Table& tab, const uint16_t*
     return timed(kTimeGemv, stream, [&] { return launch_gemv(W, tab, X, M, sT, L2, r, Y, stream); });
   }
 
-  if (M <= kMidMaxM) {   // batched decode: one pass over the 4-bit weight
+  if (M <= kMidMaxM && midm_fits(M, K, N)) {   // batched decode: one pass over the 4-bit weight
     hipError_t e = launch_small_lora_down(Xa, M, K, L1, r, s, sT, rp, T_out, part, stream);
     if (e != hipSuccess) return e;
     return timed(kTimeMidGemm, stream, [&] { return launch_midm(W, tab, X, M, sT, L2, r, (int)rp, part, Y, stream); });

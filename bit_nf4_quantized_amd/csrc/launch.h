@@ -117,6 +117,7 @@ inline int device_cu_count() {
 // used), L2 [r][N]; part holds midm_partial_bytes.
 constexpr int kMidMaxM = 128;
 size_t midm_partial_bytes(int64_t M, int64_t K, int64_t N);
+bool midm_fits(int64_t M, int64_t K, int64_t N);   // sizes the kernel's 32-bit offsets cover
 hipError_t launch_midm(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M, const uint16_t* sT,
                        const uint16_t* L2, int r, int rp, float* part, uint16_t* Y, hipStream_t stream);
 

@@ -92,25 +92,31 @@ __global__ __launch_bounds__(kMidThreads) void midm_kernel(NF4View W, NF4Table t
   const float mraw = *(dq ? W.mean : W.absmax32);
   const float mu = dq ? mraw : 0.0f;
 
+  // Per-lane 32-bit offsets from uniform bases (the launcher checks that they
+  // fit), advanced by a constant per step: a 64-bit address per load costs
+  // several VALU instructions, per step and lane.
+  const uint32_t e0 = (uint32_t)(nrow_c * K + kb) + (uint32_t)(quad * 16);   // first code of step 0
+  const uint32_t blk0 = (uint32_t)((nrow_c * K + kb) / kBlock);            // its 64-block
   auto load_codes = [&](int st, MidCodes& d) {
-    const int64_t k0 = kb + (int64_t)st * 64;
-    const int64_t e = nrow_c * K + k0 + quad * 16;     // 16 codes, inside one 64-block
+    const uint32_t e = e0 + (uint32_t)st * 64u;      // 16 codes, inside one 64-block
     d.codes = *reinterpret_cast<const u32x2_t*>(W.codes + (e >> 1));
-    const int64_t blk = e / kBlock;
-    d.c8 = bp[dq ? blk : 0];
-    d.fv = fp[dq ? blk / kDqBlock : blk];
+    const uint32_t blk = blk0 + (uint32_t)st;
+    d.c8 = bp[dq ? blk : 0u];
+    d.fv = fp[dq ? blk / (uint32_t)kDqBlock : blk];
   };
   // rows m >= M of the X tile read row 0 (finite values) and only feed
   // output columns m >= M, which are never stored: no select is needed (a
   // select after the load would make the compiler wait for it where it sinks)
-  auto load_x = [&](int st, MidX<MT>& d) {
-    const int64_t k0 = kb + (int64_t)st * 64;
+  uint32_t xo[kXPer];
 #pragma unroll
-    for (int u = 0; u < kXPer; ++u) {
-      const int idx = tid + u * kMidThreads;
-      const int m = idx >> 3, ch = idx & 7;
-      d.x[u] = *reinterpret_cast<const u32x4_t*>(X + (m < M ? (int64_t)m * K : 0) + k0 + ch * 8);
-    }
+  for (int u = 0; u < kXPer; ++u) {
+    const int idx = tid + u * kMidThreads;
+    const int m = idx >> 3, ch = idx & 7;
+    xo[u] = (uint32_t)((m < M ? (int64_t)m * K : 0) + kb) + (uint32_t)(ch * 8);
+  }
+  auto load_x = [&](int st, MidX<MT>& d) {
+#pragma unroll
+    for (int u = 0; u < kXPer; ++u) d.x[u] = *reinterpret_cast<const u32x4_t*>(X + xo[u] + (uint32_t)st * 64u);
   };
   auto store_x = [&](const MidX<MT>& d, int buf) {
 #pragma unroll
@@ -275,9 +281,15 @@ size_t midm_partial_bytes(int64_t M, int64_t K, int64_t N) {
   return p.S > 1 ? (size_t)p.S * M * N * 4 : 0;
 }
 
+bool midm_fits(int64_t M, int64_t K, int64_t N) {
+  // the kernel's per-lane element offsets into the codes and X are 32-bit
+  return N * K < ((int64_t)1 << 32) && M * K < ((int64_t)1 << 32);
+}
+
 hipError_t launch_midm(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M, const uint16_t* sT,
                        const uint16_t* L2, int r, int rp, float* part, uint16_t* Y, hipStream_t stream) {
-  if (M <= 16 || M > kMidMaxM || (W.cols % 64) != 0 || (W.rows % 8) != 0 || (rp % 64) != 0)
+  if (M <= 16 || M > kMidMaxM || (W.cols % 64) != 0 || (W.rows % 8) != 0 || (rp % 64) != 0 ||
+      !midm_fits(M, W.cols, W.rows))
     return hipErrorInvalidValue;
   const MidSplit p = mid_split(W.cols, W.rows);
   float* pp = p.S > 1 ? part : nullptr;
