@@ -80,6 +80,9 @@ def test_tiny_512(api):
     (384, 1024, 768, 64, 0.25, "normal"),        # several tiles each way
     (17, 256, 264, 8, 1.0, "student-t4"),        # smallest M above the GEMV (fused one-pass forward)
     (130, 64 * 7, 8 * 41, 256, 0.125, "normal"),  # largest rank, ragged everything
+    # more 256x256 tiles than CUs (17 x 17 = 289): 255 full tiles, then the last
+    # two tile-columns as 128-row half tiles, with ragged M and N inside them
+    (4100, 512, 4160, 16, 0.5, "normal"),
 ])
 def test_shapes(api, M, K, N, r, s, kind):
     say(f"linear M={M} K={K} N={N} r={r} s={s} {kind}")
