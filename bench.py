@@ -237,7 +237,8 @@ def bench_gemv(api, workloads, reps=4):
 
 
 def bench_quantize(api, workloads, reps=5):
-    """NF4 + DQ quantisation of a LLaMA-65B gate-shaped weight (22016 x 8192)."""
+    """NF4 + DQ quantisation of a LLaMA-65B gate-shaped weight (22016 x 8192), from
+    fp32 and from bf16, and the standalone doubleDequant of it back to bf16."""
     import torch
 
     shp = workloads.LLAMA65B[4]
@@ -263,6 +264,26 @@ def bench_quantize(api, workloads, reps=5):
                    "frac_of_hbm_peak": nbytes / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                    "pass1_kernel_ms": k_ms}
         log(f"quantize {dt} {shp.N}x{shp.K}: {call_ms:.3f} ms, {res[dt]['GBps']:.0f} GB/s")
+    # the standalone doubleDequant of the same weight to bf16
+    y = torch.empty(shp.N, shp.K, dtype=torch.bfloat16, device="cuda")
+    api.qlora_dequantize(q, out=y)
+    timer = api.KernelTimer(api.QLORA_TIMING_DEQUANT, capacity=reps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with timer:
+        e0.record()
+        for _ in range(reps):
+            api.qlora_dequantize(q, out=y)
+        e1.record()
+    torch.cuda.synchronize()
+    numel = shp.N * shp.K
+    nbytes = nf4_bytes(shp.K, shp.N) + 2 * numel
+    call_ms = e0.elapsed_time(e1) / reps
+    k_ms = sum(timer.durations_ms()) / reps
+    res["dequantize"] = {"shape": [shp.N, shp.K], "call_ms": call_ms, "GBps": nbytes / (call_ms * 1e-3) / 1e9,
+                         "frac_of_hbm_peak": nbytes / (call_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                         "kernel_ms_bracketed": k_ms}
+    log(f"dequantize {shp.N}x{shp.K} to bf16: {call_ms:.3f} ms, {res['dequantize']['GBps']:.0f} GB/s")
     return res
 
 

@@ -357,32 +357,42 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(DenseArgs p) {
   }
 }
 
-// Wd[n][k] for the forward product: 16 weights per thread, the standalone
-// dequant arithmetic (bf16(RN32(q[code] * a'))), rows of the workspace
-// padded to ldo columns (ldo >= K).
+// Wd[n][k] for the forward product, the standalone dequant arithmetic
+// (bf16(RN32(q[code] * a'))). A thread takes 4 units of 8 weights (one code
+// dword, one 16-byte store) 256 units apart, so that every load and store
+// instruction of a wave covers one contiguous range; the 4 code loads and
+// block constants are issued before any store (measured 17.0 us against
+// 19.5 us per launch for one unit of 16 weights per thread).
+constexpr int kRowsUnits = 4;
 __global__ __launch_bounds__(256) void dequant_rows_kernel(NF4View W, NF4Table tab, uint16_t* __restrict__ out) {
   __shared__ float s_q[16];
   if (threadIdx.x < 16) s_q[threadIdx.x] = tab.q[threadIdx.x];
   __syncthreads();
   const float mu = tensor_mean(W);
-  const int64_t numel = W.rows * W.cols;
-  const int64_t nunits = numel / 16;  // cols % 64 == 0
-  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < nunits;
-       u += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t e0 = u * 16;
-    const int64_t blk = e0 / kBlock;
-    const float ap = block_const(W, blk, mu);
-    const u32x2_t c = *reinterpret_cast<const u32x2_t*>(W.codes + (e0 >> 1));
-    uint32_t o[8];
+  const int64_t nunits = W.rows * W.cols / 8;  // cols % 64 == 0
+  const uint32_t* codes = reinterpret_cast<const uint32_t*>(W.codes);
+  const int64_t stride = (int64_t)gridDim.x * 256 * kRowsUnits;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * kRowsUnits + threadIdx.x; base < nunits; base += stride) {
+    uint32_t c[kRowsUnits];
+    float ap[kRowsUnits];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t word = (i < 4) ? c.x : c.y;
-      const uint32_t byte = (word >> (8 * (i & 3))) & 0xFFu;
-      o[i] = pack_bf16x2(s_q[byte & 15u] * ap, s_q[byte >> 4] * ap);
+    for (int u = 0; u < kRowsUnits; ++u) {
+      const int64_t un = base + (int64_t)u * 256;
+      const int64_t uc = un < nunits ? un : nunits - 1;  // clamped: loads stay unconditional
+      c[u] = codes[uc];
+      ap[u] = block_const(W, uc >> 3, mu);  // 8 units per 64-block
     }
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + e0);
-    dst[0] = u32x4_t{o[0], o[1], o[2], o[3]};
-    dst[1] = u32x4_t{o[4], o[5], o[6], o[7]};
+#pragma unroll
+    for (int u = 0; u < kRowsUnits; ++u) {
+      const int64_t un = base + (int64_t)u * 256;
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t byte = (c[u] >> (8 * i)) & 0xFFu;
+        o[i] = pack_bf16x2(s_q[byte & 15u] * ap[u], s_q[byte >> 4] * ap[u]);
+      }
+      if (un < nunits) *reinterpret_cast<u32x4_t*>(out + un * 8) = u32x4_t{o[0], o[1], o[2], o[3]};
+    }
   }
 }
 
@@ -445,9 +455,11 @@ __global__ __launch_bounds__(256) void dequant_cols_kernel(NF4View W, NF4Table t
 }  // namespace
 
 hipError_t launch_dequant_rows(const NF4View& W, const NF4Table& tab, uint16_t* out, hipStream_t stream) {
-  const int64_t nunits = W.rows * W.cols / 16;
-  int64_t blocks = (nunits + 255) / 256;
-  if (blocks > 256 * 32) blocks = 256 * 32;
+  const int64_t nunits = W.rows * W.cols / 8;
+  const int64_t per_block = 256 * kRowsUnits;
+  int64_t blocks = (nunits + per_block - 1) / per_block;
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  if (blocks > cap) blocks = cap;
   hipLaunchKernelGGL(dequant_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W, tab, out);
   return hipGetLastError();
 }

@@ -233,7 +233,12 @@ __global__ __launch_bounds__(kDqBlock) void dq_encode_kernel(const float* __rest
   if (t == 0) scale2[blockIdx.x] = sigma;
 }
 
-// 16 weights per thread: 8 code bytes in, 32 bytes of bf16 out.
+// Units of 8 weights (one code dword in, one 16-byte bf16 store out). A
+// thread takes 4 units 256 apart, so that each load and store instruction of
+// a wave covers one contiguous range, and issues their 4 code loads and block
+// constants before any store. The last numel % 8 weights are done by one
+// thread, one at a time.
+constexpr int kDqUnits = 4;
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ absmax8,
                                                       const float* __restrict__ scale2,
@@ -244,32 +249,39 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   if (threadIdx.x < 16) s_q[threadIdx.x] = tab.q[threadIdx.x];
   __syncthreads();
   const float mu = absmax32 ? 0.0f : mean[0];
-  const int64_t nunits = (numel + 15) / 16;
-  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < nunits;
-       u += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t e0 = u * 16;
-    const int64_t blk = e0 / kBlock;
-    const float ap = absmax32 ? absmax32[blk] : block_scale(absmax8[blk], scale2[blk / kDqBlock], mu);
-    if (e0 + 16 <= numel) {
-      const u32x2_t c = *reinterpret_cast<const u32x2_t*>(codes + (e0 >> 1));
-      uint32_t o[8];
+  auto block_a = [&](int64_t blk) {
+    return absmax32 ? absmax32[blk] : block_scale(absmax8[blk], scale2[blk / kDqBlock], mu);
+  };
+  const int64_t nunits = numel / 8;
+  const uint32_t* cw = reinterpret_cast<const uint32_t*>(codes);
+  const int64_t stride = (int64_t)gridDim.x * 256 * kDqUnits;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * kDqUnits + threadIdx.x; base < nunits; base += stride) {
+    uint32_t c[kDqUnits];
+    float ap[kDqUnits];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t word = (i < 4) ? c.x : c.y;
-        const uint32_t byte = (word >> (8 * (i & 3))) & 0xFFu;
-        const float lo = s_q[byte & 15u] * ap;
-        const float hi = s_q[byte >> 4] * ap;
-        o[i] = pack_bf16x2(lo, hi);
+    for (int u = 0; u < kDqUnits; ++u) {
+      const int64_t un = base + (int64_t)u * 256;
+      const int64_t uc = un < nunits ? un : nunits - 1;  // clamped: loads stay unconditional
+      c[u] = cw[uc];
+      ap[u] = block_a(uc >> 3);  // 8 units per 64-block
+    }
+#pragma unroll
+    for (int u = 0; u < kDqUnits; ++u) {
+      const int64_t un = base + (int64_t)u * 256;
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t byte = (c[u] >> (8 * i)) & 0xFFu;
+        o[i] = pack_bf16x2(s_q[byte & 15u] * ap[u], s_q[byte >> 4] * ap[u]);
       }
-      u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + e0);
-      dst[0] = u32x4_t{o[0], o[1], o[2], o[3]};
-      dst[1] = u32x4_t{o[4], o[5], o[6], o[7]};
-    } else {
-      for (int64_t e = e0; e < numel; ++e) {
-        const uint32_t byte = codes[e >> 1];
-        const uint32_t c = (e & 1) ? (byte >> 4) : (byte & 15u);
-        out[e] = f32_to_bf16(s_q[c] * ap);
-      }
+      if (un < nunits) *reinterpret_cast<u32x4_t*>(out + un * 8) = u32x4_t{o[0], o[1], o[2], o[3]};
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    for (int64_t e = nunits * 8; e < numel; ++e) {
+      const uint32_t byte = codes[e >> 1];
+      const uint32_t q = (e & 1) ? (byte >> 4) : (byte & 15u);
+      out[e] = f32_to_bf16(s_q[q] * block_a(e / kBlock));
     }
   }
 }
@@ -306,9 +318,10 @@ hipError_t launch_quantize(const void* w, bool bf16_in, int64_t numel, const NF4
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* absmax8, const float* scale2,
                              const float* mean, const float* absmax32, const NF4Table& tab, int64_t numel,
                              uint16_t* out, hipStream_t stream) {
-  const int64_t nunits = (numel + 15) / 16;
-  int64_t blocks = (nunits + 255) / 256;
-  if (blocks > 256 * 64) blocks = 256 * 64;
+  const int64_t nunits = numel / 8;
+  int64_t blocks = (nunits + 256 * kDqUnits - 1) / (256 * kDqUnits);
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   return timed(kTimeDequant, stream, [&] {
     hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, codes, absmax8, scale2,
