@@ -13,43 +13,19 @@
 // backward: both regenerate the mask from (seed, p).
 //
 // Kernels (both HBM-bound):
-//   dropout_input_kernel   Xd from X, 8 elements (two Philox blocks) per thread
+//   dropout_input_kernel   Xd from X, 8 elements (two Philox blocks) per thread;
+//                          the large-M layer does not use it: its adapter
+//                          kernels drop X in registers (skinny_gemm.hip)
 //   masked_lora_kernel     D[m][k] = keep c sum_j sU[m][j] L1[k][j] on MFMA (rank r),
 //                          written as fp32 (added by the dX GEMM's epilogue), or
 //                          combined with an fp32 main product into bf16 dX
 #include "common.h"
 #include "launch.h"
+#include "philox.h"
 
 namespace qlora {
 
 namespace {
-
-constexpr uint32_t kPhiloxM0 = 0xD2511F53u, kPhiloxM1 = 0xCD9E8D57u;
-constexpr uint32_t kPhiloxW0 = 0x9E3779B9u, kPhiloxW1 = 0xBB67AE85u;
-
-// Philox4x32-10 of counter (c0, c1, 0, 0) under key (k0, k1).
-__device__ __forceinline__ u32x4_t philox(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1) {
-  uint32_t x0 = c0, x1 = c1, x2 = 0u, x3 = 0u;
-#pragma unroll
-  for (int rnd = 0; rnd < 10; ++rnd) {
-    const uint64_t p0 = (uint64_t)kPhiloxM0 * x0;
-    const uint64_t p1 = (uint64_t)kPhiloxM1 * x2;
-    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
-    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
-    x0 = hi1 ^ x1 ^ k0;
-    x1 = lo1;
-    x2 = hi0 ^ x3 ^ k1;
-    x3 = lo0;
-    k0 += kPhiloxW0;
-    k1 += kPhiloxW1;
-  }
-  return u32x4_t{x0, x1, x2, x3};
-}
-
-// The four words of Philox block b (elements 4b .. 4b+3).
-__device__ __forceinline__ u32x4_t philox_block(int64_t b, uint64_t seed) {
-  return philox((uint32_t)b, (uint32_t)((uint64_t)b >> 32), (uint32_t)seed, (uint32_t)(seed >> 32));
-}
 
 __global__ __launch_bounds__(256) void dropout_input_kernel(const uint16_t* __restrict__ X, int64_t numel,
                                                             uint32_t thr, float c, uint64_t seed,
@@ -62,11 +38,7 @@ __global__ __launch_bounds__(256) void dropout_input_kernel(const uint16_t* __re
   const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
   uint32_t o[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = pack_bf16x2(__uint_as_float(xw[i] << 16) * c, 0.0f) & 0xFFFFu;
-    const uint32_t hi = pack_bf16x2(__uint_as_float(xw[i] & 0xFFFF0000u) * c, 0.0f) & 0xFFFFu;
-    o[i] = (u[2 * i] >= thr ? lo : 0u) | ((u[2 * i + 1] >= thr ? hi : 0u) << 16);
-  }
+  for (int i = 0; i < 4; ++i) o[i] = dropout_pair(xw[i], u[2 * i], u[2 * i + 1], thr, c);
   *reinterpret_cast<u32x4_t*>(Xd + e0) = u32x4_t{o[0], o[1], o[2], o[3]};
 }
 

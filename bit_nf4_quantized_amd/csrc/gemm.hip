@@ -527,14 +527,16 @@ static hipError_t make_l1t(const uint16_t* L1, int64_t K, int r, uint16_t* l1t, 
 
 // T = X L1 (fp32 split-K partials), then sT = bf16(s T) with row stride ldst
 // (zero-padded columns) and optionally T_out = bf16(T) [M][r].
+// dr (skinny path only): X is dropped in the skinny kernel's registers.
 static hipError_t lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* L1, int r, float s,
                             uint16_t* sT, int64_t ldst, uint16_t* T_out, float* part, uint16_t* l1t,
-                            hipStream_t stream) {
+                            hipStream_t stream, const DropoutParams* dr = nullptr) {
   if (skinny_ok(r, M, K)) {
     hipError_t e = make_l1t(L1, K, r, l1t, stream);
     if (e != hipSuccess) return e;
-    return skinny_nt(X, K, l1t, K, M, K, r, part, s, sT, ldst, 1.0f, T_out, stream);
+    return skinny_nt(X, K, l1t, K, M, K, r, part, s, sT, ldst, 1.0f, T_out, stream, dr);
   }
+  if (dr) return hipErrorInvalidValue;
   GemmArgs a = base_args();
   a.M = M; a.N = r; a.K = K;
   a.A = X; a.lda = K;
@@ -553,9 +555,13 @@ hipError_t linear_forward(const NF4View& W, const NF4Table& tab, const uint16_t*
   const int64_t K = W.cols, N = W.rows;
   if (M == 0) return hipSuccess;
   const LinearWorkspace L = linear_workspace_layout(M, K, N, r, dr != nullptr);
-  // the adapter branch's input: X, or its dropped copy
+  // the adapter branch's input: X, or its dropped copy. On the large-M path
+  // with the skinny T kernel, that kernel drops X in registers and no copy
+  // is written.
+  const bool large_m = M > 16 && !(M <= kMidMaxM && midm_fits(M, K, N));
+  const bool drop_in_t = dr && large_m && skinny_ok(r, M, K);
   const uint16_t* Xa = X;
-  if (dr) {
+  if (dr && !drop_in_t) {
     uint16_t* xd = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + L.xd_off);
     hipError_t e = launch_dropout_input(X, M * K, *dr, xd, stream);
     if (e != hipSuccess) return e;
@@ -582,7 +588,7 @@ hipError_t linear_forward(const NF4View& W, const NF4Table& tab, const uint16_t*
 
   const bool dense = fits_dense({M * K * 2, N * K * 2, M * rp * 2, N * rp * 2});
   const int64_t ldst = dense ? rp : r;
-  hipError_t e = lora_down(Xa, M, K, L1, r, s, sT, ldst, T_out, part, l1t, stream);
+  hipError_t e = lora_down(Xa, M, K, L1, r, s, sT, ldst, T_out, part, l1t, stream, drop_in_t ? dr : nullptr);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)cdiv(N, 32), (unsigned)cdiv(ldst, 32)), dim3(256), 0,
                      stream, L2, (int64_t)r, N, l2t, ldst);
@@ -632,10 +638,15 @@ hipError_t linear_backward(const NF4View& W, const NF4Table& tab, const uint16_t
 
   const bool dense = dX && M > 16 && (N % 64) == 0 && fits_dense({M * N * 2, K * N * 2, M * rp * 2, K * rp * 2});
   const int64_t ldsu = dense ? rp : r;
-  // the adapter branch's input: X, or its dropped copy (the same mask as the forward)
+  // the adapter branch's input: X, or its dropped copy (the same mask as the
+  // forward). When T comes from the forward and both adapter gradients take
+  // the skinny kernels, only dL1 reads the dropped input, and its kernel
+  // drops X in registers: no copy is written.
+  const bool skinny_grads = skinny_ok(r, M, K) && skinny_ok(r, M, N);
+  const bool drop_in_dl1 = dr && T && skinny_grads;
   const uint16_t* Xa = X;
   float* dd = reinterpret_cast<float*>(base + L.dd_off);
-  if (dr) {
+  if (dr && !drop_in_dl1) {
     uint16_t* xd = reinterpret_cast<uint16_t*>(base + L.xd_off);
     e = launch_dropout_input(X, M * K, *dr, xd, stream);
     if (e != hipSuccess) return e;
@@ -722,9 +733,10 @@ hipError_t linear_backward(const NF4View& W, const NF4Table& tab, const uint16_t
     if (e != hipSuccess) return e;
     T = tbuf;
   }
-  if (skinny_ok(r, M, K) && skinny_ok(r, M, N)) {
+  if (skinny_grads) {
     // dL1 = X^T sU  ([K][r]);  dL2 = s (dY^T T)^T  ([r][N])
-    e = skinny_tn(Xa, K, K, sU, ldsu, M, r, part, 1.0f, false, grad_bf16, dL1, stream);
+    e = skinny_tn(Xa, K, K, sU, ldsu, M, r, part, 1.0f, false, grad_bf16, dL1, stream,
+                  drop_in_dl1 ? dr : nullptr);
     if (e != hipSuccess) return e;
     return skinny_tn(dY, N, N, T, r, M, r, part, s, true, grad_bf16, dL2, stream);
   }

@@ -135,6 +135,14 @@ hipError_t launch_adam(float* theta, const float* g, float* m, float* v, int64_t
 hipError_t launch_merge(const NF4View& W, const NF4Table& tab, const uint16_t* L1, const uint16_t* L2, int r,
                         float s, uint16_t* out, hipStream_t stream);
 
+// LoRA dropout (dropout.hip): keep iff the element's Philox word >= thr,
+// kept values scaled by c.
+struct DropoutParams {
+  uint32_t thr;    // floor(p 2^32)
+  float c;         // RN32(1 / (1 - p))
+  uint64_t seed;
+};
+
 // Skinny adapter products (rank <= 64), skinny_gemm.hip.
 struct SkinnySplit {
   int Z;        // reduction slices
@@ -142,11 +150,14 @@ struct SkinnySplit {
 };
 SkinnySplit skinny_split(int64_t tiles, int64_t klen);
 size_t skinny_partial_bytes(int64_t M, int64_t K, int64_t N);
+// dr: A is the adapter input X ([M][K], lda == K), dropped in registers.
 hipError_t skinny_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M, int64_t K, int r,
                      float* part, float alpha, uint16_t* out, int64_t ldo, float alpha2, uint16_t* out2,
-                     hipStream_t stream);
+                     hipStream_t stream, const DropoutParams* dr = nullptr);
+// dr: L is the adapter input X ([M][W], ldl == W), dropped in registers.
 hipError_t skinny_tn(const uint16_t* L, int64_t ldl, int64_t W, const uint16_t* S, int64_t lds, int64_t M, int r,
-                     float* part, float alpha, bool transpose, bool out_bf16, void* out, hipStream_t stream);
+                     float* part, float alpha, bool transpose, bool out_bf16, void* out, hipStream_t stream,
+                     const DropoutParams* dr = nullptr);
 
 // Workspace of the linear layer (shared by forward and backward).
 struct LinearWorkspace {
@@ -177,13 +188,6 @@ hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int
                           int64_t ldc, float alpha, hipStream_t stream, const float* E = nullptr,
                           int64_t lde = 0);
 
-// LoRA dropout (dropout.hip): keep iff the element's Philox word >= thr,
-// kept values scaled by c.
-struct DropoutParams {
-  uint32_t thr;    // floor(p 2^32)
-  float c;         // RN32(1 / (1 - p))
-  uint64_t seed;
-};
 DropoutParams dropout_params(float p, uint64_t seed);
 hipError_t launch_dropout_input(const uint16_t* X, int64_t numel, const DropoutParams& d, uint16_t* Xd,
                                 hipStream_t stream);

@@ -17,13 +17,21 @@
 // skinny_nt_kernel:  C[z][m][j] = sum_{k in slice z} A[m][k] B[j][k]
 //   A [M][K] and B [64][K] (rows j >= r are zero) are both K-contiguous and
 //   are copied global -> LDS by global_load_lds_dwordx4; 128 rows x 64 j per
-//   workgroup, 4 waves of 32 rows, K-stages of 64, 3-stage ring.
+//   workgroup, 4 waves of 32 rows, K-stages of 64, 3-stage ring. With LoRA
+//   dropout (DROP) A is the adapter input X, and every A fragment is
+//   dropped in registers after its LDS read (each A element is read by
+//   exactly one lane), from the Philox words of its element indices.
 // skinny_tn_kernel:  C[z][c][j] = sum_{m in slice z} L[m][c] S[m][j]
 //   the reduction runs down the rows of both operands, so each thread loads
 //   two rows x 8 columns and writes them to LDS transposed as (m, m+1)
-//   pairs; 128 columns c x 64 j per workgroup, M-stages of 64.
+//   pairs; 128 columns c x 64 j per workgroup, M-stages of 64. With LoRA
+//   dropout (DROP) the large operand is the adapter input X and the loaded
+//   values are dropped in registers, from the Philox words of their element
+//   indices m W + c, before they go to LDS: the dropped copy of X is never
+//   written to memory.
 #include "common.h"
 #include "launch.h"
+#include "philox.h"
 
 namespace qlora {
 
@@ -53,8 +61,12 @@ struct NtArgs {
   const uint16_t* B;  // [SJ][ldb]  (64 rows; rows >= r zero)
   float* C;           // [Z][M][SJ]
   int64_t lda, ldb, M, K, k_split;
+  uint32_t thr;       // DROP: keep iff the element's Philox word >= thr; kept values scaled by c
+  float c;
+  uint64_t seed;
 };
 
+template <bool DROP>
 __global__ __launch_bounds__(kSkThreads) void skinny_nt_kernel(NtArgs p) {
   __shared__ __attribute__((aligned(1024))) uint16_t sA[kNtStages][SM * SK];
   __shared__ __attribute__((aligned(1024))) uint16_t sB[kNtStages][SJ * SK];
@@ -112,7 +124,17 @@ __global__ __launch_bounds__(kSkThreads) void skinny_nt_kernel(NtArgs p) {
 #pragma unroll
     for (int kk = 0; kk < SK / 16; ++kk) {
       const int ch = 2 * kk + (lane >> 5);
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(sA[buf] + sk_off(wave * 32 + (lane & 31), ch));
+      bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(sA[buf] + sk_off(wave * 32 + (lane & 31), ch));
+      if constexpr (DROP) {
+        // element indices of the 8 values: row m of X (row length lda), columns k .. k+7
+        const int64_t e0 = (m0 + wave * 32 + (lane & 31)) * p.lda + kz0 + (int64_t)st * SK + ch * 8;
+        const u32x4_t u0 = philox_block(e0 >> 2, p.seed), u1 = philox_block((e0 >> 2) + 1, p.seed);
+        const u32x4_t v = __builtin_bit_cast(u32x4_t, a);
+        a = __builtin_bit_cast(bf16x8_t, u32x4_t{dropout_pair(v.x, u0.x, u0.y, p.thr, p.c),
+                                                 dropout_pair(v.y, u0.z, u0.w, p.thr, p.c),
+                                                 dropout_pair(v.z, u1.x, u1.y, p.thr, p.c),
+                                                 dropout_pair(v.w, u1.z, u1.w, p.thr, p.c)});
+      }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(sB[buf] + sk_off(t * 32 + (lane & 31), ch));
@@ -140,8 +162,12 @@ struct TnArgs {
   const uint16_t* S;  // [M][lds]  small operand (U or T), r columns valid
   float* C;           // [Z][W][SJ]
   int64_t ldl, lds, M, W, r, m_split;
+  uint32_t thr;       // DROP: keep iff the element's Philox word >= thr; kept values scaled by c
+  float c;
+  uint64_t seed;
 };
 
+template <bool DROP>
 __global__ __launch_bounds__(kSkThreads) void skinny_tn_kernel(TnArgs p) {
   __shared__ __attribute__((aligned(1024))) uint16_t sL[SM * SK];  // [c][m]
   __shared__ __attribute__((aligned(1024))) uint16_t sS[SJ * SK];  // [j][m]
@@ -189,9 +215,27 @@ __global__ __launch_bounds__(kSkThreads) void skinny_tn_kernel(TnArgs p) {
     }
   };
 
+  // DROP: the staged rows of L (row-major [M][W], W % 64 == 0) after dropout;
+  // out-of-range values were loaded as 0 and stay 0
+  auto drop = [&](int64_t ms) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t m = ms + 2 * l_rp + h;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int64_t e0 = m * p.W + c0 + (l_cq * 2 + q) * 8;  // multiple of 8: two Philox blocks
+        const u32x4_t u0 = philox_block(e0 >> 2, p.seed), u1 = philox_block((e0 >> 2) + 1, p.seed);
+        u32x4_t& v = lv[h][q];
+        v = u32x4_t{dropout_pair(v.x, u0.x, u0.y, p.thr, p.c), dropout_pair(v.y, u0.z, u0.w, p.thr, p.c),
+                    dropout_pair(v.z, u1.x, u1.y, p.thr, p.c), dropout_pair(v.w, u1.z, u1.w, p.thr, p.c)};
+      }
+    }
+  };
+
   if (mz0 < mz1) load(mz0);
   for (int64_t ms = mz0; ms < mz1; ms += SK) {
     __syncthreads();  // previous stage's fragment reads are done
+    if constexpr (DROP) drop(ms);
     const int mloc = 2 * l_rp;
 #pragma unroll
     for (int q = 0; q < 2; ++q) put_pairs(sL, (l_cq * 2 + q) * 8, lv[0][q], lv[1][q], mloc);
@@ -330,12 +374,17 @@ size_t skinny_partial_bytes(int64_t M, int64_t K, int64_t N) {
 // C = A B^T over K with B [64][ldb] (rows >= r zero), then reduce.
 hipError_t skinny_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M, int64_t K, int r,
                      float* part, float alpha, uint16_t* out, int64_t ldo, float alpha2, uint16_t* out2,
-                     hipStream_t stream) {
+                     hipStream_t stream, const DropoutParams* dr) {
+  if (dr && lda != K) return hipErrorInvalidValue;  // the mask indexes a contiguous [M][K] input
   const SkinnySplit sp = skinny_split(sk_cdiv(M, SM), K);
   NtArgs a;
   a.A = A; a.B = B; a.C = part; a.lda = lda; a.ldb = ldb; a.M = M; a.K = K; a.k_split = sp.len;
-  hipLaunchKernelGGL(skinny_nt_kernel, dim3((unsigned)sk_cdiv(M, SM), 1, (unsigned)sp.Z), dim3(kSkThreads), 0, stream,
-                     a);
+  a.thr = dr ? dr->thr : 0u; a.c = dr ? dr->c : 1.0f; a.seed = dr ? dr->seed : 0u;
+  const dim3 grid((unsigned)sk_cdiv(M, SM), 1, (unsigned)sp.Z);
+  if (dr)
+    hipLaunchKernelGGL(skinny_nt_kernel<true>, grid, dim3(kSkThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(skinny_nt_kernel<false>, grid, dim3(kSkThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)sk_grid(M * ldo)), dim3(256), 0, stream, part, sp.Z, M, r,
@@ -345,12 +394,18 @@ hipError_t skinny_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t 
 
 // C[c][j] = sum_m L[m][c] S[m][j], then reduce to out (transposed if `transpose`).
 hipError_t skinny_tn(const uint16_t* L, int64_t ldl, int64_t W, const uint16_t* S, int64_t lds, int64_t M, int r,
-                     float* part, float alpha, bool transpose, bool out_bf16, void* out, hipStream_t stream) {
+                     float* part, float alpha, bool transpose, bool out_bf16, void* out, hipStream_t stream,
+                     const DropoutParams* dr) {
+  if (dr && (ldl != W || W % 64)) return hipErrorInvalidValue;  // the mask indexes a contiguous [M][W] input
   const SkinnySplit sp = skinny_split(sk_cdiv(W, SM), M);
   TnArgs a;
   a.L = L; a.S = S; a.C = part; a.ldl = ldl; a.lds = lds; a.M = M; a.W = W; a.r = r; a.m_split = sp.len;
-  hipLaunchKernelGGL(skinny_tn_kernel, dim3((unsigned)sk_cdiv(W, SM), 1, (unsigned)sp.Z), dim3(kSkThreads), 0, stream,
-                     a);
+  a.thr = dr ? dr->thr : 0u; a.c = dr ? dr->c : 1.0f; a.seed = dr ? dr->seed : 0u;
+  const dim3 grid((unsigned)sk_cdiv(W, SM), 1, (unsigned)sp.Z);
+  if (dr)
+    hipLaunchKernelGGL(skinny_tn_kernel<true>, grid, dim3(kSkThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(skinny_tn_kernel<false>, grid, dim3(kSkThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (transpose)
