@@ -59,6 +59,27 @@ def test_type_tables_match_oracle_bit_exact(lib, name):
     assert g.view(np.uint32).tolist() == qtypes.codebook(name).view(np.uint32).tolist()
 
 
+@pytest.mark.parametrize("name", ["nf4", "int4", "fp4_e2m1", "fp4_e3m0"])
+def test_quantiser_buckets_hold_at_most_one_threshold(lib, name):
+    """The GPU quantiser finds a code as (thresholds in lower buckets) + one
+    compare, over 512 buckets b(x) = trunc(clamp(RN32(RN32(x + 1) * 256), 0,
+    511)) of the normalised value. That equals the nearest code only if no
+    bucket holds two decision thresholds; the thresholds are the smallest
+    fp32 strictly above each exact midpoint of neighbouring table values."""
+    q = api.qlora_codebook(name).astype(np.float32)
+    th = []
+    for j in range(15):
+        m = 0.5 * (float(q[j]) + float(q[j + 1]))
+        f = np.float32(m)
+        if not float(f) > m:
+            f = np.nextafter(f, np.float32(np.inf))
+        th.append(f)
+    y = (np.array(th, np.float32) + np.float32(1.0)) * np.float32(256.0)
+    b = np.minimum(np.maximum(y, np.float32(0.0)), np.float32(511.0)).astype(np.int32)
+    assert np.all(np.diff(b) >= 0)                   # the map is monotone
+    assert len(np.unique(b)) == 15, b.tolist()       # one threshold per bucket at most
+
+
 def test_codebook_rejects_bad_type(lib):
     import ctypes
 
