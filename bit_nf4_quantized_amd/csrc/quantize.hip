@@ -10,15 +10,16 @@
 // Kernels (all HBM-bound; see the launchers at the bottom):
 //   quant_blocks_kernel   one workgroup per DQ group of 256 blocks
 //                         (16384 weights): coalesced loads, absmax by
-//                         cross-lane max over the 8 lanes of a block, codes,
-//                         nibble packing, and the float64 adjacent-pair tree
+//                         cross-lane max over the 8 lanes of a block, codes
+//                         from a 512-bucket LDS table, nibble packing, and
+//                         the float64 adjacent-pair tree
 //                         sum of the group's 256 absmax values in LDS.
 //   tree_fold_kernel      one workgroup folds the per-group sums with the
 //                         same adjacent-pair rule and writes the fp32 mean.
 //   dq_encode_kernel      one workgroup per group: a - mean, group absmax,
 //                         fp32 scale, E4M3 codes.
-//   dequant_kernel        16 weights per thread: codes + E4M3 constants ->
-//                         bf16, 2 x 16-byte stores.
+//   dequant_kernel        4 units of 8 weights per thread: a code dword + the
+//                         E4M3 constant -> bf16, one 16-byte store per unit.
 #include "common.h"
 #include "launch.h"
 
@@ -88,7 +89,8 @@ __device__ __forceinline__ void unpack8<uint16_t>(const u32x4_t* raw, float v[8]
 // apart). Then every threshold in a lower bucket is below x and every one in
 // a higher bucket above it, so the code is the count of thresholds in lower
 // buckets plus one compare with the bucket's own threshold (+inf if none):
-// the same result as the binary search, for about a third of its VALU work.
+// the same result as a search over the thresholds, for about a third of the
+// VALU work of a 4-level select search.
 constexpr int kLutBuckets = 512;
 
 __device__ __forceinline__ int lut_bucket(float x) {
