@@ -269,61 +269,68 @@ __global__ __launch_bounds__(kSkThreads) void skinny_tn_kernel(TnArgs p) {
 //   mode 0: out[m][j] (row stride ldo; columns [r, ldo) zero) in bf16, plus
 //           optional out2[m][j] = bf16(alpha2 * sum) with row stride r
 //   mode 1: out[m][j] fp32 or bf16, row stride r
+// Four consecutive columns per thread (r % 8 == 0 and ldo % 4 == 0, so a
+// group of four is all below r or all at or above it): 16-byte partial loads,
+// the sum over z in order, 8- or 16-byte stores.
 __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ P, int Z, int64_t rows, int r,
                                                             float alpha, int mode, int out_bf16, void* __restrict__ out,
                                                             int64_t ldo, float alpha2, uint16_t* __restrict__ out2) {
   const int64_t width = (mode == 0) ? ldo : r;
-  const int64_t total = rows * width;
+  const int64_t w4 = width / 4;
+  const int64_t total = rows * w4;
   const int64_t slab = rows * SJ;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t m = i / width, j = i - m * width;
+    const int64_t m = i / w4, j = (i - m * w4) * 4;
+    const int64_t o = m * width + j;
     if (j >= r) {
-      static_cast<uint16_t*>(out)[i] = 0;
+      *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out) + o) = u32x2_t{0u, 0u};
       continue;
     }
-    float acc = 0.0f;
-    for (int z = 0; z < Z; ++z) acc += P[(int64_t)z * slab + m * SJ + j];
-    const float v = alpha * acc;
-    if (out_bf16) static_cast<uint16_t*>(out)[i] = f32_to_bf16(v);
-    else static_cast<float*>(out)[i] = v;
-    if (mode == 0 && out2) out2[m * r + j] = f32_to_bf16(alpha2 * acc);
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int z = 0; z < Z; ++z) acc += *reinterpret_cast<const f32x4_t*>(P + (int64_t)z * slab + m * SJ + j);
+    const f32x4_t v = {alpha * acc.x, alpha * acc.y, alpha * acc.z, alpha * acc.w};
+    if (out_bf16)
+      *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out) + o) = u32x2_t{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+    else
+      *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + o) = v;
+    if (mode == 0 && out2)
+      *reinterpret_cast<u32x2_t*>(out2 + m * r + j) =
+          u32x2_t{pack_bf16x2(alpha2 * acc.x, alpha2 * acc.y), pack_bf16x2(alpha2 * acc.z, alpha2 * acc.w)};
   }
 }
 
 // Transposed reduction: out[j][c] = alpha * sum_z P[z][c][j] for j < r, c < W,
-// output row stride W. One workgroup per 64 columns c: the Z partial tiles
-// (64 c x 64 j, contiguous) are read with 16-byte loads and summed in a fixed
-// z order, then transposed through LDS so that every output row segment is
-// written contiguously.
+// output row stride W. One workgroup per 64 columns c and 16 ranks j (so
+// that even W = 4096 gives 256 workgroups): each thread sums 4 ranks of one
+// column over the Z partial tiles in a fixed z order (16-byte loads), the
+// 64 x 16 result is transposed through LDS, and each output row segment is
+// written 4 columns per thread.
 __global__ __launch_bounds__(256) void skinny_reduce_t_kernel(const float* __restrict__ P, int Z, int64_t W, int r,
                                                               float alpha, int out_bf16, void* __restrict__ out) {
-  __shared__ float tile[64][65];
+  __shared__ float tile[64][16 + 1];
   const int t = threadIdx.x;
   const int64_t c0 = (int64_t)blockIdx.x * 64;
-  const int cl = t >> 2, jq = (t & 3) * 16;     // column c0 + cl, ranks jq .. jq+16
+  const int j0 = blockIdx.y * 16;
+  if (j0 >= r) return;                         // uniform per workgroup
+  const int cl = t >> 2, jq = (t & 3) * 4;     // column c0 + cl, ranks j0 + jq .. +4
   const int64_t c = c0 + cl;
-  f32x4_t acc[4] = {};
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
   if (c < W) {
     const int64_t slab = W * SJ;
-    for (int z = 0; z < Z; ++z) {
-      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(P + (int64_t)z * slab + c * SJ + jq);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] += src[q];
-    }
+    for (int z = 0; z < Z; ++z) acc += *reinterpret_cast<const f32x4_t*>(P + (int64_t)z * slab + c * SJ + j0 + jq);
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) tile[cl][jq + 4 * q + e] = acc[q][e];
+  for (int e = 0; e < 4; ++e) tile[cl][jq + e] = acc[e];
   __syncthreads();
-  const int j = t >> 2, cq = (t & 3) * 16;      // rank j, columns c0 + cq .. +16
+  const int jl = t >> 4, cq = (t & 15) * 4;   // rank j0 + jl, columns c0 + cq .. +4
+  const int j = j0 + jl;
   if (j < r) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int e = 0; e < 4; ++e) {
       const int64_t cc = c0 + cq + e;
       if (cc < W) {
-        const float v = alpha * tile[cq + e][j];
+        const float v = alpha * tile[cq + e][jl];
         if (out_bf16) static_cast<uint16_t*>(out)[(int64_t)j * W + cc] = f32_to_bf16(v);
         else static_cast<float*>(out)[(int64_t)j * W + cc] = v;
       }
@@ -387,7 +394,7 @@ hipError_t skinny_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t 
     hipLaunchKernelGGL(skinny_nt_kernel<false>, grid, dim3(kSkThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)sk_grid(M * ldo)), dim3(256), 0, stream, part, sp.Z, M, r,
+  hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)sk_grid(M * ldo / 4)), dim3(256), 0, stream, part, sp.Z, M, r,
                      alpha, 0, 1, (void*)out, ldo, alpha2, out2);
   return hipGetLastError();
 }
@@ -409,10 +416,10 @@ hipError_t skinny_tn(const uint16_t* L, int64_t ldl, int64_t W, const uint16_t* 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (transpose)
-    hipLaunchKernelGGL(skinny_reduce_t_kernel, dim3((unsigned)sk_cdiv(W, 64)), dim3(256), 0, stream, part, sp.Z, W, r,
+    hipLaunchKernelGGL(skinny_reduce_t_kernel, dim3((unsigned)sk_cdiv(W, 64), SJ / 16), dim3(256), 0, stream, part, sp.Z, W, r,
                        alpha, out_bf16 ? 1 : 0, out);
   else
-    hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)sk_grid(W * (int64_t)r)), dim3(256), 0, stream, part, sp.Z,
+    hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)sk_grid(W * (int64_t)r / 4)), dim3(256), 0, stream, part, sp.Z,
                        W, r, alpha, 1, out_bf16 ? 1 : 0, out, (int64_t)r, 0.0f, (uint16_t*)nullptr);
   return hipGetLastError();
 }
