@@ -383,6 +383,42 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
   }
 }
 
+// Two independent transposes of the kind above in one launch (the adapter
+// matrices are small, so each alone is mostly launch latency): workgroups
+// [0, a.tiles) take job a, the rest job b; tiles are 32 x 32, row-major
+// over (src columns / 32) x (dst columns / 32).
+struct TransposeJob {
+  const uint16_t* src;
+  int64_t R, C;
+  uint16_t* dst;
+  int64_t ldd;
+  int gx, tiles;  // tiles along src columns; gx * (tiles along dst columns)
+};
+
+TransposeJob transpose_job(const uint16_t* src, int64_t R, int64_t C, uint16_t* dst, int64_t ldd) {
+  TransposeJob j{src, R, C, dst, ldd, (int)((C + 31) / 32), 0};
+  j.tiles = j.gx * (int)((ldd + 31) / 32);
+  return j;
+}
+
+__global__ __launch_bounds__(256) void transpose2_kernel(TransposeJob a, TransposeJob b) {
+  __shared__ uint16_t tile[32][33];
+  const bool first = (int)blockIdx.x < a.tiles;  // uniform per workgroup
+  const TransposeJob& j = first ? a : b;
+  const int id = first ? (int)blockIdx.x : (int)blockIdx.x - a.tiles;
+  const int64_t c0 = (int64_t)(id % j.gx) * 32, r0 = (int64_t)(id / j.gx) * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  for (int y = ty; y < 32; y += 8) {
+    const int64_t r = r0 + y, c = c0 + tx;
+    tile[y][tx] = (r < j.R && c < j.C) ? j.src[r * j.C + c] : 0;
+  }
+  __syncthreads();
+  for (int y = ty; y < 32; y += 8) {
+    const int64_t c = c0 + y, r = r0 + tx;
+    if (r < j.ldd && c < j.C) j.dst[c * j.ldd + r] = tile[tx][y];
+  }
+}
+
 // dst[r][c] = src[r][c] for c < C, 0 for C <= c < ldd (bf16).
 __global__ __launch_bounds__(256) void pad_cols_kernel(const uint16_t* __restrict__ src, int64_t R, int64_t C,
                                                        uint16_t* __restrict__ dst, int64_t ldd) {
@@ -530,9 +566,9 @@ static hipError_t make_l1t(const uint16_t* L1, int64_t K, int r, uint16_t* l1t, 
 // dr (skinny path only): X is dropped in the skinny kernel's registers.
 static hipError_t lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* L1, int r, float s,
                             uint16_t* sT, int64_t ldst, uint16_t* T_out, float* part, uint16_t* l1t,
-                            hipStream_t stream, const DropoutParams* dr = nullptr) {
+                            hipStream_t stream, const DropoutParams* dr = nullptr, bool l1t_ready = false) {
   if (skinny_ok(r, M, K)) {
-    hipError_t e = make_l1t(L1, K, r, l1t, stream);
+    hipError_t e = l1t_ready ? hipSuccess : make_l1t(L1, K, r, l1t, stream);
     if (e != hipSuccess) return e;
     return skinny_nt(X, K, l1t, K, M, K, r, part, s, sT, ldst, 1.0f, T_out, stream, dr);
   }
@@ -588,11 +624,22 @@ hipError_t linear_forward(const NF4View& W, const NF4Table& tab, const uint16_t*
 
   const bool dense = fits_dense({M * K * 2, N * K * 2, M * rp * 2, N * rp * 2});
   const int64_t ldst = dense ? rp : r;
-  hipError_t e = lora_down(Xa, M, K, L1, r, s, sT, ldst, T_out, part, l1t, stream, drop_in_t ? dr : nullptr);
+  // L2^T for the GEMM's slab stage, and with the skinny T kernel also L1^T,
+  // in one launch
+  const bool skinny_t = skinny_ok(r, M, K);
+  const TransposeJob jl2 = transpose_job(L2, (int64_t)r, N, l2t, ldst);
+  if (skinny_t) {
+    if (r < 64)  // rows r .. 63 of L1^T are zero
+      hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)grid_for((64 - r) * K / 2)), dim3(256), 0, stream,
+                         reinterpret_cast<uint32_t*>(l1t + (int64_t)r * K), (size_t)((64 - r) * K / 2));
+    const TransposeJob jl1 = transpose_job(L1, K, (int64_t)r, l1t, K);
+    hipLaunchKernelGGL(transpose2_kernel, dim3((unsigned)(jl1.tiles + jl2.tiles)), dim3(256), 0, stream, jl1, jl2);
+  } else {
+    hipLaunchKernelGGL(transpose2_kernel, dim3((unsigned)jl2.tiles), dim3(256), 0, stream, jl2, jl2);
+  }
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((unsigned)cdiv(N, 32), (unsigned)cdiv(ldst, 32)), dim3(256), 0,
-                     stream, L2, (int64_t)r, N, l2t, ldst);
-  e = hipGetLastError();
+  e = lora_down(Xa, M, K, L1, r, s, sT, ldst, T_out, part, l1t, stream, drop_in_t ? dr : nullptr, skinny_t);
   if (e != hipSuccess) return e;
 
   if (dense) {
