@@ -397,58 +397,36 @@ __global__ __launch_bounds__(256) void dequant_rows_kernel(NF4View W, NF4Table t
 }
 
 // WdT[k][n] = Wd[n][k] for the dX product, rows padded to ldo >= N columns
-// with zeros. One workgroup per 64 x 64 tile (64 weight rows n, 64 weight
-// columns k = one 64-block per row): each thread dequantises 16 weights of
-// one row, the tile is transposed through LDS, and written 16 bytes per thread.
+// with zeros, without LDS: a thread dequantises two adjacent weight rows
+// (n, n+1) over 32 k (16 code bytes each, inside one 64-block), so that each
+// (row n, row n+1) pair at one k is one dword of output row k; the 64 lanes
+// of a wave take 64 consecutive row pairs, so every store instruction
+// writes 256 contiguous bytes. Workgroup: 128 rows n x 128 k (4 waves along k).
 __global__ __launch_bounds__(256) void dequant_cols_kernel(NF4View W, NF4Table tab, uint16_t* __restrict__ out,
                                                            int64_t ldo) {
   __shared__ float s_q[16];
-  __shared__ uint16_t tile[64][64 + 8];
   if (threadIdx.x < 16) s_q[threadIdx.x] = tab.q[threadIdx.x];
   __syncthreads();
   const float mu = tensor_mean(W);
   const int64_t K = W.cols, N = W.rows;
-  const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
-  const int t = threadIdx.x;
-  {
-    const int row = t >> 2, part = t & 3;  // 64 rows x 4 parts of 16 weights
-    const int64_t n = n0 + row;
-    uint32_t o[8];
-    if (n < N) {
-      const int64_t e0 = n * K + k0 + part * 16;
-      const int64_t blk = e0 / kBlock;
-      const float ap = block_const(W, blk, mu);
-      const u32x2_t c = *reinterpret_cast<const u32x2_t*>(W.codes + (e0 >> 1));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n = (int64_t)blockIdx.y * 128 + 2 * lane;           // rows n, n + 1 (N % 8 == 0)
+  const int64_t k0 = (int64_t)blockIdx.x * 128 + wave * 32;         // k0 .. k0 + 32
+  if (k0 >= K) return;                                              // wave-uniform; no barrier follows
+  const bool in = n < N;
+  const int64_t na = in ? n : 0;
+  const int64_t e0 = na * K + k0, e1 = e0 + K;
+  const u32x4_t ca = *reinterpret_cast<const u32x4_t*>(W.codes + (e0 >> 1));
+  const u32x4_t cb = *reinterpret_cast<const u32x4_t*>(W.codes + (e1 >> 1));
+  const float aa = block_const(W, e0 / kBlock, mu), ab = block_const(W, e1 / kBlock, mu);
+  const uint32_t wa[4] = {ca.x, ca.y, ca.z, ca.w}, wb[4] = {cb.x, cb.y, cb.z, cb.w};
+  if (n >= ldo) return;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t word = (i < 4) ? c.x : c.y;
-        const uint32_t byte = (word >> (8 * (i & 3))) & 0xFFu;
-        o[i] = pack_bf16x2(s_q[byte & 15u] * ap, s_q[byte >> 4] * ap);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] = 0u;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      tile[row][part * 16 + 2 * i] = (uint16_t)(o[i] & 0xFFFFu);
-      tile[row][part * 16 + 2 * i + 1] = (uint16_t)(o[i] >> 16);
-    }
-  }
-  __syncthreads();
-  {
-    const int kr = t >> 2, part = t & 3;  // output row k0+kr, columns n0 + 16 part .. +16
-    const int64_t k = k0 + kr;
-    uint32_t o[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      o[i] = (uint32_t)tile[part * 16 + 2 * i][kr] | ((uint32_t)tile[part * 16 + 2 * i + 1][kr] << 16);
-    const int64_t c0 = n0 + part * 16;
-    if (k < K && c0 < ldo) {
-      u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + k * ldo + c0);
-      dst[0] = u32x4_t{o[0], o[1], o[2], o[3]};
-      dst[1] = u32x4_t{o[4], o[5], o[6], o[7]};
-    }
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t qa = (wa[i >> 3] >> (4 * (i & 7))) & 15u;
+    const uint32_t qb = (wb[i >> 3] >> (4 * (i & 7))) & 15u;
+    const uint32_t v = in ? pack_bf16x2(s_q[qa] * aa, s_q[qb] * ab) : 0u;
+    *reinterpret_cast<uint32_t*>(out + (k0 + i) * ldo + n) = v;
   }
 }
 
@@ -466,7 +444,7 @@ hipError_t launch_dequant_rows(const NF4View& W, const NF4Table& tab, uint16_t* 
 
 hipError_t launch_dequant_cols(const NF4View& W, const NF4Table& tab, uint16_t* out, int64_t ldo,
                                hipStream_t stream) {
-  const dim3 grid((unsigned)(W.cols / 64), (unsigned)((ldo + 63) / 64));
+  const dim3 grid((unsigned)((W.cols + 127) / 128), (unsigned)((ldo + 127) / 128));
   hipLaunchKernelGGL(dequant_cols_kernel, grid, dim3(256), 0, stream, W, tab, out, ldo);
   return hipGetLastError();
 }
