@@ -1,13 +1,15 @@
 #!/usr/bin/env python3
 """Benchmark of the QLoRA NF4 hot path on one MI355X.
 
-Timed step: forward + backward of all 7 linears of a LLaMA-7B-shaped layer
-(q, k, v, o 4096x4096; gate, up 4096->11008; down 11008->4096) for 8192
-tokens with NF4 + DQ base weights (normal, 0.1 % outliers x10), LoRA rank 64
-on every linear, s = 0.25. Per linear: qlora_linear_fwd (Y and T) then
-qlora_linear_bwd (dX, dL1, dL2). The weights are quantised once before
+Timed step (the headline): forward + backward of all 7 linears of a
+LLaMA-33B-shaped block (q, k, v, o 6656x6656; gate, up 6656->17920; down
+17920->6656) for 8192 tokens (4 x 2048) with NF4 + DQ base weights drawn
+from a Student-t distribution with 4 degrees of freedom (std 0.02), LoRA
+rank 64 on every linear, s = 0.25. Per linear: qlora_linear_fwd (Y and T)
+then qlora_linear_bwd (dX, dL1, dL2). The weights are quantised once before
 timing (the base is frozen, as in QLoRA training). Inputs are synthetic and
-already resident in HBM when timing starts.
+already resident in HBM when timing starts. The K timed steps are repeated
+in 5 trials; value is the median trial.
 
 value = algorithmic fwd+bwd flops per step / time per step, with flops
 4 M K N + 6 M r (K + N) per linear (3 forward and 5 backward products, no
@@ -18,29 +20,33 @@ The same run also measures:
     computes both Y = X Wd^T + (s X L1) L2 and dX = dY Wd + (s dY L2^T) L1^T,
     from HIP events that the library records around each of its launches on
     the call's stream, in a second pass of the same steps (the timed steps
-    themselves run without those brackets, which cost about 14 us each);
-    its HBM traffic comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counters
-    stored under profiles/ (scaled by the same counters on a plain device
-    copy, see --copy-probe) and is reported only while the kernel source
-    still has the hash recorded with them;
+    themselves run without those brackets); its HBM traffic comes from
+    rocprofv3 FETCH_SIZE / WRITE_SIZE counters stored under profiles/
+    (scaled by the same counters on a plain device copy, see --copy-probe)
+    and is reported only while the kernel source still has the hash
+    recorded with them;
+  * the same step on the LLaMA-7B-shaped layer set (normal weights with 0.1 %
+    outliers x10), with its own GEMM roofline;
+  * the same headline step with LoRA dropout 0.05 (the pages' 33B setting);
   * the small-M dequant-GEMV (M in {1, 4, 16}; 4096->11008 and 11008->4096)
     in GB/s against 8 TB/s, cycling >= 24 distinct weight copies (> 512 MB)
     so the 256 MB last-level cache cannot serve the weights;
-  * NF4 + DQ quantisation throughput on a LLaMA-65B-shaped tensor;
+  * the LLaMA-65B-shaped quantisation pass: 80 layers x 7 tensors (560
+    tensors, 64.76 B weights) quantised from fp32 and from bf16, drawn from
+    a pool of 2 layers cycled 40 times into 80 distinct output sets;
   * the four 4-bit data types (NF4, Int4, FP4 E2M1, FP4 E3M0, all with DQ)
     and NF4 without DQ on a 4096 x 11008 weight: relative RMS error of the
     dequantised weight for normal (0.1 % outliers) and Student-t weights,
     storage bits per parameter and quantise GB/s;
   * the blockwise Int8 absmax codec: quantise and dequantise GB/s on the
     LLaMA-65B gate-shaped tensor, and the error by block size (64 .. 4096);
-  * the same step with LoRA dropout 0.1 on every adapter;
   * the batched-decode forward at M in {32, 64, 128};
   * the optimiser step (clip + Adam) at the size of all LLaMA-7B adapters,
     with 0-100 % of the Adam state paged out to pinned host memory;
   * the adapter merge (bf16 dequantised base + s L1 L2, r = 64) in GB/s on
     the LLaMA-7B linear shapes;
-  * the CPU oracle on the same step (all 7 linears, 8192 tokens) as a
-    baseline.
+  * the CPU oracle on the headline step (all 7 linears, 8192 tokens) as a
+    baseline, and on one layer of the 65B quantisation pass (x80).
 Prints one JSON line.
 """
 
@@ -59,7 +65,11 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 GEMM_SOURCE = os.path.join(ROOT, "bit_nf4_quantized_amd", "csrc", "dense_gemm.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_nt_llama7b-layer_hbm-traffic.md")
+HEADLINE = "llama33b-layer"
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"gemm_nt_{workload}_hbm-traffic.md")
 
 
 def log(msg):
@@ -115,8 +125,9 @@ def run_step(api, layers, ws):
 
 
 def bench_dropout_step(api, layers, flops_step, plain_ms, steps=5, warmup=2, p=0.1, seed=2024):
-    """The same fwd+bwd step with LoRA dropout p = 0.1 on every adapter
-    (the 7B/13B Guanaco setting): ms per step and the cost over the plain step."""
+    """The same fwd+bwd step with LoRA dropout p on every adapter (the
+    pages' Guanaco settings: 0.1 for 7B/13B, 0.05 for 33B/65B): ms per step
+    and the cost over the plain step."""
     import torch
 
     ws_bytes = max(api.qlora_linear_workspace_dropout(d["M"], d["shape"].K, d["shape"].N, d["r"]) for d in layers)
@@ -145,13 +156,14 @@ def bench_dropout_step(api, layers, flops_step, plain_ms, steps=5, warmup=2, p=0
     return {"p": p, "ms_per_step": ms, "tflops": flops_step / (ms * 1e-3) / 1e12, "overhead_vs_plain": ms / plain_ms - 1}
 
 
-def gemm_traffic():
-    """HBM bytes per gemm_nt_kernel launch from the stored counter summary, or
-    None when it is absent or was taken on a different kernel source."""
+def gemm_traffic(workload):
+    """HBM bytes per gemm_nt_kernel launch from the stored counter summary of
+    this workload, or None when it is absent or was taken on a different
+    kernel source."""
     import hashlib
 
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(traffic_file(workload)).read()
     except OSError:
         return None
     src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
@@ -517,18 +529,46 @@ def bench_qtypes(api, workloads, reps=5):
     return out
 
 
-def cpu_baseline(host, tokens=8192):
-    """The oracle (dequant + forward + backward) on all 7 linears for a sample
-    of the tokens, on the host cores; reported in the same unit."""
+def host_info():
+    """Host cores, CPU model and BLAS library of this machine (for the
+    oracle baselines)."""
+    import subprocess
+
     import numpy as np
 
-    from oracle import linear, nf4
-
+    info = {"os_cpu_count": os.cpu_count()}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+    except Exception:  # pragma: no cover
+        pass
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+            info["blas_threads"] = max(int(p.get("num_threads", 1)) for p in blas)
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        pass
+    if "blas" not in info:
+        cfg = np.show_config(mode="dicts") if hasattr(np, "show_config") else {}
+        try:
+            info["blas"] = cfg["Build Dependencies"]["blas"]["name"]
+        except Exception:  # pragma: no cover
+            info["blas"] = "unknown"
+    return info
+
+
+def cpu_baseline(host, tokens=8192):
+    """The oracle (dequant + forward + backward) on all 7 linears of the
+    timed step, on the host cores; reported in the same unit."""
+    from oracle import linear, nf4
+
+    hi = host_info()
+    cores = hi.get("blas_threads", os.cpu_count() or 1)
     qts = [(shp, inp, nf4.quantize(inp.W)) for shp, inp in host]   # outside the timed region
     flops = 0
     t0 = time.perf_counter()
@@ -540,19 +580,151 @@ def cpu_baseline(host, tokens=8192):
         flops += linear_flops(tokens, shp.K, shp.N, inp.L1.shape[1])
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "seconds": dt,
-            "sample": f"all 7 linears, {tokens} of 8192 tokens: float64 NumPy dequant + fwd + bwd "
-                      f"(BLAS threads = cores; elementwise steps single-threaded)"}
+            "seconds": dt, "host": hi,
+            "sample": f"the whole timed step: all 7 linears, {tokens} tokens; float64 NumPy dequant + fwd + bwd. "
+                      f"The matmuls run on {cores} BLAS threads; the dequantisation is single-threaded NumPy."}
+
+
+def setup_and_time(api, workloads, name, steps, warmup, trials):
+    """Quantise the 7 linears of a layer set, run warmup steps, then time
+    ``trials`` runs of ``steps`` steps each (HIP events around each run,
+    synchronised on both sides), and one more pass of the same steps with
+    event brackets around every GEMM launch for the kernel's roofline."""
+    import torch
+
+    layers, host, ws = setup_layer(api, workloads, name)
+    flops_step = sum(linear_flops(d["M"], d["shape"].K, d["shape"].N, d["r"]) for d in layers)
+    fwd_flops = [2 * d["M"] * d["shape"].K * d["shape"].N + 2 * d["M"] * d["r"] * d["shape"].N for d in layers]
+    dx_flops = [2 * d["M"] * d["shape"].K * d["shape"].N + 2 * d["M"] * d["r"] * d["shape"].K for d in layers]
+    for _ in range(warmup):
+        run_step(api, layers, ws)
+    torch.cuda.synchronize()
+    trial_ms = []
+    wall = []
+    for _ in range(trials):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            run_step(api, layers, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        wall.append((time.perf_counter() - w0) / steps * 1e3)
+        trial_ms.append(e0.elapsed_time(e1) / steps)
+    ms_step = sorted(trial_ms)[len(trial_ms) // 2]
+    value = flops_step / (ms_step * 1e-3) / 1e12
+    log(f"{name}: step {ms_step:.3f} ms (median of {trials} trials of {steps} steps: "
+        f"{', '.join(f'{t:.3f}' for t in trial_ms)}), {value:.1f} TFLOP/s")
+    n_l = len(layers)
+    t_fwd = api.KernelTimer(api.QLORA_TIMING_FWD_GEMM, capacity=n_l * steps)
+    t_dx = api.KernelTimer(api.QLORA_TIMING_DX_GEMM, capacity=n_l * steps)
+    torch.cuda.synchronize()
+    with t_fwd, t_dx:
+        for _ in range(steps):
+            run_step(api, layers, ws)
+    torch.cuda.synchronize()
+    dfwd, ddx = t_fwd.durations_ms(), t_dx.durations_ms()
+    kf = kernel_summary(dfwd, fwd_flops * steps)
+    kd = kernel_summary(ddx, dx_flops * steps)
+    kg = kernel_summary(dfwd + ddx, fwd_flops * steps + dx_flops * steps)
+    log(f"{name}: fwd GEMM {kf['tflops']:.1f} TFLOP/s avg {kf['avg_ms']:.3f} ms; "
+        f"dX GEMM {kd['tflops']:.1f} TFLOP/s avg {kd['avg_ms']:.3f} ms")
+    # gemm_nt_kernel runs both products (one launch each per linear): its
+    # algorithmic flops per launch averaged over the 14 launches of a step,
+    # over its average launch duration.
+    roofline = {"bound": "mfma", "achieved": kg["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": kg["tflops"] / PEAK_BF16_TFLOPS, "traffic": gemm_traffic(name),
+                "kernel": "gemm_nt_kernel", "avg_launch_ms": kg["avg_ms"], "launches": kg["launches"],
+                "flops_per_launch": (sum(fwd_flops) + sum(dx_flops)) / (2 * n_l)}
+    shp_desc = ", ".join(f"{d['shape'].name} {d['shape'].K}->{d['shape'].N}" for d in layers)
+    cfg = workloads.WORKLOADS[name]
+    config = {"workload": f"{name}: 7 linears ({shp_desc}), {layers[0]['M']} tokens, NF4+DQ base "
+                          f"(block 64, DQ block 256, {cfg['w_kind']} weights std {cfg['w_std']}), "
+                          f"LoRA r={layers[0]['r']} s={layers[0]['s']} on all 7, fwd+bwd per step",
+              "tokens": layers[0]["M"], "rank": layers[0]["r"], "lora_scale": layers[0]["s"],
+              "flops_per_step": flops_step}
+    res = {"ms_per_step": ms_step, "value": value, "trials_ms_per_step": trial_ms,
+           "wall_ms_per_step": wall, "roofline": roofline, "kernels": {"fwd_gemm": kf, "dx_gemm": kd},
+           "config": config, "flops_per_step": flops_step}
+    return res, layers, host, ws
+
+
+def bench_quantize_pass(api, workloads, layers=80, pool=2, oracle_layer=True):
+    """The LLaMA-65B-shaped quantisation pass: ``layers`` x 7 tensors (q, k,
+    v, o 8192x8192; gate, up 8192->22016; down 22016->8192) quantised to NF4
+    + DQ from fp32 and from bf16. The inputs are a pool of ``pool`` distinct
+    layers (host-drawn, N(0, 0.015)), cycled so that every layer writes its
+    own output set (codes, absmax8, scale2, mean); the whole pass is timed
+    with HIP events. GB/s = (input + output bytes) / time. The oracle
+    quantises one layer (fp32 input) on the host cores; the pass estimate is
+    that time x 80."""
+    import torch
+
+    shapes = workloads.LLAMA65B
+    res = {"layers": layers, "tensors": layers * len(shapes), "pool_layers": pool}
+    outs = []
+    for _ in range(layers):
+        outs.append([api.NF4Tensor.empty(sh.N, sh.K) for sh in shapes])
+    ws = torch.empty(max(api.qlora_quant_sizes(sh.N, sh.K)["workspace"] for sh in shapes), dtype=torch.uint8,
+                     device="cuda")
+    numel = sum(sh.N * sh.K for sh in shapes) * layers
+    out_bytes = sum(nf4_bytes(sh.K, sh.N) for sh in shapes) * layers
+    res["weights"] = numel
+    res["output_bytes"] = out_bytes
+    pool32 = []
+    for li in range(pool):
+        pool32.append([torch.from_numpy(workloads.quantize_weight(sh, 4, 7 * li + i)).cuda()
+                       for i, sh in enumerate(shapes)])
+        log(f"65B pass: pool layer {li} drawn")
+    for dt in ("f32", "bf16"):
+        src = pool32 if dt == "f32" else [[w.to(torch.bfloat16) for w in lay] for lay in pool32]
+        for i, w in enumerate(src[0]):      # warm-up of every shape
+            api.qlora_quantize(w, out=outs[0][i], workspace=ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for layer in range(layers):
+            for i, w in enumerate(src[layer % pool]):
+                api.qlora_quantize(w, out=outs[layer][i], workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        in_bytes = numel * (4 if dt == "f32" else 2)
+        gbps = (in_bytes + out_bytes) / (ms * 1e-3) / 1e9
+        res[dt] = {"ms": ms, "input_bytes": in_bytes, "GBps": gbps, "frac_of_hbm_peak": gbps / PEAK_HBM_GBPS,
+                   "roofline_ms": (in_bytes + out_bytes) / (PEAK_HBM_GBPS * 1e9) * 1e3}
+        log(f"65B pass from {dt}: {ms:.1f} ms for {layers * len(shapes)} tensors, {gbps:.0f} GB/s")
+        if dt == "bf16":
+            del src
+    del outs, ws
+    if oracle_layer:
+        from oracle import nf4
+
+        host = [workloads.quantize_weight(sh, 4, i) for i, sh in enumerate(shapes)]
+        t0 = time.perf_counter()
+        for w in host:
+            nf4.quantize(w)
+        dt = time.perf_counter() - t0
+        res["cpu_oracle"] = {"seconds_one_layer": dt, "seconds_pass_estimate": dt * layers,
+                             "GBps_estimate": (numel * 4 + out_bytes) / (dt * layers) / 1e9,
+                             "sample": "one layer (7 tensors, 809.5M weights, fp32 input) through the NumPy "
+                                       "oracle, single-threaded; the pass estimate is x80"}
+        log(f"65B pass: oracle one layer {dt:.1f} s (x80 = {dt * layers:.0f} s)")
+    del pool32
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama7b-layer", choices=["llama7b-layer", "llama33b-layer"])
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--trials", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE, choices=["llama7b-layer", "llama33b-layer"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip the GEMV and quantize sections")
+    ap.add_argument("--no-extras", action="store_true", help="only the headline step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (calibration of the HBM byte counters)")
     args = ap.parse_args()
@@ -574,86 +746,43 @@ def main():
         return
     api.library()
     name = args.workload
-    layers, host, ws = setup_layer(api, workloads, name)
-    flops_step = sum(linear_flops(d["M"], d["shape"].K, d["shape"].N, d["r"]) for d in layers)
-    fwd_flops = [2 * d["M"] * d["shape"].K * d["shape"].N + 2 * d["M"] * d["r"] * d["shape"].N for d in layers]
-    dx_flops = [2 * d["M"] * d["shape"].K * d["shape"].N + 2 * d["M"] * d["r"] * d["shape"].K for d in layers]
-
-    for _ in range(args.warmup):
-        run_step(api, layers, ws)
-    torch.cuda.synchronize()
-    # the timed steps, uninstrumented
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
-        run_step(api, layers, ws)
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = e0.elapsed_time(e1) / args.steps
-    value = flops_step / (ms_step * 1e-3) / 1e12
-    log(f"step {ms_step:.3f} ms, {value:.1f} TFLOP/s (wall {wall / args.steps * 1e3:.3f} ms/step)")
-    # the same number of steps again with HIP events around every GEMM launch
-    # (the per-kernel durations of the roofline; the brackets cost some time,
-    # which is why the step itself is timed without them)
-    n_l = len(layers)
-    t_fwd = api.KernelTimer(api.QLORA_TIMING_FWD_GEMM, capacity=n_l * args.steps)
-    t_dx = api.KernelTimer(api.QLORA_TIMING_DX_GEMM, capacity=n_l * args.steps)
-    torch.cuda.synchronize()
-    with t_fwd, t_dx:
-        for _ in range(args.steps):
-            run_step(api, layers, ws)
-    torch.cuda.synchronize()
-
-    dfwd, ddx = t_fwd.durations_ms(), t_dx.durations_ms()
-    kf = kernel_summary(dfwd, fwd_flops * args.steps)
-    kd = kernel_summary(ddx, dx_flops * args.steps)
-    kg = kernel_summary(dfwd + ddx, fwd_flops * args.steps + dx_flops * args.steps)
-    log(f"fwd GEMM {kf['tflops']:.1f} TFLOP/s avg {kf['avg_ms']:.3f} ms; "
-        f"dX GEMM {kd['tflops']:.1f} TFLOP/s avg {kd['avg_ms']:.3f} ms")
-    # gemm_nt_kernel runs both products (one launch each per linear): its
-    # algorithmic flops per launch averaged over the 14 launches of a step,
-    # over its average launch duration.
-    roofline = {"bound": "mfma", "achieved": kg["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": kg["tflops"] / PEAK_BF16_TFLOPS, "traffic": gemm_traffic(),
-                "kernel": "gemm_nt_kernel", "avg_launch_ms": kg["avg_ms"], "launches": kg["launches"],
-                "flops_per_launch": (sum(fwd_flops) + sum(dx_flops)) / (2 * len(layers))}
-
-    shp_desc = ", ".join(f"{d['shape'].name} {d['shape'].K}->{d['shape'].N}" for d in layers)
+    head, layers, host, ws = setup_and_time(api, workloads, name, args.steps, args.warmup, args.trials)
     result = {
         "metric": "QLoRA NF4 linear fwd+bwd TFLOP/s; NF4 GEMV weight GB/s (% of peak)",
-        "value": value,
+        "value": head["value"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{name}: 7 linears ({shp_desc}), {layers[0]['M']} tokens, NF4+DQ base "
-                               f"(block 64, DQ block 256), LoRA r={layers[0]['r']} s={layers[0]['s']} on all 7, "
-                               f"fwd+bwd per step",
-                   "tokens": layers[0]["M"], "rank": layers[0]["r"], "lora_scale": layers[0]["s"],
-                   "flops_per_step": flops_step},
-        "roofline": roofline,
-        "kernels": {"fwd_gemm": kf, "dx_gemm": kd},
+        "config": head["config"],
+        "trials_ms_per_step": head["trials_ms_per_step"],
+        "roofline": head["roofline"],
+        "kernels": head["kernels"],
     }
     if not args.no_extras:
         del ws
         torch.cuda.empty_cache()
-        result["dropout_step"] = bench_dropout_step(api, layers, flops_step, ms_step)
-        del layers
-    else:
-        del layers, ws
+        p_drop = 0.05 if name == "llama33b-layer" else 0.1
+        result["dropout_step"] = bench_dropout_step(api, layers, head["flops_per_step"], head["ms_per_step"],
+                                                    p=p_drop)
+    del layers
     torch.cuda.empty_cache()
     if not args.no_extras:
+        other = "llama7b-layer" if name == "llama33b-layer" else "llama33b-layer"
+        sec, l2, _, ws2 = setup_and_time(api, workloads, other, max(args.steps // 2, 5), 3, 1)
+        del l2, ws2
+        torch.cuda.empty_cache()
+        result[other.replace("-", "_") + "_step"] = {k: sec[k] for k in ("value", "ms_per_step", "roofline",
+                                                                          "kernels", "config")}
         result["gemv"] = bench_gemv(api, workloads)
         result["quantize"] = bench_quantize(api, workloads)
+        result["quantize_65b_pass"] = bench_quantize_pass(api, workloads, oracle_layer=not args.no_cpu_baseline)
         result["qtypes"] = bench_qtypes(api, workloads)
         result["int8"] = bench_int8(api, workloads)
         result["merge"] = bench_merge(api, workloads)

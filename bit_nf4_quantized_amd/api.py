@@ -158,6 +158,30 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(fn):
+    """Run a wrapper with torch's current stream set to its ``stream``
+    argument (when one is given), so that the workspace and the outputs it
+    allocates belong to the stream the library's kernels run on. The caching
+    allocator then hands a freed workspace only to later work on that same
+    stream, which the stream orders after the kernels still using it."""
+    import functools
+    import inspect
+
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        stream = sig.bind_partial(*args, **kwargs).arguments.get("stream")
+        if stream is None:
+            return fn(*args, **kwargs)
+        import torch
+
+        with torch.cuda.stream(stream):
+            return fn(*args, **kwargs)
+
+    return wrapper
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -235,6 +259,7 @@ def _need_mem(t, dtype, shape, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+@_on_stream
 def qlora_clip_grad_norm(g, max_norm: float, coef=None, norm=None, workspace=None, stream=None):
     """coef = min(1, max_norm / (||g|| + 1e-6)) and the norm (float64), as 1-element device tensors."""
     import torch
@@ -250,6 +275,7 @@ def qlora_clip_grad_norm(g, max_norm: float, coef=None, norm=None, workspace=Non
     return coef, norm
 
 
+@_on_stream
 def qlora_adam_step(theta, g, m, v, step: int, lr: float, beta1: float = 0.9, beta2: float = 0.999,
                     eps: float = 1e-8, weight_decay: float = 0.0, coef=None, theta_bf16=None, stream=None):
     """One Adam step in place on flat fp32 theta, m, v (each a device tensor or
@@ -266,6 +292,7 @@ def qlora_adam_step(theta, g, m, v, step: int, lr: float, beta1: float = 0.9, be
                                    _ptr(theta_bf16), _stream(stream)), "qlora_adam_step")
 
 
+@_on_stream
 def qlora_lora_dropout(X, p: float, seed: int, out=None, stream=None):
     """The dropped adapter input Xd of a bf16 device tensor (same shape)."""
     import torch
@@ -380,6 +407,7 @@ def _workspace(nbytes: int, device, ws=None):
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
+@_on_stream
 def qlora_quantize(W, out: NF4Tensor | None = None, workspace=None, stream=None, qtype: str | int = "nf4",
                    double_quant: bool = True) -> NF4Tensor:
     """NF4 + DQ quantisation of a [rows][cols] fp32 or bf16 device tensor (or another
@@ -406,6 +434,7 @@ def qlora_quantize(W, out: NF4Tensor | None = None, workspace=None, stream=None,
     return q
 
 
+@_on_stream
 def qlora_dequantize(q: NF4Tensor, out=None, stream=None):
     """doubleDequant to a bf16 [rows][cols] device tensor."""
     import torch
@@ -417,6 +446,7 @@ def qlora_dequantize(q: NF4Tensor, out=None, stream=None):
     return y
 
 
+@_on_stream
 def qlora_merge_adapters(q: NF4Tensor, L1, L2, scale: float, out=None, stream=None):
     """bf16 [N][K] = dequant(Wt) + s (L1 L2)^T, rounded once to bf16."""
     import torch
@@ -432,6 +462,7 @@ def qlora_merge_adapters(q: NF4Tensor, L1, L2, scale: float, out=None, stream=No
     return y
 
 
+@_on_stream
 def qlora_int8_quantize(X, block: int = 64, codes=None, absmax=None, stream=None):
     """Blockwise Int8 absmax codes of a contiguous fp32 or bf16 device tensor
     (flattened); returns (codes int8 [numel], absmax float32 [ceil(numel/block)])."""
@@ -455,6 +486,7 @@ def qlora_int8_quantize(X, block: int = 64, codes=None, absmax=None, stream=None
     return codes, absmax
 
 
+@_on_stream
 def qlora_int8_dequantize(codes, absmax, block: int = 64, dtype=None, out=None, stream=None):
     """x' = code * RN32(absmax / 127) as a flat float32 (default) or bfloat16 device tensor."""
     import torch
@@ -473,6 +505,7 @@ def qlora_int8_dequantize(codes, absmax, block: int = 64, dtype=None, out=None, 
     return y
 
 
+@_on_stream
 def qlora_linear_fwd(q: NF4Tensor, X, L1, L2, scale: float, want_T: bool = False, Y=None, T_out=None,
                      workspace=None, stream=None, dropout=None):
     """Y = X dequant(Wt)^T + s (X L1) L2; returns (Y, T) with T = bf16(X L1) or None.
@@ -509,6 +542,7 @@ def qlora_linear_fwd(q: NF4Tensor, X, L1, L2, scale: float, want_T: bool = False
     return Y, T_out
 
 
+@_on_stream
 def qlora_linear_bwd(q: NF4Tensor, X, dY, L1, L2, scale: float, T=None, need_dX: bool = True,
                      grad_dtype=None, dX=None, dL1=None, dL2=None, workspace=None, stream=None, dropout=None):
     """Returns (dX or None, dL1, dL2) of the QLoRA linear for upstream gradient dY

@@ -585,6 +585,22 @@ static hipError_t lora_down(const uint16_t* X, int64_t M, int64_t K, const uint1
   return reduce(part, sp.Z, M, r, s, sT, true, ldst, 1.0f, T_out, stream);
 }
 
+SmallForwardScratch small_forward_scratch(int64_t M, int64_t K, int r) {
+  SmallForwardScratch S;
+  S.st_off = 0;
+  S.part_off = align_up((size_t)M * r * 2, 256);
+  S.total = S.part_off + align_up(small_t_partial_bytes(M, K, r), 256);
+  return S;
+}
+
+hipError_t linear_forward_small(const NF4View& W, const NF4Table& tab, const uint16_t* X, const uint16_t* Xa,
+                                int64_t M, const uint16_t* L1, const uint16_t* L2, int r, float s, uint16_t* Y,
+                                uint16_t* T_out, uint16_t* sT, float* part, hipStream_t stream) {
+  hipError_t e = launch_small_lora_down(Xa, M, W.cols, L1, r, s, sT, r, T_out, part, stream);
+  if (e != hipSuccess) return e;
+  return timed(kTimeGemv, stream, [&] { return launch_gemv(W, tab, X, M, sT, L2, r, Y, stream); });
+}
+
 hipError_t linear_forward(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M,
                           const uint16_t* L1, const uint16_t* L2, int r, float s, uint16_t* Y,
                           uint16_t* T_out, void* ws, hipStream_t stream, const DropoutParams* dr) {
@@ -610,11 +626,7 @@ hipError_t linear_forward(const NF4View& W, const NF4Table& tab, const uint16_t*
   float* part = reinterpret_cast<float*>(base + L.part_off);
 
   uint16_t* l1t = reinterpret_cast<uint16_t*>(base + L.l1t_off);
-  if (M <= 16) {
-    hipError_t e = launch_small_lora_down(Xa, M, K, L1, r, s, sT, r, T_out, part, stream);
-    if (e != hipSuccess) return e;
-    return timed(kTimeGemv, stream, [&] { return launch_gemv(W, tab, X, M, sT, L2, r, Y, stream); });
-  }
+  if (M <= 16) return linear_forward_small(W, tab, X, Xa, M, L1, L2, r, s, Y, T_out, sT, part, stream);
 
   if (M <= kMidMaxM && midm_fits(M, K, N)) {   // batched decode: one pass over the 4-bit weight
     hipError_t e = launch_small_lora_down(Xa, M, K, L1, r, s, sT, rp, T_out, part, stream);

@@ -195,6 +195,19 @@ hipError_t launch_dropout_input(const uint16_t* X, int64_t numel, const DropoutP
 hipError_t launch_masked_lora(const uint16_t* sU, int64_t ldsu, const uint16_t* L1, int r, int64_t M, int64_t K,
                               const DropoutParams& d, const float* F, float* D, uint16_t* dX, hipStream_t stream);
 
+// Decode-path forward (M <= 16): bf16(s Xa L1) into sT ([M][r]) from the
+// K-slice partials in part, then the dequant-GEMV with the LoRA term. Xa is
+// the adapter branch's input (X, or its dropped copy).
+hipError_t linear_forward_small(const NF4View& W, const NF4Table& tab, const uint16_t* X, const uint16_t* Xa,
+                                int64_t M, const uint16_t* L1, const uint16_t* L2, int r, float s, uint16_t* Y,
+                                uint16_t* T_out, uint16_t* sT, float* part, hipStream_t stream);
+
+// Scratch of linear_forward_small packed back to back: sT, then the partials.
+struct SmallForwardScratch {
+  size_t st_off, part_off, total;
+};
+SmallForwardScratch small_forward_scratch(int64_t M, int64_t K, int r);
+
 // With dr, the adapter branch reads the dropped input (regenerated from
 // dr's seed in both passes) and the workspace is linear_workspace_layout(...,
 // true).

@@ -84,10 +84,23 @@ def draw_weight(rng: np.random.Generator, N: int, K: int, kind: str, std: float)
             flat[pos] *= np.float32(10.0)
         return w
     if kind == "student-t4":
-        # Student-t with 4 degrees of freedom has variance 2; scale to std
-        t = rng.standard_t(4, size=(N, K))
-        return (std / np.sqrt(2.0) * t).astype(np.float32)
+        return (std / np.sqrt(2.0) * student_t4(rng, (N, K))).astype(np.float32)
     raise ValueError(kind)
+
+
+def student_t4(rng: np.random.Generator, shape) -> np.ndarray:
+    """Student-t draws with 4 degrees of freedom (variance 2), float64.
+
+    t = Z / sqrt(C / 4) with Z ~ N(0, 1) and C ~ chi-square(4); C is the
+    sum of two independent Exp(1) draws times 2, so t = Z sqrt(2 / (E1 + E2)).
+    This is the textbook construction of the t distribution, drawn here from
+    three fast float32 streams (Z, E1, E2 in that order) instead of numpy's
+    gamma-based standard_t.
+    """
+    z = rng.standard_normal(shape, dtype=np.float32).astype(np.float64)
+    e1 = rng.standard_exponential(shape, dtype=np.float32).astype(np.float64)
+    e2 = rng.standard_exponential(shape, dtype=np.float32).astype(np.float64)
+    return z * np.sqrt(2.0 / (e1 + e2))
 
 
 @dataclass
@@ -156,5 +169,5 @@ def random_weight(rng: np.random.Generator, numel: int, kind: str = "normal", st
     if kind == "normal":
         return (std * rng.standard_normal(numel, dtype=np.float32)).astype(np.float32)
     if kind == "student-t4":
-        return (std / np.sqrt(2.0) * rng.standard_t(4, size=numel)).astype(np.float32)
+        return (std / np.sqrt(2.0) * student_t4(rng, numel)).astype(np.float32)
     raise ValueError(kind)

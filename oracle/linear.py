@@ -26,7 +26,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .nf4 import bf16_bits_to_f32
+from .nf4 import bf16_bits_to_f32, bf16_rne
 
 _F64 = np.float64
 
@@ -77,6 +77,15 @@ def linear_bwd_dx_rows(Wt, L1, L2, s: float, dY, rows):
     dY = widen(np.asarray(dY)[rows])
     Wt, L1, L2 = widen(Wt), widen(L1), widen(L2)
     return dY @ Wt + float(s) * ((dY @ L2.T) @ L1.T)
+
+
+def bf16_floor(R) -> float:
+    """The error that rounding the exact result to bf16 alone leaves:
+    max |bf16_RNE(R) - R| / RMS(R) (R rounded to fp32 first, then to bf16).
+    A bf16 output cannot score below this on the agreement metric."""
+    R = np.asarray(R, dtype=_F64)
+    rb = widen(bf16_rne(R.astype(np.float32)))
+    return rel_err(rb, R)
 
 
 def rel_err(G, R) -> float:

@@ -234,3 +234,40 @@ def test_bf16_gradients(api):
     torch.cuda.synchronize()
     assert linear.rel_err(api.to_host_bits(dL1), ref["dL1"]) <= TOL
     assert linear.rel_err(api.to_host_bits(dL2), ref["dL2"]) <= TOL
+
+
+@pytest.mark.parametrize("M", [8, 96, 384])
+def test_side_stream_with_allocation_churn(api, M):
+    """Calls on a non-default stream, with allocations churning on the
+    default stream meanwhile, give the same bits as calls on the default
+    stream: the binding's workspaces and outputs belong to the call's stream,
+    so the caching allocator never hands them to other work while the
+    library's kernels still use them."""
+    import torch
+
+    say(f"side stream + allocation churn M={M}")
+    inp = case(M, 1024, 768, 64, 0.25, 300 + M)
+    q, _ = gpu_quantize(api, inp.W)
+    X, L1, L2, dY = dev(api, inp.X), dev(api, inp.L1), dev(api, inp.L2), dev(api, inp.dY)
+    Y0, T0 = api.qlora_linear_fwd(q, X, L1, L2, inp.s, want_T=True)
+    dX0, a0, b0 = api.qlora_linear_bwd(q, X, dY, L1, L2, inp.s, T=T0)
+    torch.cuda.synchronize()
+    ref = [api.to_host_bits(Y0), api.to_host_bits(dX0), a0.cpu().numpy(), b0.cpu().numpy()]
+    side = torch.cuda.Stream()          # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(4):
+        Y, T = api.qlora_linear_fwd(q, X, L1, L2, inp.s, want_T=True, stream=side)
+        dX, a, b = api.qlora_linear_bwd(q, X, dY, L1, L2, inp.s, T=T, stream=side)
+        outs.append((Y, dX, a, b))
+        for _ in range(8):              # churn on the default stream
+            junk = torch.full((M * 1024 + 4096,), 7.0, device="cuda")
+            junk.mul_(3.0)
+            del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    for Y, dX, a, b in outs:
+        np.testing.assert_array_equal(api.to_host_bits(Y), ref[0])
+        np.testing.assert_array_equal(api.to_host_bits(dX), ref[1])
+        np.testing.assert_array_equal(a.cpu().numpy(), ref[2])
+        np.testing.assert_array_equal(b.cpu().numpy(), ref[3])

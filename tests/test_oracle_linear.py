@@ -136,3 +136,31 @@ def test_rel_err_metric():
     assert linear.rel_err(G, R) == pytest.approx(0.1 / np.sqrt(12.5))
     bf = nf4.bf16_rne(np.array([1.0 + 2 ** -7 + 2 ** -9], np.float32))
     assert linear.rel_err(bf, np.array([1.0 + 2 ** -7 + 2 ** -9])) > 0
+
+
+@pytest.mark.parametrize("seed", [3, 4])
+def test_row_helpers_match_python_loops(seed):
+    """The sampled-row helpers give exactly the selected rows of Y and dX,
+    checked against the pure-Python loops (a dropped LoRA term, a transposed
+    operand or a row mix-up in either helper fails here)."""
+    rng = np.random.default_rng(seed)
+    X, Wt, L1, L2, dY = tiny(rng, M=7, K=6, N=5, r=3)
+    s = 0.5
+    w = [linear.widen(a).tolist() for a in (X, Wt, L1, L2, dY)]
+    rows = np.array([0, 3, 6])
+    lY = loops_fwd(*w[:4], s)
+    lX, _, _ = loops_bwd(*w[:4], s, w[4])
+    np.testing.assert_allclose(linear.linear_fwd_rows(X, Wt, L1, L2, s, rows), lY[rows], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(linear.linear_bwd_dx_rows(Wt, L1, L2, s, dY, rows), lX[rows], rtol=1e-12, atol=1e-14)
+    # and they agree with the full-tensor functions row for row
+    Y, _ = linear.linear_fwd(X, Wt, L1, L2, s)
+    dX, _, _ = linear.linear_bwd(X, Wt, L1, L2, s, dY)
+    np.testing.assert_allclose(linear.linear_fwd_rows(X, Wt, L1, L2, s, rows), Y[rows], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(linear.linear_bwd_dx_rows(Wt, L1, L2, s, dY, rows), dX[rows], rtol=1e-14, atol=1e-15)
+
+
+def test_bf16_floor():
+    """The output-rounding floor: max |bf16_RNE(R) - R| / RMS(R)."""
+    R = np.array([1.0, -1.0, 1.0 + 2 ** -9])       # RMS ~ 1; the third value rounds by 2^-9
+    assert linear.bf16_floor(R) == pytest.approx(2 ** -9 / np.sqrt(np.mean(R * R)))
+    assert linear.bf16_floor(np.array([0.5, 0.25])) == 0.0
