@@ -88,6 +88,30 @@ def bf16_floor(R) -> float:
     return rel_err(rb, R)
 
 
+def bf16_half_ulp(R) -> np.ndarray:
+    """Half the spacing of bf16 values in the binade of |R| (8 significand
+    bits: values in [2^e, 2^(e+1)) are 2^(e-7) apart), elementwise; below
+    the normal range the subnormal spacing 2^-133."""
+    a = np.abs(np.asarray(R, dtype=_F64))
+    _, e = np.frexp(a)                  # a = f 2^e with f in [0.5, 1): binade exponent e - 1
+    e = np.maximum(e - 1, -126)
+    return np.where(a > 0, np.ldexp(1.0, e - 8), np.ldexp(1.0, -134))
+
+
+def rel_err_beyond_bf16(G, R) -> float:
+    """The agreement metric for a bf16 output with its own output rounding
+    taken out: max over elements of max(0, |G - R| - half a bf16 ulp at R),
+    over RMS(R). A correctly rounded bf16 result scores 0; anything the
+    computation adds beyond the final rounding (operand or accumulation
+    error, a wrong term) counts in full."""
+    G = widen(G)
+    R = np.asarray(R, dtype=_F64)
+    rms = float(np.sqrt(np.mean(R * R))) if R.size else 0.0
+    ex = np.maximum(np.abs(G - R) - bf16_half_ulp(R), 0.0)
+    top = float(np.max(ex)) if ex.size else 0.0
+    return top / rms if rms > 0 else top
+
+
 def rel_err(G, R) -> float:
     """max |G - R| / RMS(R), G widened to float64; R the oracle result."""
     G = widen(G)

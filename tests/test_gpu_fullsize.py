@@ -6,10 +6,13 @@ at M in {1, 4, 16}.
 
 Every output is compared whole against the float64 oracle (oracle.linear on
 the oracle's own quantise + dequantise of the same weight): Y, dX, dL1 and
-dL2, max |err| / RMS <= 2e-2. Beside each error the test prints the bf16
-floor, the error that rounding the exact result to bf16 alone leaves; on
-the 33B shapes the floor sits close to the bar, so the GPU path must add
-no rounding beyond the final one. The quantised weight itself is checked
+dL2 within 2e-2 of RMS (bf16 outputs: beyond their own bf16 rounding; see
+gpu_util.check_output). Beside each error the test prints the bf16 floor,
+the error that rounding the exact result to bf16 alone leaves: with the
+heavy-tailed weights of these sets (0.1 % outliers x10, Student-t) the
+largest outputs reach binades where that floor alone is 0.021 (LLaMA-7B q,
+dX) and 0.034 (LLaMA-33B k, Y), so the GPU path must add no rounding beyond
+the final one. The quantised weight itself is checked
 bit-exactly against the oracle's (codes, absmax8, scale2, mean).
 """
 
@@ -18,7 +21,7 @@ import pytest
 
 from bit_nf4_quantized_amd import workloads
 from oracle import linear, nf4
-from gpu_util import assert_quant_equal, gpu_quantize, require_gpu, say
+from gpu_util import assert_quant_equal, check_output, gpu_quantize, require_gpu, say
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -30,9 +33,7 @@ def api():
 
 
 def report(label, k, G, R):
-    err = linear.rel_err(G, R)
-    say(f"  {label} {k}: err {err:.5f} (bf16 floor {linear.bf16_floor(R):.5f})")
-    assert err <= TOL, (label, k, err)
+    check_output(label, k, G, R)
 
 
 LAYERS = [(name, i) for name in ("llama7b-layer", "llama33b-layer") for i in range(7)]

@@ -164,3 +164,26 @@ def test_bf16_floor():
     R = np.array([1.0, -1.0, 1.0 + 2 ** -9])       # RMS ~ 1; the third value rounds by 2^-9
     assert linear.bf16_floor(R) == pytest.approx(2 ** -9 / np.sqrt(np.mean(R * R)))
     assert linear.bf16_floor(np.array([0.5, 0.25])) == 0.0
+
+
+def test_error_beyond_bf16_rounding():
+    """A correctly rounded bf16 output scores 0, even where half an ulp is
+    far above 2 % of the RMS; one ulp off at the largest element scores half
+    an ulp; an error added before the rounding counts in full."""
+    rng = np.random.default_rng(11)
+    R = rng.standard_normal(4096) * 1.3
+    R[7] = 9.71875                                 # a bf16 midpoint in [8, 16): half an ulp (2^-5) away
+    rounded = nf4.bf16_rne(R.astype(np.float32))
+    assert linear.rel_err_beyond_bf16(rounded, R) == 0.0
+    assert linear.rel_err(rounded, R) > 0.015     # the plain metric sees the rounding
+    rms = np.sqrt(np.mean(R * R))
+    off = rounded.copy()
+    off[7] = off[7] + 1                            # next bf16 above: 9.75 -> 9.8125 (RNE picked 9.75)
+    got = linear.rel_err_beyond_bf16(off, R)
+    expect = (abs(linear.widen(off)[7] - R[7]) - 2.0 ** -5) / rms
+    assert got == pytest.approx(expect, rel=1e-12) and got > 0
+    shifted = nf4.bf16_rne((R + 0.05 * rms).astype(np.float32))   # a bias before rounding
+    assert linear.rel_err_beyond_bf16(shifted, R) > 0.03
+    # half ulps: 1.0 -> 2^-8, 9.7 -> 2^-5, 0.3 -> 2^-10, 2^-130 (subnormal) -> 2^-134
+    np.testing.assert_array_equal(linear.bf16_half_ulp(np.array([1.0, -9.7, 0.3, 2.0 ** -130])),
+                                  [2.0 ** -8, 2.0 ** -5, 2.0 ** -10, 2.0 ** -134])
