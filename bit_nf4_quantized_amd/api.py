@@ -38,7 +38,9 @@ EXPORTS = (
     "qlora_linear_bwd", "qlora_set_timing", "qlora_int8_quantize", "qlora_int8_dequantize",
     "qlora_merge_adapters", "qlora_linear_workspace_dropout", "qlora_linear_fwd_dropout",
     "qlora_linear_bwd_dropout", "qlora_lora_dropout", "qlora_clip_grad_norm", "qlora_adam_step",
+    "qlora_linear_fwd_noalloc",
 )
+QLORA_NOALLOC_SCRATCH_BYTES = (2 << 20) + (64 << 10)
 QLORA_CLIP_WORKSPACE_BYTES = 8192
 
 
@@ -114,6 +116,8 @@ def _load():
     lib.qlora_linear_bwd.argtypes = [P(QNF4), vp, vp, i64, vp, vp, ctypes.c_int, ctypes.c_float, vp, vp, vp, vp,
                                      ctypes.c_int, vp, sz, vp]
     lib.qlora_linear_bwd.restype = ctypes.c_int
+    lib.qlora_linear_fwd_noalloc.argtypes = [P(QNF4), vp, i64, vp, vp, ctypes.c_int, ctypes.c_float, vp, vp, vp]
+    lib.qlora_linear_fwd_noalloc.restype = ctypes.c_int
     lib.qlora_set_timing.argtypes = [ctypes.c_int, vp, vp, ctypes.c_int, P(ctypes.c_int)]
     lib.qlora_set_timing.restype = ctypes.c_int
     u64 = ctypes.c_uint64
@@ -539,6 +543,29 @@ def qlora_linear_fwd(q: NF4Tensor, X, L1, L2, scale: float, want_T: bool = False
                                                 float(p), int(seed), _ptr(Y), _ptr(T_out), _ptr(ws),
                                                 ws.numel() * ws.element_size(), _stream(stream)),
                "qlora_linear_fwd_dropout")
+    return Y, T_out
+
+
+def qlora_linear_fwd_noalloc(q: NF4Tensor, X, L1, L2, scale: float, Y, T_out=None, stream=None):
+    """Y = X dequant(Wt)^T + s (X L1) L2 for M <= 16 into the caller's Y (and
+    T_out), with the library's own scratch: nothing is allocated here or in
+    the library."""
+    import torch
+
+    M, K = X.shape
+    N = q.rows
+    r = L1.shape[1]
+    if K != q.cols:
+        raise ValueError("X columns must equal the weight's in_features")
+    _need(X, torch.bfloat16, (M, K), "X")
+    _need(L1, torch.bfloat16, (K, r), "L1")
+    _need(L2, torch.bfloat16, (r, N), "L2")
+    _need(Y, torch.bfloat16, (M, N), "Y")
+    if T_out is not None:
+        _need(T_out, torch.bfloat16, (M, r), "T_out")
+    st = q.struct()
+    _check(_load().qlora_linear_fwd_noalloc(ctypes.byref(st), _ptr(X), M, _ptr(L1), _ptr(L2), r, float(scale),
+                                            _ptr(Y), _ptr(T_out), _stream(stream)), "qlora_linear_fwd_noalloc")
     return Y, T_out
 
 

@@ -348,9 +348,67 @@ void* device_view(const void* p) {
   return nullptr;
 }
 
+// ---- the allocation-free decode forward ----------------------------------------
+//
+// Scratch of qlora_linear_fwd_noalloc: one array per device, in the module's
+// device memory (zero-initialised when the code object loads; held until the
+// process ends). Host code never passes the array's name to a kernel: the
+// name is a host-side stand-in. The device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// that address is what the kernels receive. Calls that overlap on one device
+// share the array and race.
+__device__ __align__(256) unsigned char scratch[QLORA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device).
+int device_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return QLORA_ERR_ARG;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!p) return hip_fail(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QLORA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int qlora_linear_fwd_noalloc(const qlora_nf4* W, const uint16_t* X, int64_t M, const uint16_t* L1,
+                             const uint16_t* L2, int r, float scale, uint16_t* Y, uint16_t* T_out,
+                             hipStream_t stream) {
+  int st = check_linear(W, M, r, scale);
+  if (st != QLORA_OK) return st;
+  if (M > 16) return QLORA_ERR_SHAPE;
+  if (!L1 || !L2) return QLORA_ERR_ARG;
+  if (M > 0 && (!X || !Y)) return QLORA_ERR_ARG;
+  if (!aligned16(X) || !aligned16(L1) || !aligned16(L2) || !aligned16(Y) || !aligned16(T_out))
+    return QLORA_ERR_ALIGN;
+  const qlora::SmallForwardScratch S = qlora::small_forward_scratch(M, W->cols, r);
+  if (S.total > QLORA_NOALLOC_SCRATCH_BYTES) return QLORA_ERR_WORKSPACE;
+  if (M == 0) return QLORA_OK;
+  void* base = nullptr;
+  st = device_scratch(&base);
+  if (st != QLORA_OK) return st;
+  (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
+  char* p = static_cast<char*>(base);
+  const hipError_t e = qlora::linear_forward_small(
+      view_of(W), tables(W->qtype).tab, X, X, M, L1, L2, r, scale, Y, T_out, reinterpret_cast<uint16_t*>(p + S.st_off),
+      reinterpret_cast<float*>(p + S.part_off), stream);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
 
 int qlora_linear_fwd(const qlora_nf4* W, const uint16_t* X, int64_t M, const uint16_t* L1, const uint16_t* L2,
                      int r, float scale, uint16_t* Y, uint16_t* T_out, void* ws, size_t ws_bytes,

@@ -26,7 +26,9 @@
  *   - bf16 tensors are passed as uint16_t bit patterns.
  *   - Ownership: the caller allocates and frees every buffer, including
  *     workspaces sized by the query functions. The library allocates no
- *     memory and keeps no mutable state; all calls are reentrant.
+ *     memory and keeps no mutable state, and calls are reentrant, with one
+ *     exception: qlora_linear_fwd_noalloc uses a library-held device array
+ *     per device (see there).
  *   - Asynchrony: work is enqueued on `stream` and the call returns without
  *     synchronising. Errors found on the host (arguments, shapes,
  *     alignment, workspace size) are returned before anything is enqueued.
@@ -241,6 +243,27 @@ int qlora_linear_workspace(int64_t M, int64_t K, int64_t N, int r, size_t *bytes
 int qlora_linear_fwd(const qlora_nf4 *W, const uint16_t *X, int64_t M, const uint16_t *L1,
                      const uint16_t *L2, int r, float scale, uint16_t *Y, uint16_t *T_out,
                      void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * qlora_linear_fwd_noalloc: qlora_linear_fwd for M <= 16 (the decode path)
+ * without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation. It allocates nothing; its scratch (bf16(s X L1) and the
+ * fp32 K-slice partials of X L1) lives in a library-held device array of
+ * QLORA_NOALLOC_SCRATCH_BYTES per device, held until the process ends. The
+ * caller passes inputs and outputs as for qlora_linear_fwd and gets the same
+ * bits: the same kernels run.
+ *   Errors as for qlora_linear_fwd, plus QLORA_ERR_SHAPE for M > 16 and
+ *   QLORA_ERR_WORKSPACE when the scratch the shape needs,
+ *   2 M r + 4 M r ceil(K / 512) bytes (each part rounded up to 256), exceeds
+ *   the array (with M = 16 and r = 256 that allows K up to 67072).
+ *   Calls on one device share the array: calls that overlap on one device
+ *   (other streams, other threads) race and must be serialised by the caller.
+ */
+#define QLORA_NOALLOC_SCRATCH_BYTES ((size_t)(2u << 20) + (size_t)(64u << 10))
+int qlora_linear_fwd_noalloc(const qlora_nf4 *W, const uint16_t *X, int64_t M, const uint16_t *L1,
+                             const uint16_t *L2, int r, float scale, uint16_t *Y, uint16_t *T_out,
+                             hipStream_t stream);
 
 /*
  * qlora_linear_bwd: gradients of the layer for the upstream gradient dY

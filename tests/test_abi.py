@@ -38,7 +38,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     assert sorted(api.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -214,6 +214,26 @@ def test_linear_validation(lib):
     assert b(ctypes.byref(W), X, dY, 64, L1, L2, 8, 2.0, None, p(0x27000004), g1, g2, 0, ws, big,
              None) == api.QLORA_ERR_ALIGN
     assert b(ctypes.byref(W), X, dY, 64, L1, L2, 8, 2.0, None, dX, g1, g2, 0, ws, 100, None) == api.QLORA_ERR_WORKSPACE
+
+
+def test_noalloc_validation(lib):
+    """qlora_linear_fwd_noalloc refuses on the host: bad arguments, M > 16,
+    and shapes whose scratch exceeds the library-held array."""
+    W = fake_nf4(512, 512)
+    p = lambda a: ctypes.c_void_p(a)
+    X, L1, L2, Y = p(0x21000000), p(0x22000000), p(0x23000000), p(0x24000000)
+    f = lib.qlora_linear_fwd_noalloc
+    assert f(None, X, 4, L1, L2, 8, 2.0, Y, None, None) == api.QLORA_ERR_ARG
+    assert f(ctypes.byref(W), X, 4, L1, L2, 12, 2.0, Y, None, None) == api.QLORA_ERR_ARG
+    assert f(ctypes.byref(W), X, 17, L1, L2, 8, 2.0, Y, None, None) == api.QLORA_ERR_SHAPE
+    assert f(ctypes.byref(W), X, 4, None, L2, 8, 2.0, Y, None, None) == api.QLORA_ERR_ARG
+    assert f(ctypes.byref(W), X, 4, L1, L2, 8, 2.0, p(0x24000002), None, None) == api.QLORA_ERR_ALIGN
+    # M = 16, r = 256: 8 KB of bf16(s X L1) plus 16 KB of partials per 512 k
+    fits = fake_nf4(256, 131 * 512)           # 131 slices: 8 KB + 131 x 16 KB fit in 2 MiB + 64 KiB
+    too_big = fake_nf4(256, 131 * 512 + 64)   # 132 slices do not
+    assert f(ctypes.byref(too_big), X, 16, L1, L2, 256, 2.0, Y, None, None) == api.QLORA_ERR_WORKSPACE
+    assert f(ctypes.byref(fits), X, 17, L1, L2, 256, 2.0, Y, None, None) == api.QLORA_ERR_SHAPE
+    assert api.QLORA_NOALLOC_SCRATCH_BYTES == (2 << 20) + (64 << 10)
 
 
 def test_dropout_validation(lib):
