@@ -302,6 +302,7 @@ int linear_fwd_impl(const qlora_nf4* W, const uint16_t* X, int64_t M, const uint
   if (!ws) return QLORA_ERR_WORKSPACE;
   if (!aligned16(X) || !aligned16(L1) || !aligned16(L2) || !aligned16(Y) || !aligned16(T_out) || !aligned16(ws))
     return QLORA_ERR_ALIGN;
+  if (!qlora::linear_forward_supported(M, W->cols, W->rows, r)) return QLORA_ERR_SHAPE;
   if (ws_bytes < qlora::linear_workspace_layout(M, W->cols, W->rows, r, dr != nullptr).total)
     return QLORA_ERR_WORKSPACE;
   (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call

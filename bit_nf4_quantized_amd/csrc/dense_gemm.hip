@@ -37,17 +37,19 @@
 //     than the 8-row swizzle c ^ (r & 7));
 //   * one workgroup runs per CU. When the tile count would leave at least
 //     half of the CUs idle in the last round, the tile-columns holding that
-//     remainder run as (TM/2) x TN tiles, dispatched after the full tiles so
-//     that they share the last round (at 8192 x 11008: 1280 full tiles and
-//     192 half tiles instead of 1376 full tiles in 5.4 rounds; the step is
-//     about 0.8 % faster);
+//     remainder run as quarter-height (64 x 256) tiles if those fit in one
+//     round, else as half-height (128 x 256) tiles, dispatched after the full
+//     tiles so that they share the last round (8192 x 6656: 768 full tiles
+//     and 256 quarter tiles instead of 832 full tiles in 3.25 rounds;
+//     8192 x 11008: 1280 full tiles and 192 half tiles instead of 1376 full
+//     tiles in 5.4 rounds);
 //   * workgroups are numbered so that the 8 XCDs (each with its own L2) get
 //     contiguous blocks of tiles, ordered in groups of 4 tile-rows so that
 //     concurrently running tiles share A rows and B columns (measured: 4
 //     and 6 tile-rows about 0.5 % faster per training step than 2, 8 or 16).
-// Rows beyond M or N are read clamped (finite data) and never stored. Every
-// operand must be readable for K (or K2) columns and hold less than 4 GB, so
-// that per-lane offsets fit in 32 bits (the launcher splits larger M).
+// Rows beyond M or N are read clamped (finite data) and never stored. Per-lane
+// offsets are 32-bit: B (and B2) must be smaller than 2 GB, and the launcher
+// runs the rows of A in chunks of at most 2 GB, one launch per chunk.
 #include "common.h"
 #include "launch.h"
 
@@ -70,8 +72,9 @@ constexpr int RPI = 8;           // rows per wave load instruction (64 lanes x 1
 constexpr int kStageElems = TM * TK;  // LDS elements per operand per stage (TM == TN)
 
 // The tail of a launch whose tile count leaves the last round of workgroups
-// mostly empty runs as half-height tiles (TM / 2 rows): wave sub-tiles of
-// WTM / 2 rows, so the last round takes about half a tile's time.
+// mostly empty runs as half- or quarter-height tiles (TM / 2 or TM / 4
+// rows, wave sub-tiles of 64 or 32 rows), so that the last round holds more,
+// shorter tiles.
 template <int TMX>
 struct TileShape {
   static constexpr int kWtm = TMX / (kWaves / WGN);  // wave sub-tile rows
@@ -92,7 +95,8 @@ struct DenseArgs {
   int64_t K2;       // slab reduction, multiple of TK (0 = no slab)
   float alpha;
   int tiles_m, tiles_n;
-  int full_n;       // tile-columns [0, full_n) run as TM x TN tiles, the rest as (TM/2) x TN
+  int full_n;       // tile-columns [0, full_n) run as TM x TN tiles, the rest as (TM/tail_split) x TN
+  int tail_split;   // 2 or 4
   const float* E;   // ADD: fp32 addend [M][N] (row stride lde), C = bf16(alpha acc + E)
   int64_t lde;
 };
@@ -207,14 +211,22 @@ __device__ __forceinline__ void gemm_tile(const DenseArgs& p, int64_t m0, int64_
   // (measured 0.1-0.3 % faster)
   auto order = [&]() {
     constexpr int nr = MI + NJ, nm = MI * NJ;
-    static_assert(nm >= nr, "at least one MFMA per fragment read");
-    constexpr int per = nm / nr, left = nm - nr * per;
+    if constexpr (nm >= nr) {
+      constexpr int per = nm / nr, left = nm - nr * per;
 #pragma unroll
-    for (int q = 0; q < nr; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // one DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, per, 0);  // MFMAs
+      for (int q = 0; q < nr; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // one DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, per, 0);  // MFMAs
+      }
+      if constexpr (left > 0) __builtin_amdgcn_sched_group_barrier(0x008, left, 0);
+    } else {  // quarter tiles: fewer MFMAs than reads per k-step
+#pragma unroll
+      for (int q = 0; q < nm; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, nr - nm, 0);
     }
-    if constexpr (left > 0) __builtin_amdgcn_sched_group_barrier(0x008, left, 0);
   };
   // One stage; on entry the fragments of its k-step 0 are in set 0 and the
   // next stage's copy was started one stage earlier.
@@ -289,20 +301,22 @@ __device__ __forceinline__ void gemm_tile(const DenseArgs& p, int64_t m0, int64_
   }
 
   // Epilogue through LDS (the stage buffers are free now): each wave writes
-  // half of its 128 x 64 sub-tile (64 rows) as bf16 into its own padded LDS
-  // slice, then stores it to C in 16-byte row chunks. In a 32x32 accumulator,
-  // register v of lane l is row (v%4) + 4(l/32) + 8(v/4), column l%32.
+  // up to two 32-row blocks of its sub-tile (64 rows) as bf16 into its own
+  // padded LDS slice, then stores them to C in 16-byte row chunks. In a
+  // 32x32 accumulator, register v of lane l is row (v%4) + 4(l/32) +
+  // 8(v/4), column l%32.
   constexpr int kEpiStride = WTN + 8;  // padded row (elements)
   constexpr int CPRO = WTN / 8;        // 16-byte chunks per sub-tile row
   constexpr int RPIT = 64 / CPRO;      // rows stored per iteration
+  constexpr int RB = MI < 2 ? MI : 2;  // 32-row blocks staged per pass
   __syncthreads();
   uint16_t* ep = smem + wave * (64 * kEpiStride);
   const int64_t row_base = m0 + wm * WTM, col_base = n0 + wn * WTN;
 #pragma unroll
-  for (int h = 0; h < MI / 2; ++h) {
+  for (int h = 0; h < MI / RB; ++h) {
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii) {
-      const int i = 2 * h + ii;
+    for (int ii = 0; ii < RB; ++ii) {
+      const int i = RB * h + ii;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
 #pragma unroll
@@ -315,11 +329,11 @@ __device__ __forceinline__ void gemm_tile(const DenseArgs& p, int64_t m0, int64_
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done (wave-private slice)
 #pragma unroll
-    for (int it = 0; it < 64 / RPIT; ++it) {
+    for (int it = 0; it < 32 * RB / RPIT; ++it) {
       const int r = it * RPIT + lane / CPRO;
       const int ch = lane % CPRO;
       const u32x4_t val = *reinterpret_cast<const u32x4_t*>(ep + r * kEpiStride + ch * 8);
-      const int64_t row = row_base + h * 64 + r;
+      const int64_t row = row_base + h * 32 * RB + r;
       const int64_t col = col_base + ch * 8;
       if (row < p.M && col < p.N) *reinterpret_cast<u32x4_t*>(p.C + row * p.ldc + col) = val;
     }
@@ -347,13 +361,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(DenseArgs p) {
     const int tn = tl / gm;
     gemm_tile<ADD, TM>(p, (int64_t)tm * TM, (int64_t)tn * TN, smem);
   } else {
-    // the tail tile-columns, as half-height tiles; dispatched last, they
-    // fill the last round of workgroups
+    // the tail tile-columns, as half- or quarter-height tiles; dispatched
+    // last, they fill the last round of workgroups
     const int h = bid - nfull;
     const int ncols = p.tiles_n - p.full_n;
-    const int64_t m0 = (int64_t)(h / ncols) * (TM / 2);
-    if (m0 >= p.M) return;  // the lower half of a last tile-row beyond M (uniform per workgroup)
-    gemm_tile<ADD, TM / 2>(p, m0, (int64_t)(p.full_n + h % ncols) * TN, smem);
+    const int64_t m0 = (int64_t)(h / ncols) * (TM / p.tail_split);
+    if (m0 >= p.M) return;  // a piece of a last tile-row beyond M (uniform per workgroup)
+    const int64_t n0 = (int64_t)(p.full_n + h % ncols) * TN;
+    if (p.tail_split == 4)
+      gemm_tile<ADD, TM / 4>(p, m0, n0, smem);
+    else
+      gemm_tile<ADD, TM / 2>(p, m0, n0, smem);
   }
 }
 
@@ -449,10 +467,13 @@ hipError_t launch_dequant_cols(const NF4View& W, const NF4Table& tab, uint16_t* 
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
-                          int64_t M, int64_t N, int64_t K, const uint16_t* A2, const uint16_t* B2, int64_t ld2,
-                          int64_t K2, uint16_t* C, int64_t ldc, float alpha, hipStream_t stream, const float* E,
-                          int64_t lde) {
+namespace {
+
+// One launch over all M rows (row offsets of A and A2 below 4 GB).
+hipError_t launch_gemm_nt_rows(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M, int64_t N,
+                               int64_t K, const uint16_t* A2, const uint16_t* B2, int64_t ld2, int64_t K2,
+                               uint16_t* C, int64_t ldc, float alpha, hipStream_t stream, const float* E,
+                               int64_t lde) {
   DenseArgs p;
   p.A = A; p.B = B; p.A2 = A2; p.B2 = B2; p.C = C;
   p.lda = lda; p.ldb = ldb; p.ld2 = ld2; p.ldc = ldc;
@@ -462,22 +483,52 @@ hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int
   p.E = E; p.lde = lde;
   // One workgroup per CU at a time. When the last round of tiles would
   // leave at least half of the CUs idle, the last tile-columns that hold
-  // those tiles run as half-height tiles, all in that round.
+  // those tiles run as quarter-height tiles if those fit in one round, else
+  // as half-height tiles, all in that round.
   const int cus = device_cu_count();
   const int tiles = p.tiles_m * p.tiles_n;
   const int tail = tiles % cus;
   int tail_cols = 0;
+  p.tail_split = 2;
   if (tail > 0) {
     const int tc = (tail + p.tiles_m - 1) / p.tiles_m;
-    if (tc <= p.tiles_n && 2 * tc * p.tiles_m <= cus) tail_cols = tc;
+    if (tc <= p.tiles_n && 4 * tc * p.tiles_m <= cus) {
+      tail_cols = tc;
+      p.tail_split = 4;
+    } else if (tc <= p.tiles_n && 2 * tc * p.tiles_m <= cus) {
+      tail_cols = tc;
+    }
   }
   p.full_n = p.tiles_n - tail_cols;
-  const int ntiles = p.tiles_m * p.full_n + 2 * p.tiles_m * tail_cols;
+  const int ntiles = p.tiles_m * p.full_n + p.tail_split * p.tiles_m * tail_cols;
   if (E)
     hipLaunchKernelGGL(gemm_nt_kernel<true>, dim3((unsigned)ntiles), dim3(kThreads), 0, stream, p);
   else
     hipLaunchKernelGGL(gemm_nt_kernel<false>, dim3((unsigned)ntiles), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                          int64_t M, int64_t N, int64_t K, const uint16_t* A2, const uint16_t* B2, int64_t ld2,
+                          int64_t K2, uint16_t* C, int64_t ldc, float alpha, hipStream_t stream, const float* E,
+                          int64_t lde) {
+  // per-lane offsets are 32-bit: B and B2 must fit, and the rows of A (A2)
+  // are taken in chunks of at most 2 GB, one launch each
+  const int64_t two_gb = (int64_t)1 << 31;
+  if (N * ldb * 2 >= two_gb || N * ld2 * 2 >= two_gb) return hipErrorInvalidValue;
+  const int64_t widest = lda > ld2 ? lda : ld2;
+  int64_t chunk = (two_gb - 1) / (widest * 2);
+  chunk = chunk / TM * TM;
+  if (chunk < TM) return hipErrorInvalidValue;
+  for (int64_t r0 = 0; r0 < M; r0 += chunk) {
+    const int64_t rows = M - r0 < chunk ? M - r0 : chunk;
+    hipError_t e = launch_gemm_nt_rows(A + r0 * lda, lda, B, ldb, rows, N, K, A2 ? A2 + r0 * ld2 : nullptr, B2, ld2,
+                                       K2, C + r0 * ldc, ldc, alpha, stream, E ? E + r0 * lde : nullptr, lde);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace qlora

@@ -14,8 +14,6 @@
 //            A_COL  A stored as [k][m] (m contiguous), transposed while staging
 //   B modes: B_ROW  B[n][k], k contiguous
 //            B_COL  B stored as [k][n], transposed while staging
-//            B_NF4  B[n][k] = dequant(Wt)[n][k]: 32 codes per thread (16
-//                   bytes) -> bf16(RN32(q[code] * a')) written to LDS
 //            B_NF4T B[k][n] = dequant(Wt)[n][k] (the dX product reduces over
 //                   the weight's rows): each thread dequantises an 8-row x
 //                   4-column patch and writes it transposed
@@ -36,7 +34,7 @@ namespace qlora {
 namespace {
 
 enum { A_ROW = 0, A_COL = 1 };
-enum { B_ROW = 0, B_COL = 1, B_NF4 = 2, B_NF4T = 3 };
+enum { B_ROW = 0, B_COL = 1, B_NF4T = 3 };
 enum { EPI_BF16 = 0, EPI_F32 = 1 };
 
 constexpr int BM = 128, BN = 128, BK = 64;
@@ -50,7 +48,7 @@ struct GemmArgs {
   int64_t lda;
   const uint16_t* B;
   int64_t ldb;
-  NF4View W;         // B_NF4 / B_NF4T
+  NF4View W;         // B_NF4T
   const uint16_t* A2;  // slab: A2[m][j], j < r, row stride r
   const uint16_t* B2;  // slab: B2[n][j], j < r, row stride r
   int r;
@@ -129,46 +127,6 @@ __device__ __forceinline__ void store_col(uint16_t* __restrict__ S, const RowReg
 
 // ---- NF4 weight staging -------------------------------------------------------
 
-struct NF4Regs {
-  u32x4_t codes;   // B_NF4: 32 codes of one row
-  float ap;
-};
-
-// B_NF4: rows n in [n0, n0+128), k in [k0, k0+64): one 64-block per row.
-__device__ __forceinline__ void load_nf4(const NF4View& W, float mu, int64_t n0, int64_t k0, NF4Regs& R) {
-  const int tid = threadIdx.x;
-  const int row = tid >> 1, half = tid & 1;
-  const int64_t gn = n0 + row;
-  const int64_t kw = W.cols;
-  if (gn < W.rows) {
-    R.codes = *reinterpret_cast<const u32x4_t*>(W.codes + gn * (kw >> 1) + (k0 >> 1) + half * 16);
-    const int64_t blk = gn * (kw / kBlock) + k0 / kBlock;
-    R.ap = block_const(W, blk, mu);
-  } else {
-    R.codes = u32x4_t{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
-    R.ap = 0.0f;
-  }
-}
-
-__device__ __forceinline__ void store_nf4(uint16_t* __restrict__ S, const float* __restrict__ sq,
-                                          const NF4Regs& R) {
-  const int tid = threadIdx.x;
-  const int row = tid >> 1, half = tid & 1;
-  const uint32_t words[4] = {R.codes.x, R.codes.y, R.codes.z, R.codes.w};
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const uint32_t w = words[c];
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float lo = sq[(w >> (8 * i)) & 15u] * R.ap;
-      const float hi = sq[(w >> (8 * i + 4)) & 15u] * R.ap;
-      o[i] = pack_bf16x2(lo, hi);
-    }
-    *reinterpret_cast<u32x4_t*>(S + swz(row, half * 4 + c)) = u32x4_t{o[0], o[1], o[2], o[3]};
-  }
-}
-
 struct NF4TRegs {
   uint32_t code16[8];  // 4 codes (2 bytes) of each of 8 weight rows
   float ap[8];
@@ -233,13 +191,12 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
   const int nsteps = nmain + nslab;
 
   float mu = 0.0f;
-  if constexpr (BMODE == B_NF4 || BMODE == B_NF4T) {
+  if constexpr (BMODE == B_NF4T) {
     if (tid < 16) sQ[tid] = p.tab.q[tid];
     mu = tensor_mean(p.W);
   }
 
   RowRegs ra, rb;
-  NF4Regs rq;
   NF4TRegs rt;
 
   auto load_step = [&](int st) {
@@ -249,7 +206,6 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
       else load_col(p.A, p.lda, m0, p.M, k0, kz1, ra);
       if constexpr (BMODE == B_ROW) load_row(p.B, p.ldb, n0, p.N, k0, kz1, rb);
       else if constexpr (BMODE == B_COL) load_col(p.B, p.ldb, n0, p.N, k0, kz1, rb);
-      else if constexpr (BMODE == B_NF4) load_nf4(p.W, mu, n0, k0, rq);
       else load_nf4t(p.W, mu, n0, k0, rt);
     } else {
       const int64_t j0 = (int64_t)(st - nmain) * BK;
@@ -263,7 +219,6 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs p) {
       else store_col(sA[buf], ra);
       if constexpr (BMODE == B_ROW) store_row(sB[buf], rb);
       else if constexpr (BMODE == B_COL) store_col(sB[buf], rb);
-      else if constexpr (BMODE == B_NF4) store_nf4(sB[buf], sQ, rq);
       else store_nf4t(sB[buf], sQ, rt);
     } else {
       store_row(sA[buf], ra);
@@ -634,8 +589,11 @@ hipError_t linear_forward(const NF4View& W, const NF4Table& tab, const uint16_t*
     return timed(kTimeMidGemm, stream, [&] { return launch_midm(W, tab, X, M, sT, L2, r, (int)rp, part, Y, stream); });
   }
 
-  const bool dense = fits_dense({M * K * 2, N * K * 2, M * rp * 2, N * rp * 2});
-  const int64_t ldst = dense ? rp : r;
+  // the dequantised weight and L2^T are addressed with 32-bit offsets (the
+  // token dimension is cut into chunks inside launch_gemm_nt); larger
+  // weights are refused by the C ABI before anything is enqueued
+  if (!fits_dense({N * K * 2, N * rp * 2})) return hipErrorInvalidValue;
+  const int64_t ldst = rp;
   // L2^T for the GEMM's slab stage, and with the skinny T kernel also L1^T,
   // in one launch
   const bool skinny_t = skinny_ok(r, M, K);
@@ -654,21 +612,18 @@ hipError_t linear_forward(const NF4View& W, const NF4Table& tab, const uint16_t*
   e = lora_down(Xa, M, K, L1, r, s, sT, ldst, T_out, part, l1t, stream, drop_in_t ? dr : nullptr, skinny_t);
   if (e != hipSuccess) return e;
 
-  if (dense) {
-    uint16_t* wd = reinterpret_cast<uint16_t*>(base + L.wd_off);
-    e = launch_dequant_rows(W, tab, wd, stream);
-    if (e != hipSuccess) return e;
-    return timed(kTimeFwdGemm, stream, [&] {
-      return launch_gemm_nt(X, K, wd, K, M, N, K, sT, l2t, rp, rp, Y, N, 1.0f, stream);
-    });
-  }
-  GemmArgs a = base_args();
-  a.M = M; a.N = N; a.K = K; a.k_split = K;
-  a.A = X; a.lda = K;
-  a.W = W; a.tab = tab;
-  a.A2 = sT; a.B2 = l2t; a.r = r;
-  a.C = Y; a.ldc = N;
-  return timed(kTimeFwdGemm, stream, [&] { return run_gemm<A_ROW, B_NF4, EPI_BF16, true>(a, 1, stream); });
+  uint16_t* wd = reinterpret_cast<uint16_t*>(base + L.wd_off);
+  e = launch_dequant_rows(W, tab, wd, stream);
+  if (e != hipSuccess) return e;
+  return timed(kTimeFwdGemm, stream, [&] {
+    return launch_gemm_nt(X, K, wd, K, M, N, K, sT, l2t, rp, rp, Y, N, 1.0f, stream);
+  });
+}
+
+bool linear_forward_supported(int64_t M, int64_t K, int64_t N, int r) {
+  if (M <= 16 || (M <= kMidMaxM && midm_fits(M, K, N))) return true;
+  const int64_t rp = cdiv(r, 64) * 64;
+  return fits_dense({N * K * 2, N * rp * 2});
 }
 
 hipError_t linear_backward(const NF4View& W, const NF4Table& tab, const uint16_t* X, const uint16_t* dY,
@@ -695,7 +650,7 @@ hipError_t linear_backward(const NF4View& W, const NF4Table& tab, const uint16_t
     return hipGetLastError();
   }
 
-  const bool dense = dX && M > 16 && (N % 64) == 0 && fits_dense({M * N * 2, K * N * 2, M * rp * 2, K * rp * 2});
+  const bool dense = dX && M > 16 && (N % 64) == 0 && fits_dense({K * N * 2, K * rp * 2});
   const int64_t ldsu = dense ? rp : r;
   // the adapter branch's input: X, or its dropped copy (the same mask as the
   // forward). When T comes from the forward and both adapter gradients take

@@ -211,6 +211,10 @@ SmallForwardScratch small_forward_scratch(int64_t M, int64_t K, int r);
 // With dr, the adapter branch reads the dropped input (regenerated from
 // dr's seed in both passes) and the workspace is linear_workspace_layout(...,
 // true).
+// Whether linear_forward takes these sizes: the large-M path needs the bf16
+// dequantised weight (and L2^T) below 2 GB.
+bool linear_forward_supported(int64_t M, int64_t K, int64_t N, int r);
+
 hipError_t linear_forward(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M,
                           const uint16_t* L1, const uint16_t* L2, int r, float s, uint16_t* Y,
                           uint16_t* T_out, void* ws, hipStream_t stream, const DropoutParams* dr = nullptr);

@@ -238,7 +238,10 @@ int qlora_linear_workspace(int64_t M, int64_t K, int64_t N, int r, size_t *bytes
  * Shapes: M >= 0; K a positive multiple of 64; N a positive multiple of 8;
  * r a multiple of 8 in [8, 256]. M <= 16 takes the bandwidth-bound GEMV
  * kernel, 16 < M <= 128 a one-pass fused dequant-GEMM over K-slices with a
- * fixed-order reduction, larger M the MFMA GEMM; all return the same layer.
+ * fixed-order reduction, larger M the MFMA GEMM on the dequantised weight
+ * (written to the workspace); all return the same layer. The MFMA path
+ * needs that bf16 weight below 2 GB (N K < 2^30), else QLORA_ERR_SHAPE; it
+ * takes any M (the token rows run in chunks of at most 2 GB).
  */
 int qlora_linear_fwd(const qlora_nf4 *W, const uint16_t *X, int64_t M, const uint16_t *L1,
                      const uint16_t *L2, int r, float scale, uint16_t *Y, uint16_t *T_out,

@@ -206,6 +206,11 @@ def test_linear_validation(lib):
     assert f(ctypes.byref(W), p(0x21000008), 64, L1, L2, 8, 2.0, Y, None, ws, big, None) == api.QLORA_ERR_ALIGN
     assert f(ctypes.byref(W), X, 64, L1, L2, 8, 2.0, Y, None, ws, 64, None) == api.QLORA_ERR_WORKSPACE
     assert f(ctypes.byref(W), X, 64, L1, L2, 8, 2.0, Y, None, None, big, None) == api.QLORA_ERR_WORKSPACE
+    # the large-M forward needs the bf16 dequantised weight below 2 GB; the
+    # decode path (M <= 16) does not materialise it
+    huge = fake_nf4(32768, 32768)
+    assert f(ctypes.byref(huge), X, 4096, L1, L2, 8, 2.0, Y, None, ws, big, None) == api.QLORA_ERR_SHAPE
+    assert f(ctypes.byref(huge), X, 8, L1, L2, 8, 2.0, Y, None, ws, 64, None) == api.QLORA_ERR_WORKSPACE
     b = lib.qlora_linear_bwd
     dY, dX, g1, g2 = p(0x26000000), p(0x27000000), p(0x28000000), p(0x29000000)
     assert b(ctypes.byref(W), X, dY, 64, L1, L2, 8, 2.0, None, dX, g1, g2, 5, ws, big, None) == api.QLORA_ERR_ARG

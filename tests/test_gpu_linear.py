@@ -79,6 +79,9 @@ def test_tiny_512(api):
     # more 256x256 tiles than CUs (17 x 17 = 289): 255 full tiles, then the last
     # two tile-columns as 128-row half tiles, with ragged M and N inside them
     (4100, 512, 4160, 16, 0.5, "normal"),
+    # 4 x 66 tiles: the last 2 tile-columns as 64-row quarter tiles (ragged M
+    # and N inside them); dX: 4 x 2 tiles, no tail split
+    (1000, 512, 66 * 256 - 8, 16, 0.5, "normal"),
 ])
 def test_shapes(api, M, K, N, r, s, kind):
     say(f"linear M={M} K={K} N={N} r={r} s={s} {kind}")
@@ -267,3 +270,40 @@ def test_side_stream_with_allocation_churn(api, M):
         np.testing.assert_array_equal(api.to_host_bits(dX), ref[1])
         np.testing.assert_array_equal(a.cpu().numpy(), ref[2])
         np.testing.assert_array_equal(b.cpu().numpy(), ref[3])
+
+
+def test_token_rows_beyond_2gb(api):
+    """M = 131072 tokens of K = 8192: X and dX hold 2 GiB each, so the dense
+    GEMMs run the token rows in two launches (130816 + 256 rows) and the
+    adapter products take the generic path. Rows on both sides of the chunk
+    boundary are compared with the oracle; dL1 and dL2 are sums over all
+    rows, accumulated over row chunks through oracle.linear.linear_bwd."""
+    import torch
+
+    M, K, N, r, s = 131072, 8192, 256, 8, 0.5
+    say(f"linear with 2 GiB activations: M={M} K={K} N={N} r={r}")
+    rng = np.random.default_rng(77)
+    inp = workloads.draw_linear(rng, workloads.LinearShape("t", K, N), 8, r, s, "normal", 0.02, True)
+    X = workloads.to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    dY = workloads.to_bf16_bits(rng.standard_normal((M, N), dtype=np.float32))
+    q, _ = gpu_quantize(api, inp.W)
+    Xd, L1, L2, dYd = dev(api, X), dev(api, inp.L1), dev(api, inp.L2), dev(api, dY)
+    Y, T = api.qlora_linear_fwd(q, Xd, L1, L2, s, want_T=True)
+    dX, dL1, dL2 = api.qlora_linear_bwd(q, Xd, dYd, L1, L2, s, T=T)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 130815, 130816, 130817, 131071])
+    Yr = api.to_host_bits(Y[rows.tolist()])
+    dXr = api.to_host_bits(dX[rows.tolist()])
+    dL1g, dL2g = dL1.cpu().numpy(), dL2.cpu().numpy()
+    del Y, T, dX, dL1, dL2, Xd, dYd
+    Wd = nf4.dequantize(nf4.quantize(inp.W), inp.W.shape)
+    check_output("2 GiB", "Y rows", Yr, linear.linear_fwd_rows(X, Wd, inp.L1, inp.L2, s, rows))
+    check_output("2 GiB", "dX rows", dXr, linear.linear_bwd_dx_rows(Wd, inp.L1, inp.L2, s, dY, rows))
+    g1 = np.zeros((K, r))
+    g2 = np.zeros((r, N))
+    for c in range(0, M, 8192):
+        _, a, b = linear.linear_bwd(X[c:c + 8192], Wd, inp.L1, inp.L2, s, dY[c:c + 8192])
+        g1 += a
+        g2 += b
+    check_output("2 GiB", "dL1", dL1g, g1)
+    check_output("2 GiB", "dL2", dL2g, g2)
