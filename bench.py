@@ -236,13 +236,37 @@ def bench_gemv(api, workloads, reps=4):
             kbytes = wbytes + 2 * M * K + 2 * M * r + 2 * r * N + 2 * M * N   # kernel's own stream
             cbytes = wbytes + 2 * r * (K + N) + 2 * M * K + 2 * M * N          # whole call
             call_ms = e0.elapsed_time(e1) / n
+            # The same calls replayed from a captured HIP graph: the GPU time of
+            # a whole call without the host's per-call cost (which bounds the
+            # eager loop above). The replayed result must equal the eager one.
+            api.qlora_linear_fwd(qs[copies - 1], X, L1, L2, inp.s, Y=Y, workspace=ws)
+            torch.cuda.synchronize()
+            y_eager = Y.clone()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(copies):
+                    api.qlora_linear_fwd(qs[i], X, L1, L2, inp.s, Y=Y, workspace=ws)
+            graph.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            graph_ms = e0.elapsed_time(e1) / (reps * copies)
+            same = bool(torch.equal(Y.view(torch.int16), y_eager.view(torch.int16)))
+            del graph
             out.append({"K": K, "N": N, "M": M, "kernel_us": avg * 1e3,
                         "kernel_GBps": kbytes / (avg * 1e-3) / 1e9,
                         "kernel_frac_of_hbm_peak": kbytes / (avg * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                         "call_us": call_ms * 1e3, "call_GBps": cbytes / (call_ms * 1e-3) / 1e9,
-                        "weight_copies": copies})
+                        "graph_call_us": graph_ms * 1e3, "graph_call_GBps": cbytes / (graph_ms * 1e-3) / 1e9,
+                        "graph_call_frac_of_hbm_peak": cbytes / (graph_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                        "graph_result_equal": same, "weight_copies": copies})
             log(f"gemv K={K} N={N} M={M}: kernel {avg*1e3:.2f} us "
-                f"{out[-1]['kernel_GBps']:.0f} GB/s, call {call_ms*1e3:.2f} us")
+                f"{out[-1]['kernel_GBps']:.0f} GB/s, call {call_ms*1e3:.2f} us, "
+                f"graph-replayed call {graph_ms*1e3:.2f} us ({out[-1]['graph_call_GBps']:.0f} GB/s, "
+                f"{'same bits' if same else 'DIFFERENT bits'})")
         del qs
         torch.cuda.empty_cache()
     return out

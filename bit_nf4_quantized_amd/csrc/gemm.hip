@@ -473,6 +473,7 @@ LinearWorkspace linear_workspace_layout(int64_t M, int64_t K, int64_t N, int r, 
   L.l2p_off = off; off += align_up((size_t)64 * N * 2, 256);
   if (r <= 64) upd(skinny_partial_bytes(M, K, N));
   if (M <= kMidMaxM) upd(small_t_partial_bytes(M, K, r));
+  if (M == 1) upd(gemv1_partial_bytes(K, r));
   upd(midm_partial_bytes(M, K, N));
   L.part_off = off; L.part_bytes = align_up(part, 256); off += L.part_bytes;
   // dense path: the dequantised weight (forward [N][K], backward [K][np])
@@ -544,13 +545,15 @@ SmallForwardScratch small_forward_scratch(int64_t M, int64_t K, int r) {
   SmallForwardScratch S;
   S.st_off = 0;
   S.part_off = align_up((size_t)M * r * 2, 256);
-  S.total = S.part_off + align_up(small_t_partial_bytes(M, K, r), 256);
+  const size_t pb = small_t_partial_bytes(M, K, r), p1 = gemv1_partial_bytes(K, r);
+  S.total = S.part_off + align_up(pb > p1 ? pb : p1, 256);
   return S;
 }
 
 hipError_t linear_forward_small(const NF4View& W, const NF4Table& tab, const uint16_t* X, const uint16_t* Xa,
                                 int64_t M, const uint16_t* L1, const uint16_t* L2, int r, float s, uint16_t* Y,
                                 uint16_t* T_out, uint16_t* sT, float* part, hipStream_t stream) {
+  if (Xa == X && gemv1_applies(W, M, r)) return launch_gemv1(W, tab, X, L1, L2, r, s, Y, T_out, part, stream);
   hipError_t e = launch_small_lora_down(Xa, M, W.cols, L1, r, s, sT, r, T_out, part, stream);
   if (e != hipSuccess) return e;
   return timed(kTimeGemv, stream, [&] { return launch_gemv(W, tab, X, M, sT, L2, r, Y, stream); });

@@ -195,6 +195,16 @@ hipError_t launch_dropout_input(const uint16_t* X, int64_t numel, const DropoutP
 hipError_t launch_masked_lora(const uint16_t* sU, int64_t ldsu, const uint16_t* L1, int r, int64_t M, int64_t K,
                               const DropoutParams& d, const float* F, float* D, uint16_t* dX, hipStream_t stream);
 
+// Single-token forward (gemv1.hip): one launch for the LoRA partials over
+// K-slices (fp32 [K/256][r] in part), then the streaming dequant-GEMV that
+// reduces them and adds the LoRA term. gemv1_applies says whether the shape
+// takes this path (M == 1, r <= 64, K a multiple of 256 up to 16384).
+bool gemv1_applies(const NF4View& W, int64_t M, int r);
+size_t gemv1_partial_bytes(int64_t K, int r);
+hipError_t launch_gemv1(const NF4View& W, const NF4Table& tab, const uint16_t* X, const uint16_t* L1,
+                        const uint16_t* L2, int r, float s, uint16_t* Y, uint16_t* T_out, float* part,
+                        hipStream_t stream);
+
 // Decode-path forward (M <= 16): bf16(s Xa L1) into sT ([M][r]) from the
 // K-slice partials in part, then the dequant-GEMV with the LoRA term. Xa is
 // the adapter branch's input (X, or its dropped copy).
