@@ -38,7 +38,7 @@ EXPORTS = (
     "qlora_linear_bwd", "qlora_set_timing", "qlora_int8_quantize", "qlora_int8_dequantize",
     "qlora_merge_adapters", "qlora_linear_workspace_dropout", "qlora_linear_fwd_dropout",
     "qlora_linear_bwd_dropout", "qlora_lora_dropout", "qlora_clip_grad_norm", "qlora_adam_step",
-    "qlora_linear_fwd_noalloc",
+    "qlora_linear_fwd_noalloc", "qlora_check_conversions",
 )
 QLORA_NOALLOC_SCRATCH_BYTES = (2 << 20) + (64 << 10)
 QLORA_CLIP_WORKSPACE_BYTES = 8192
@@ -140,6 +140,8 @@ def _load():
     lib.qlora_int8_quantize.argtypes = [vp, ctypes.c_int, i64, ctypes.c_int, vp, vp, vp]
     lib.qlora_int8_quantize.restype = ctypes.c_int
     lib.qlora_int8_dequantize.argtypes = [vp, vp, i64, ctypes.c_int, vp, ctypes.c_int, vp]
+    lib.qlora_check_conversions.argtypes = [ctypes.c_uint32, i64, vp, vp, vp, vp]
+    lib.qlora_check_conversions.restype = ctypes.c_int
     lib.qlora_int8_dequantize.restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -307,6 +309,23 @@ def qlora_lora_dropout(X, p: float, seed: int, out=None, stream=None):
     _check(_load().qlora_lora_dropout(_ptr(X), X.numel(), float(p), int(seed), _ptr(y), _stream(stream)),
            "qlora_lora_dropout")
     return y
+
+
+@_on_stream
+def qlora_check_conversions(first: int, count: int, bf16=True, e4m3=True, table=False, stream=None):
+    """The device conversions on the fp32 bit patterns first .. first + count - 1.
+
+    Returns (bf16 bits as a device int16 tensor or None, E4M3 codes as a
+    device uint8 tensor or None, the 256 decoded E4M3 codes as a device
+    float32 tensor or None)."""
+    import torch
+
+    bf = torch.empty(count, dtype=torch.int16, device="cuda") if bf16 else None
+    e8 = torch.empty(count, dtype=torch.uint8, device="cuda") if e4m3 else None
+    tb = torch.empty(256, dtype=torch.float32, device="cuda") if table else None
+    _check(_load().qlora_check_conversions(int(first) & 0xFFFFFFFF, int(count), _ptr(bf), _ptr(e8), _ptr(tb),
+                                           _stream(stream)), "qlora_check_conversions")
+    return bf, e8, tb
 
 
 class KernelTimer:

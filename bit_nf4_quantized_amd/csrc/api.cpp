@@ -498,6 +498,14 @@ int qlora_lora_dropout(const uint16_t* X, int64_t numel, float p, uint64_t seed,
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 
+int qlora_check_conversions(uint32_t first, int64_t count, uint16_t* bf16_out, uint8_t* e4m3_out,
+                            float* e4m3_table, hipStream_t stream) {
+  if (count < 0 || count > ((int64_t)1 << 32)) return QLORA_ERR_SHAPE;
+  (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
+  const hipError_t e = qlora::launch_convcheck(first, count, bf16_out, e4m3_out, e4m3_table, stream);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
+
 int qlora_set_timing(int kernel, hipEvent_t* start, hipEvent_t* stop, int n, int* count) {
   if (kernel < 0 || kernel >= QLORA_TIMING_CLASSES || n < 0) return QLORA_ERR_ARG;
   qlora::TimingSlot& t = qlora::timing_slots()[kernel];

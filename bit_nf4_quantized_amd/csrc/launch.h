@@ -205,6 +205,11 @@ hipError_t launch_gemv1(const NF4View& W, const NF4Table& tab, const uint16_t* X
                         const uint16_t* L2, int r, float s, uint16_t* Y, uint16_t* T_out, float* part,
                         hipStream_t stream);
 
+// The device conversions applied to fp32 bit patterns first .. first +
+// count - 1 (convcheck.hip); any output may be null.
+hipError_t launch_convcheck(uint32_t first, int64_t count, uint16_t* bf, uint8_t* e8, float* table,
+                            hipStream_t stream);
+
 // Decode-path forward (M <= 16): bf16(s Xa L1) into sT ([M][r]) from the
 // K-slice partials in part, then the dequant-GEMV with the LoRA term. Xa is
 // the adapter branch's input (X, or its dropped copy).

@@ -2,9 +2,9 @@
 //
 //   M[n][k] = bf16( Wd[n][k] + s * sum_j L1[k][j] L2[j][n] )
 //
-// with Wd the doubleDequant bf16 weight (QLoRA pages: neura.market "QLoRA",
-// the pitfalls list, merge into the dequantised 16-bit base rather than the
-// 4-bit one; diycv.top "QLoRA 论文解读", section 关键公式 for the dequant).
+// with Wd the doubleDequant bf16 weight (QLoRA pages: robocikowo.com "QLoRA",
+// the list of common mistakes, entry on merging: merge into the dequantised
+// 16-bit base rather than the 4-bit one; diycv.top "QLoRA 论文解读", section 关键公式 for the dequant).
 // Per element: Wd = bf16(RN32(q[code] * a')), t = RN32(s * D) with D the
 // fp32-accumulated rank-r product, result bf16_RNE(RN32(Wd + t)).
 //

@@ -370,9 +370,9 @@ int qlora_adam_step(float *theta, const float *g, float *m, float *v, int64_t n,
 
 /*
  * qlora_merge_adapters: the trained adapters merged into the bf16
- * dequantised base, for inference without the adapter branch (neura.market
- * "QLoRA", pitfalls list: merge into the 16-bit dequantised base, never back
- * into the 4-bit one; diycv.top, section 关键公式 for the dequant):
+ * dequantised base, for inference without the adapter branch (robocikowo.com
+ * "QLoRA", the list of common mistakes, entry on merging: merge into the
+ * 16-bit dequantised base, never back into the 4-bit one; diycv.top, section 关键公式 for the dequant):
  *   out[n][k] = bf16_RNE(RN32(Wd[n][k] + RN32(s * D[k][n]))),
  *   Wd = bf16(RN32(q[code] * a')) as in qlora_dequantize,
  *   D  = L1 L2 with bf16 operands and fp32 accumulation,
@@ -416,6 +416,28 @@ enum {
   QLORA_TIMING_CLASSES = 6
 };
 int qlora_set_timing(int kernel, hipEvent_t *start, hipEvent_t *stop, int n, int *count);
+
+/*
+ * qlora_check_conversions: verification entry point (it computes nothing of
+ * the method). Runs the device number conversions that every kernel uses
+ * on the fp32 bit patterns first, first + 1, ..., first + count - 1 (mod
+ * 2^32), so that the formats the pages fix (first-level constants in an
+ * 8-bit float, products in bf16: diycv.top, section 关键公式, the dtype
+ * table) can be checked against their definitions over every pattern:
+ *   bf16_out[i]  bf16 bits of the pattern rounded to nearest, ties to even,
+ *                by the packed-pair conversion the kernels use (both halves
+ *                of the pair must agree; 0xFFFF marks a pair that did not)
+ *   e4m3_out[i]  E4M3 (E4M3FN) code: nearest value, ties to the even code,
+ *                saturating at +-448, sign bit = the input's sign bit
+ *   e4m3_table   optional device f32[256]: the decoded value of each code
+ *                (the NaN codes 0x7F and 0xFF give unspecified values).
+ * bf16_out (device uint16_t[count]) and e4m3_out (device uint8_t[count])
+ * may each be NULL. Non-finite patterns, and finite ones that round beyond
+ * the largest bf16, give unspecified results (the library never converts
+ * them). count in [0, 2^32]. Returns QLORA_ERR_SHAPE for count out of range.
+ */
+int qlora_check_conversions(uint32_t first, int64_t count, uint16_t *bf16_out, uint8_t *e4m3_out,
+                            float *e4m3_table, hipStream_t stream);
 
 #ifdef __cplusplus
 }

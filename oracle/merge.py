@@ -3,7 +3,8 @@
 The pages warn that folding the trained adapters back into the 4-bit base
 (W + B A re-quantised) loses the adapters' precision, and that the merge
 belongs in the dequantised 16-bit base, or the adapters stay separate
-(neura.market "QLoRA", the pitfalls list; diycv.top "QLoRA 论文解读",
+(robocikowo.com "QLoRA", the list of common mistakes, the entry on merging
+the adapters; diycv.top "QLoRA 论文解读",
 section 训练与推理流程, inference keeps the 4-bit base and the adapters).
 In this layout (base stored as Wt[N][K], Y = X Wt^T + s (X L1) L2) the
 merged weight is

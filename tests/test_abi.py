@@ -38,7 +38,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     assert sorted(api.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -331,3 +331,8 @@ def test_set_timing_validation(lib):
     assert lib.qlora_set_timing(5, None, None, 0, None) == api.QLORA_OK
     assert lib.qlora_set_timing(0, None, None, -2, ctypes.byref(cnt)) == api.QLORA_ERR_ARG
     assert lib.qlora_set_timing(0, None, None, 0, None) == api.QLORA_OK       # clearing is always fine
+
+
+def test_check_conversions_rejects_bad_count(lib):
+    assert lib.qlora_check_conversions(0, -1, None, None, None, None) == api.QLORA_ERR_SHAPE
+    assert lib.qlora_check_conversions(0, (1 << 32) + 1, None, None, None, None) == api.QLORA_ERR_SHAPE

@@ -5,7 +5,8 @@ bf16 weights are unique under the method's steps, so the HIP results must
 equal the oracle's bit for bit: on the 512x512 workload, on ragged sizes
 (short last block and short last DQ group), on bf16 inputs, on special
 tensors (all zero, a single block, constructed ties) and on full LLaMA-7B,
--33B and -65B weight shapes.
+-33B and -65B weight shapes (the 22016-wide 65B MLP weights from fp32 and
+from bf16 included).
 """
 
 import numpy as np
@@ -110,3 +111,14 @@ def test_llama65b_shape_bf16(api):
     W = workloads.quantize_weight(shp, 4, 0)
     check_roundtrip(api, W)
     check_roundtrip(api, workloads.to_bf16_bits(W), bf16=True)
+
+
+@pytest.mark.parametrize("index", [4, 6], ids=["gate-22016x8192", "down-8192x22016"])
+@pytest.mark.parametrize("bf16", [False, True], ids=["fp32", "bf16"])
+def test_llama65b_22016_wide(api, index, bf16):
+    """The 22016-wide LLaMA-65B MLP weights (the tensors the 65B quantise
+    pass spends most of its bytes on), whole, from fp32 and from bf16."""
+    shp = workloads.LLAMA65B[index]
+    say(f"quantize llama65b {shp.name} {shp.N}x{shp.K} ({'bf16' if bf16 else 'fp32'})")
+    W = workloads.quantize_weight(shp, 4, index)
+    check_roundtrip(api, workloads.to_bf16_bits(W) if bf16 else W, bf16=bf16)
