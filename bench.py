@@ -16,15 +16,19 @@ value = algorithmic fwd+bwd flops per step / time per step, with flops
 weight gradient; dequantisation is not counted).
 
 The same run also measures:
+  * what the GPU attains on plain loops: the library's register-only bf16
+    MFMA loop (with its shader clock) and a 1 GiB streaming read, reported
+    beside the published peaks (roofline.attainable, attainable);
   * roofline of the dominant kernel, the bf16 MFMA GEMM (gemm_nt_kernel) that
     computes both Y = X Wd^T + (s X L1) L2 and dX = dY Wd + (s dY L2^T) L1^T,
     from HIP events that the library records around each of its launches on
     the call's stream, in a second pass of the same steps (the timed steps
     themselves run without those brackets); its HBM traffic comes from
     rocprofv3 FETCH_SIZE / WRITE_SIZE counters stored under profiles/
-    (scaled by the same counters on a plain device copy, see --copy-probe)
-    and is reported only while the kernel source still has the hash
-    recorded with them;
+    (scaled by the same counters on a plain device copy, see --copy-probe),
+    with the exact bytes of the request-size counters beside it
+    (traffic_exact), both reported only while the kernel source still has
+    the hash recorded with them;
   * the same step on the LLaMA-7B-shaped layer set (normal weights with 0.1 %
     outliers x10), with its own GEMM roofline;
   * the same headline step with LoRA dropout 0.05 (the pages' 33B setting);
@@ -158,14 +162,15 @@ def bench_dropout_step(api, layers, flops_step, plain_ms, steps=5, warmup=2, p=0
 
 def gemm_traffic(workload):
     """HBM bytes per gemm_nt_kernel launch from the stored counter summary of
-    this workload, or None when it is absent or was taken on a different
-    kernel source."""
+    this workload: (FETCH_SIZE + WRITE_SIZE scaled by a plain copy's, exact
+    bytes from the request-size counters), each None when absent or when the
+    summary was taken on a different kernel source."""
     import hashlib
 
     try:
         text = open(traffic_file(workload)).read()
     except OSError:
-        return None
+        return None, None
     src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
     fields = {}
     for line in text.splitlines():
@@ -173,11 +178,58 @@ def gemm_traffic(workload):
             k, v = line[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
     if fields.get("kernel source sha256") != src:
-        return None
-    try:
-        return float(fields["bytes per launch (scaled)"])
-    except (KeyError, ValueError):
-        return None
+        return None, None
+    out = []
+    for key in ("bytes per launch (scaled)", "bytes per launch (exact, request counters)"):
+        try:
+            out.append(float(fields[key]))
+        except (KeyError, ValueError):
+            out.append(None)
+    return tuple(out)
+
+
+def attainable_peaks(api, iters=20000, read_bytes=1 << 30, reps=5):
+    """What this GPU delivers on plain loops, for context beside the
+    published peaks: the library's register-only bf16 MFMA loop (one
+    8-wave workgroup per CU) with its shader clock, and a streaming read of
+    1 GiB (4x the 256 MB last-level cache) with 16-byte loads. Median of
+    ``reps`` launches each, timed with HIP events on the launch stream."""
+    import torch
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
+    clocks = torch.zeros(2, dtype=torch.int64, device="cuda")
+    flops = cus * 8 * iters * 8 * 32768
+    api.qlora_probe_mfma(cus, 1000, sink, clocks)
+    mf, clk = [], []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        api.qlora_probe_mfma(cus, iters, sink, clocks)
+        e1.record()
+        torch.cuda.synchronize()
+        mf.append(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        c = clocks.cpu().tolist()
+        clk.append(c[0] / (c[1] * 10.0))          # shader clocks per ns = GHz
+    buf = torch.full((read_bytes // 4,), 0x01010101, dtype=torch.int32, device="cuda")
+    rsink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    api.qlora_probe_read(buf, 0xFFFFFFFF, rsink)  # words XOR to 0: never 0xFFFFFFFF
+    rd = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        api.qlora_probe_read(buf, 0xFFFFFFFF, rsink)
+        e1.record()
+        torch.cuda.synchronize()
+        rd.append(read_bytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf
+    med = lambda v: sorted(v)[len(v) // 2]
+    out = {"mfma_bf16_tflops": med(mf), "mfma_clock_ghz": med(clk), "hbm_read_GBps": med(rd),
+           "mfma_loop": f"{cus} workgroups x 8 waves x {iters} rounds of 8 independent v_mfma_f32_32x32x16_bf16",
+           "read": f"{read_bytes} bytes once, 16-byte loads, 16 per thread issued before use"}
+    log(f"attainable: MFMA loop {out['mfma_bf16_tflops']:.0f} TFLOP/s at {out['mfma_clock_ghz']:.2f} GHz, "
+        f"streaming read {out['hbm_read_GBps']:.0f} GB/s")
+    return out
 
 
 def copy_probe(nbytes=1 << 30, reps=5):
@@ -657,8 +709,9 @@ def setup_and_time(api, workloads, name, steps, warmup, trials):
     # gemm_nt_kernel runs both products (one launch each per linear): its
     # algorithmic flops per launch averaged over the 14 launches of a step,
     # over its average launch duration.
+    traffic, traffic_exact = gemm_traffic(name)
     roofline = {"bound": "mfma", "achieved": kg["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": kg["tflops"] / PEAK_BF16_TFLOPS, "traffic": gemm_traffic(name),
+                "frac": kg["tflops"] / PEAK_BF16_TFLOPS, "traffic": traffic, "traffic_exact": traffic_exact,
                 "kernel": "gemm_nt_kernel", "avg_launch_ms": kg["avg_ms"], "launches": kg["launches"],
                 "flops_per_launch": (sum(fwd_flops) + sum(dx_flops)) / (2 * n_l)}
     shp_desc = ", ".join(f"{d['shape'].name} {d['shape'].K}->{d['shape'].N}" for d in layers)
@@ -749,6 +802,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=["llama7b-layer", "llama33b-layer"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the headline step")
+    ap.add_argument("--only", choices=["gemv", "mid_m", "merge", "quantize", "attainable"],
+                    help="run one extra section alone and print its JSON (for profiling)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (calibration of the HBM byte counters)")
     args = ap.parse_args()
@@ -769,8 +824,17 @@ def main():
         copy_probe()
         return
     api.library()
+    if args.only:
+        fn = {"gemv": lambda: bench_gemv(api, workloads), "mid_m": lambda: bench_mid_m(api, workloads),
+              "merge": lambda: bench_merge(api, workloads), "quantize": lambda: bench_quantize(api, workloads),
+              "attainable": lambda: attainable_peaks(api)}[args.only]
+        print(json.dumps({args.only: fn()}), flush=True)
+        return
     name = args.workload
+    peaks = attainable_peaks(api)
     head, layers, host, ws = setup_and_time(api, workloads, name, args.steps, args.warmup, args.trials)
+    head["roofline"]["attainable"] = peaks["mfma_bf16_tflops"]
+    head["roofline"]["frac_of_attainable"] = head["roofline"]["achieved"] / peaks["mfma_bf16_tflops"]
     result = {
         "metric": "QLoRA NF4 linear fwd+bwd TFLOP/s; NF4 GEMV weight GB/s (% of peak)",
         "value": head["value"],
@@ -788,6 +852,7 @@ def main():
         "trials_ms_per_step": head["trials_ms_per_step"],
         "roofline": head["roofline"],
         "kernels": head["kernels"],
+        "attainable": peaks,
     }
     if not args.no_extras:
         del ws
@@ -805,6 +870,8 @@ def main():
         result[other.replace("-", "_") + "_step"] = {k: sec[k] for k in ("value", "ms_per_step", "roofline",
                                                                           "kernels", "config")}
         result["gemv"] = bench_gemv(api, workloads)
+        for g in result["gemv"]:
+            g["graph_call_frac_of_attainable_read"] = g["graph_call_GBps"] / peaks["hbm_read_GBps"]
         result["quantize"] = bench_quantize(api, workloads)
         result["quantize_65b_pass"] = bench_quantize_pass(api, workloads, oracle_layer=not args.no_cpu_baseline)
         result["qtypes"] = bench_qtypes(api, workloads)

@@ -38,7 +38,7 @@ EXPORTS = (
     "qlora_linear_bwd", "qlora_set_timing", "qlora_int8_quantize", "qlora_int8_dequantize",
     "qlora_merge_adapters", "qlora_linear_workspace_dropout", "qlora_linear_fwd_dropout",
     "qlora_linear_bwd_dropout", "qlora_lora_dropout", "qlora_clip_grad_norm", "qlora_adam_step",
-    "qlora_linear_fwd_noalloc", "qlora_check_conversions",
+    "qlora_linear_fwd_noalloc", "qlora_check_conversions", "qlora_probe_mfma", "qlora_probe_read",
 )
 QLORA_NOALLOC_SCRATCH_BYTES = (2 << 20) + (64 << 10)
 QLORA_CLIP_WORKSPACE_BYTES = 8192
@@ -142,6 +142,10 @@ def _load():
     lib.qlora_int8_dequantize.argtypes = [vp, vp, i64, ctypes.c_int, vp, ctypes.c_int, vp]
     lib.qlora_check_conversions.argtypes = [ctypes.c_uint32, i64, vp, vp, vp, vp]
     lib.qlora_check_conversions.restype = ctypes.c_int
+    lib.qlora_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp]
+    lib.qlora_probe_mfma.restype = ctypes.c_int
+    lib.qlora_probe_read.argtypes = [vp, sz, ctypes.c_uint32, vp, vp]
+    lib.qlora_probe_read.restype = ctypes.c_int
     lib.qlora_int8_dequantize.restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -326,6 +330,24 @@ def qlora_check_conversions(first: int, count: int, bf16=True, e4m3=True, table=
     _check(_load().qlora_check_conversions(int(first) & 0xFFFFFFFF, int(count), _ptr(bf), _ptr(e8), _ptr(tb),
                                            _stream(stream)), "qlora_check_conversions")
     return bf, e8, tb
+
+
+QLORA_PROBE_READ_GRANULE = 65536
+
+
+@_on_stream
+def qlora_probe_mfma(workgroups: int, iters: int, sink, clocks, stream=None):
+    """Enqueue the register-only MFMA loop (measurement aid); sink: device
+    float32[workgroups * 512], clocks: device int64[2]."""
+    _check(_load().qlora_probe_mfma(int(workgroups), int(iters), _ptr(sink), _ptr(clocks), _stream(stream)),
+           "qlora_probe_mfma")
+
+
+@_on_stream
+def qlora_probe_read(src, never: int, sink, stream=None):
+    """Enqueue one streaming read of the device tensor src (measurement aid)."""
+    _check(_load().qlora_probe_read(_ptr(src), src.numel() * src.element_size(), int(never) & 0xFFFFFFFF,
+                                    _ptr(sink), _stream(stream)), "qlora_probe_read")
 
 
 class KernelTimer:

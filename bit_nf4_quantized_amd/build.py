@@ -24,7 +24,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libqlora_nf4.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 OBJ_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "gemv.hip", "gemv1.hip", "dense_gemm.hip", "skinny_gemm.hip", "int8.hip", "merge.hip", "midm.hip", "dropout.hip", "optim.hip", "convcheck.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "gemv.hip", "gemv1.hip", "dense_gemm.hip", "skinny_gemm.hip", "int8.hip", "merge.hip", "midm.hip", "dropout.hip", "optim.hip", "convcheck.hip", "probe.hip"]
 ARCH = os.environ.get("QLORA_OFFLOAD_ARCH", "gfx950")
 
 

@@ -506,6 +506,25 @@ int qlora_check_conversions(uint32_t first, int64_t count, uint16_t* bf16_out, u
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 
+int qlora_probe_mfma(int workgroups, int iters, float* sink, uint64_t* clocks, hipStream_t stream) {
+  if (!sink || !clocks || workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 20))
+    return QLORA_ERR_ARG;
+  (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
+  const hipError_t e = qlora::launch_mfma_probe(workgroups, iters, sink,
+                                                reinterpret_cast<unsigned long long*>(clocks), stream);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
+
+int qlora_probe_read(const void* src, size_t bytes, uint32_t never, uint32_t* sink, hipStream_t stream) {
+  static_assert(QLORA_PROBE_READ_GRANULE == 65536, "granule");
+  if (bytes == 0 || bytes % qlora::read_probe_granule() != 0 || bytes >= ((size_t)1 << 40)) return QLORA_ERR_SHAPE;
+  if (!src || !sink) return QLORA_ERR_ARG;
+  if (!aligned16(src)) return QLORA_ERR_ALIGN;
+  (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
+  const hipError_t e = qlora::launch_read_probe(src, bytes, never, sink, stream);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
+
 int qlora_set_timing(int kernel, hipEvent_t* start, hipEvent_t* stop, int n, int* count) {
   if (kernel < 0 || kernel >= QLORA_TIMING_CLASSES || n < 0) return QLORA_ERR_ARG;
   qlora::TimingSlot& t = qlora::timing_slots()[kernel];

@@ -210,6 +210,13 @@ hipError_t launch_gemv1(const NF4View& W, const NF4Table& tab, const uint16_t* X
 hipError_t launch_convcheck(uint32_t first, int64_t count, uint16_t* bf, uint8_t* e8, float* table,
                             hipStream_t stream);
 
+// Measurement aids (probe.hip): a register-only MFMA loop (clocks[0] =
+// shader clocks, clocks[1] = 100 MHz ticks of workgroup 0's loop) and a
+// streaming read of `bytes` (a multiple of read_probe_granule()).
+hipError_t launch_mfma_probe(int workgroups, int iters, float* sink, unsigned long long* clocks, hipStream_t stream);
+size_t read_probe_granule();
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t never, uint32_t* sink, hipStream_t stream);
+
 // Decode-path forward (M <= 16): bf16(s Xa L1) into sT ([M][r]) from the
 // K-slice partials in part, then the dequant-GEMV with the LoRA term. Xa is
 // the adapter branch's input (X, or its dropped copy).

@@ -439,6 +439,32 @@ int qlora_set_timing(int kernel, hipEvent_t *start, hipEvent_t *stop, int n, int
 int qlora_check_conversions(uint32_t first, int64_t count, uint16_t *bf16_out, uint8_t *e4m3_out,
                             float *e4m3_table, hipStream_t stream);
 
+/*
+ * Measurement aids for the benchmark's roofline figures; they compute
+ * nothing of the method and change no state of the library.
+ *
+ * qlora_probe_mfma: `workgroups` workgroups of 8 waves; each wave runs
+ * `iters` rounds of 8 independent v_mfma_f32_32x32x16_bf16 on register
+ * operands (2^18 flops per wave per round, no memory traffic in the loop).
+ *   sink    device f32[workgroups * 512], overwritten (keeps the work).
+ *   clocks  device uint64[2]: shader clocks (s_memtime) and 100 MHz ticks
+ *           (s_memrealtime) spent in workgroup 0's loop, for the clock rate.
+ * Returns QLORA_ERR_ARG for NULL pointers or workgroups, iters outside
+ * [1, 2^20].
+ *
+ * qlora_probe_read: reads `bytes` of src once with 16-byte loads (every
+ * thread's loads issued before any use) and stores nothing unless the XOR
+ * of a thread's words equals `never` (choose a value the data cannot give).
+ *   src     device, 16-byte aligned; bytes a positive multiple of
+ *           QLORA_PROBE_READ_GRANULE and below 2^40.
+ *   sink    device uint32[1].
+ * Returns QLORA_ERR_SHAPE for a bad size, QLORA_ERR_ARG for NULL pointers,
+ * QLORA_ERR_ALIGN for a misaligned src.
+ */
+#define QLORA_PROBE_READ_GRANULE 65536
+int qlora_probe_mfma(int workgroups, int iters, float *sink, uint64_t *clocks, hipStream_t stream);
+int qlora_probe_read(const void *src, size_t bytes, uint32_t never, uint32_t *sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
