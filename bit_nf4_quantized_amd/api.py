@@ -15,7 +15,8 @@ from dataclasses import dataclass
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libqlora_nf4.so")
+# QLORA_NF4_LIB selects another build of the same library (the sanitizer run)
+LIB_PATH = os.environ.get("QLORA_NF4_LIB") or os.path.join(HERE, "libqlora_nf4.so")
 
 QLORA_OK = 0
 QLORA_ERR_ARG = -1

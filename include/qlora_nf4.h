@@ -58,7 +58,16 @@ typedef enum {
   QLORA_ERR_HIP = -5         /* a HIP launch or runtime call failed */
 } qlora_status;
 
+/* Element types of the float operands. C callers may pass any int here; the
+ * C++ view gives the enum an int underlying type so that the library can
+ * read and reject values outside the list (QLORA_ERR_ARG) without undefined
+ * behaviour. */
+#ifdef __cplusplus
+enum qlora_dtype_values : int { QLORA_F32 = 0, QLORA_BF16 = 1 };
+typedef qlora_dtype_values qlora_dtype;
+#else
 typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
+#endif
 
 enum {
   QLORA_BLOCK = 64,      /* weights per first-level absmax constant */
