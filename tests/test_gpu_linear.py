@@ -117,6 +117,9 @@ def test_gemv_ragged(api, M, K, N, r):
     (16, 4096, 200, 72),    # 8-wave workgroups, X in registers, rank above 64
     (3, 2048, 1000, 8),     # 8-wave workgroups, X staged, rank 8
     (2, 128, 40, 256),      # one k-step per row (idle waves), largest rank
+    (1, 512, 264, 8),       # single-token kernel, rank 8: columns 8..63 of the LoRA split idle
+    (1, 4096, 22528, 16),   # single-token kernel, 88 rows per CU (11 row groups), rank 16
+    (1, 16384, 2048, 64),   # single-token kernel, largest K (64 LoRA slices, 32 KB of X)
 ])
 def test_gemv_paths(api, M, K, N, r):
     say(f"gemv path M={M} K={K} N={N} r={r}")
