@@ -15,7 +15,9 @@
 //                         the float64 adjacent-pair tree
 //                         sum of the group's 256 absmax values in LDS.
 //   tree_fold_kernel      one workgroup folds the per-group sums with the
-//                         same adjacent-pair rule and writes the fp32 mean.
+//                         same adjacent-pair rule (first levels in
+//                         registers, the rest in LDS) and writes the fp32
+//                         mean.
 //   dq_encode_kernel      one workgroup per group: a - mean, group absmax,
 //                         fp32 scale, E4M3 codes.
 //   dequant_kernel        4 units of 8 weights per thread: a code dword + the
@@ -218,21 +220,60 @@ __global__ __launch_bounds__(kQuantThreads) void quant_blocks_kernel(
 
 // Folds buf[0..n) with the adjacent-pair rule, level by level, in place
 // across two halves of the workspace, then writes mean = RN32(S / nb).
+// Adjacent-pair tree over the n group sums: at each level s'[i] = s[2i] +
+// s[2i+1], an odd last value carried up unchanged. With n <= 32 x 1024 the
+// first 5 levels run in registers (thread t folds the aligned 32 values
+// [32 t, 32 t + 32); a whole run of 32 reduces exactly as inside the full
+// tree, and the last, partial run ends the array at every level, so its
+// carries are the tree's own), the remaining levels in LDS. Larger n fold
+// level by level in the two global buffers.
 __global__ __launch_bounds__(1024) void tree_fold_kernel(double* __restrict__ a, double* __restrict__ b,
                                                          int64_t n, int64_t nb, float* __restrict__ mean) {
+  constexpr int kRun = 32;
+  __shared__ double s_fold[2][1024];
+  const int t = threadIdx.x;
+  if (n <= (int64_t)kRun * 1024) {
+    const int nruns = (int)((n + kRun - 1) / kRun);
+    if (t < nruns) {
+      const int64_t c0 = (int64_t)t * kRun;
+      int cnt = (int)(n - c0 < kRun ? n - c0 : kRun);
+      double r[kRun];
+#pragma unroll
+      for (int i = 0; i < kRun; ++i) r[i] = i < cnt ? a[c0 + i] : 0.0;
+#pragma unroll
+      for (int w = kRun; w > 1; w >>= 1) {          // one tree level: cnt values -> ceil(cnt / 2)
+#pragma unroll
+        for (int i = 0; i < w / 2; ++i) r[i] = (2 * i + 1 < cnt) ? r[2 * i] + r[2 * i + 1] : r[2 * i];
+        cnt = (cnt + 1) >> 1;
+      }
+      s_fold[0][t] = r[0];
+    }
+    __syncthreads();
+    int m = nruns, cur = 0;
+    while (m > 1) {
+      const int half = m >> 1;
+      if (t < half) s_fold[cur ^ 1][t] = s_fold[cur][2 * t] + s_fold[cur][2 * t + 1];
+      if ((m & 1) && t == 0) s_fold[cur ^ 1][half] = s_fold[cur][m - 1];
+      __syncthreads();
+      cur ^= 1;
+      m = (m + 1) >> 1;
+    }
+    if (t == 0) mean[0] = (nb > 0 && n > 0) ? (float)(s_fold[cur][0] / (double)nb) : 0.0f;
+    return;
+  }
   double* src = a;
   double* dst = b;
   while (n > 1) {
     const int64_t half = n >> 1;
-    for (int64_t i = threadIdx.x; i < half; i += blockDim.x) dst[i] = src[2 * i] + src[2 * i + 1];
-    if ((n & 1) && threadIdx.x == 0) dst[half] = src[n - 1];
+    for (int64_t i = t; i < half; i += blockDim.x) dst[i] = src[2 * i] + src[2 * i + 1];
+    if ((n & 1) && t == 0) dst[half] = src[n - 1];
     __syncthreads();
     double* tmp = src;
     src = dst;
     dst = tmp;
     n = (n + 1) >> 1;
   }
-  if (threadIdx.x == 0) {
+  if (t == 0) {
     const double S = (n == 1) ? src[0] : 0.0;
     mean[0] = nb > 0 ? (float)(S / (double)nb) : 0.0f;
   }
