@@ -82,6 +82,7 @@ def compare(got, ref, label):
     (8, 1024, 520, 64, 0.1),      # GEMV forward, small-M backward
     (64, 512, 256, 64, 0.1),      # batched-decode forward, GEMM dX
     (130, 448, 328, 72, 0.3),     # rank above 64: generic adapter products
+    (130, 256, 64 * 193, 16, 0.1),  # dX GEMM with the fp32 addend over N >= 12288 (three B buffers)
 ])
 def test_linear_with_dropout(api, M, K, N, r, p):
     say(f"dropout linear M={M} K={K} N={N} r={r} p={p}")

@@ -82,6 +82,10 @@ def test_tiny_512(api):
     # 4 x 66 tiles: the last 2 tile-columns as 64-row quarter tiles (ragged M
     # and N inside them); dX: 4 x 2 tiles, no tail split
     (1000, 512, 66 * 256 - 8, 16, 0.5, "normal"),
+    # reductions of 12288 and more run with three B stage buffers: the
+    # forward (K = 12352) here, and dX (over N = 12352) in the next case
+    (300, 64 * 193, 200, 16, 0.5, "normal"),
+    (300, 256, 64 * 193, 16, 0.25, "student-t4"),
 ])
 def test_shapes(api, M, K, N, r, s, kind):
     say(f"linear M={M} K={K} N={N} r={r} s={s} {kind}")
