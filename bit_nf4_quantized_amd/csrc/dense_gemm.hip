@@ -18,22 +18,20 @@
 //   * each wave owns a 128 x 64 sub-tile = 4 x 2 v_mfma_f32_32x32x16_bf16
 //     accumulators (128 fp32 registers per lane);
 //   * K advances in stages of 64: the A and B stage tiles (2 x 32 KB) are
-//     copied global -> LDS by global_load_lds_dwordx4 (no register staging),
-//     double-buffered (128 KB of the 160 KB LDS); for K >= 12288 the B tile
-//     is triple-buffered (all 160 KB), so that its copy is issued one stage
-//     earlier;
+//     copied global -> LDS by global_load_lds_dwordx4 (no register staging);
+//     A is double-buffered and B triple-buffered (all 160 KB of LDS);
 //   * software pipeline: the fragments of k-step kk+1 are read from LDS into
 //     a second register set while the 8 MFMAs of k-step kk run; the stage
 //     barrier sits before the last k-step, so the first fragments of the
 //     next stage are read while those MFMAs run;
 //   * each stage copy is issued in two halves, each spread one instruction
-//     per two MFMAs. With two B buffers: the B tile of stage st+2 among the
-//     MFMAs right after the barrier of stage st, its A tile among those of
-//     k-step 0 of stage st+1 (against both tiles as one burst after the
-//     barrier, 2-8 % faster per launch; B first, with the longer lead, was
-//     the best of the placements tried). With three: the B tile of stage
-//     st+2 during k-step 0 of stage st, its A tile after that stage's
-//     barrier;
+//     per two MFMAs: the B tile of stage st+2 among the MFMAs of k-step 1 of
+//     stage st (its third buffer held stage st-1), the A tile among those
+//     right after the barrier of stage st. So the B copy has almost two
+//     stages to land and the A copy one. Measured per launch against the
+//     earlier schedule (both tiles double-buffered and issued as one burst
+//     after the barrier): 3-8 % faster at K = 6656 and up to 13 % at
+//     K = 17920, where the copies had waited for memory 23 % of the loop;
 //   * the LDS copies are issued from inline assembly: with the compiler
 //     builtin for them, the generated code waited for all fragment reads
 //     (lgkmcnt(0)) and for the in-flight copy of the next stage (vmcnt(0))
@@ -79,7 +77,6 @@ constexpr int MI = WTM / 32;
 constexpr int NJ = WTN / 32;
 constexpr int RPI = 8;           // rows per wave load instruction (64 lanes x 16 B = 8 rows of 128 B)
 constexpr int kStageElems = TM * TK;  // LDS elements per operand per stage (TM == TN)
-constexpr int64_t kLongK = 12288;     // main reductions from this length on use three B buffers
 
 // The tail of a launch whose tile count leaves the last round of workgroups
 // mostly empty runs as half- or quarter-height tiles (TM / 2 or TM / 4
@@ -165,10 +162,9 @@ __device__ __forceinline__ void stage_load(const uint16_t* __restrict__ P, const
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * TK + ((chunk ^ swz(row)) << 3); }
 
 // One TMX x TN output tile at (m0, n0). smem holds the stage tiles: two A
-// buffers, then NBB (2 or 3) B buffers, kStageElems elements each.
-template <bool ADD, int TMX, int NBB>
+// buffers, then three B buffers, kStageElems elements each.
+template <bool ADD, int TMX>
 __device__ __forceinline__ void gemm_tile(const DenseArgs& p, int64_t m0, int64_t n0, uint16_t* smem) {
-  static_assert(NBB == 2 || NBB == 3, "two or three B buffers");
   using S = TileShape<TMX>;
   constexpr int WTM = S::kWtm, MI = S::kMi;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -192,7 +188,7 @@ __device__ __forceinline__ void gemm_tile(const DenseArgs& p, int64_t m0, int64_
   // then the slab (A2, B2). Operand selection is branch-free so that the
   // copy can be scheduled among the MFMAs of the same block.
   auto a_buf = [&](int st) { return smem + (st & 1) * kStageElems; };
-  auto b_buf = [&](int st) { return smem + (2 + (NBB == 2 ? (st & 1) : st % 3)) * kStageElems; };
+  auto b_buf = [&](int st) { return smem + (2 + st % 3) * kStageElems; };
   auto issue = [&](int st) {
     const bool slab = st >= nmain;
     const int64_t k0 = (int64_t)(slab ? st - nmain : st) * TK;
@@ -278,41 +274,32 @@ __device__ __forceinline__ void gemm_tile(const DenseArgs& p, int64_t m0, int64_
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // One stage. On entry the fragments of its k-step 0 are in set 0. The
-  // copies of stage st+2 go into the buffers that are free by then:
-  //   NBB == 2: the A tile of stage st+1 is issued during k-step 0 (the B
-  //     tile went out after the previous barrier), the B tile of st+2 after
-  //     this stage's barrier;
-  //   NBB == 3: the B tile of stage st+2 during k-step 0 (its third buffer
-  //     held stage st-1), the A tile of st+2 after the barrier; the B tile
-  //     may still be in flight at the next barrier.
+  // One stage. On entry the fragments of its k-step 0 are in set 0, and the
+  // copies of stages st+1 (complete or in flight) and st+2 (the B tile, in
+  // flight: the A tile goes out after this stage's barrier) were issued.
   // The prologue issued all of stages 0 and 1.
   auto stage = [&](int st, bool refill, bool next) {
-    frag(st, 1, 1);
-    if constexpr (NBB == 2)
-      mma_copies(0, st + 1, 0, S::kIpwA, st >= 1 && st + 1 < nk);
-    else
-      mma_copies(0, st + 2, S::kIpwA, S::kIpwB, refill);
 #pragma unroll
-    for (int kk = 1; kk < TK / 16 - 1; ++kk) {
+    for (int kk = 0; kk < TK / 16 - 1; ++kk) {
       frag(st, kk + 1, (kk + 1) & 1);
-      mma(kk & 1);
-      order();
+      if (kk == 1) {
+        mma_copies(1, st + 2, S::kIpwA, S::kIpwB, refill);  // B tile of stage st+2
+      } else {
+        mma(kk & 1);
+        order();
+      }
     }
     // every read of this stage's buffers by this wave has been issued; the
-    // barrier's release fence completes them, the vmcnt completes this
-    // wave's copies of stage st+1 (in-order completion: with NBB == 3 the
-    // B copies of st+2, issued after them, may stay in flight)
+    // barrier's release fence completes them. The vmcnt completes this
+    // wave's copies of stage st+1; the B copies of st+2, issued after them,
+    // may stay in flight (copies complete in issue order)
     __builtin_amdgcn_sched_barrier(0);
-    if (NBB == 3 && refill) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(S::kIpwB) : "memory");
+    if (refill) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(S::kIpwB) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     if (next) frag(st + 1, 0, 0);
-    if constexpr (NBB == 2)
-      mma_copies(1, st + 2, S::kIpwA, S::kIpwB, refill);  // B tile of stage st+2
-    else
-      mma_copies(1, st + 2, 0, S::kIpwA, refill);         // A tile of stage st+2
+    mma_copies(1, st + 2, 0, S::kIpwA, refill);  // A tile of stage st+2
   };
   if (nk > 0) issue(0);
   if (nk > 1) issue(1);
@@ -406,9 +393,9 @@ __device__ __forceinline__ void gemm_tile(const DenseArgs& p, int64_t m0, int64_
   }
 }
 
-template <bool ADD, int NBB>
+template <bool ADD>
 __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(DenseArgs p) {
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[(2 + NBB) * kStageElems];  // A x 2, B x NBB
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[5 * kStageElems];  // A x 2, B x 3
   const int bid = blockIdx.x;
   const int nfull = p.tiles_m * p.full_n;
   if (bid < nfull) {
@@ -424,7 +411,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(DenseArgs p) {
     const int tl = t - g * group * p.full_n;
     const int tm = first_m + tl % gm;
     const int tn = tl / gm;
-    gemm_tile<ADD, TM, NBB>(p, (int64_t)tm * TM, (int64_t)tn * TN, smem);
+    gemm_tile<ADD, TM>(p, (int64_t)tm * TM, (int64_t)tn * TN, smem);
   } else {
     // the tail tile-columns, as half- or quarter-height tiles; dispatched
     // last, they fill the last round of workgroups
@@ -434,9 +421,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_nt_kernel(DenseArgs p) {
     if (m0 >= p.M) return;  // a piece of a last tile-row beyond M (uniform per workgroup)
     const int64_t n0 = (int64_t)(p.full_n + h % ncols) * TN;
     if (p.tail_split == 4)
-      gemm_tile<ADD, TM / 4, NBB>(p, m0, n0, smem);
+      gemm_tile<ADD, TM / 4>(p, m0, n0, smem);
     else
-      gemm_tile<ADD, TM / 2, NBB>(p, m0, n0, smem);
+      gemm_tile<ADD, TM / 2>(p, m0, n0, smem);
   }
 }
 
@@ -566,18 +553,10 @@ hipError_t launch_gemm_nt_rows(const uint16_t* A, int64_t lda, const uint16_t* B
   }
   p.full_n = p.tiles_n - tail_cols;
   const int ntiles = p.tiles_m * p.full_n + p.tail_split * p.tiles_m * tail_cols;
-  // Long reductions take a third B buffer (all 160 KB of LDS), so that the
-  // B copies are issued a stage earlier: at K >= 12288 the copies waited
-  // for memory 10-23 % of the loop with two (8192 x 6656 x 17920: 1723 ->
-  // 1594 us); at K <= 11008 two buffers measured 0-4 % faster.
-  const dim3 grid((unsigned)ntiles), block(kThreads);
-  if (K >= kLongK) {
-    if (E) hipLaunchKernelGGL((gemm_nt_kernel<true, 3>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((gemm_nt_kernel<false, 3>), grid, block, 0, stream, p);
-  } else {
-    if (E) hipLaunchKernelGGL((gemm_nt_kernel<true, 2>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((gemm_nt_kernel<false, 2>), grid, block, 0, stream, p);
-  }
+  if (E)
+    hipLaunchKernelGGL(gemm_nt_kernel<true>, dim3((unsigned)ntiles), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(gemm_nt_kernel<false>, dim3((unsigned)ntiles), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
