@@ -148,7 +148,7 @@ struct SkinnySplit {
   int Z;        // reduction slices
   int64_t len;  // reduction length per slice (multiple of 64)
 };
-SkinnySplit skinny_split(int64_t tiles, int64_t klen);
+SkinnySplit skinny_split(int64_t tiles, int64_t klen, int64_t fit = 0);
 size_t skinny_partial_bytes(int64_t M, int64_t K, int64_t N);
 // dr: A is the adapter input X ([M][K], lda == K), dropped in registers.
 hipError_t skinny_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t M, int64_t K, int r,

@@ -265,6 +265,149 @@ __global__ __launch_bounds__(kSkThreads) void skinny_tn_kernel(TnArgs p) {
   }
 }
 
+// skinny_tn_dma_kernel: the product of skinny_tn_kernel<false> with both
+// operands copied global -> LDS by global_load_lds_dwordx4 in their memory
+// layout (rows of 128 L columns and of 64 S columns, m running down the rows)
+// into a ring of kTnStages stages, so that the copies of two stages are in
+// flight while a third is multiplied. The MFMA fragments (8 consecutive m of
+// one column) are read with the transpose read ds_read_b64_tr_b16: in each
+// group of 16 lanes, lane i receives element i % 4 of the 8 bytes that lane
+// 4e + i / 4 addresses, as its element e. If lane j of the group addresses
+// row m0 + j / 4, columns cb + 4 (j % 4) .. +3, lane i receives rows
+// m0 .. m0 + 3 of column cb + i. Two such reads make one 8-element fragment.
+// Rows outside the slice and S columns at or beyond r are copied from a
+// zeroed 16-byte block, L columns at or beyond W from clamped (valid)
+// addresses: their outputs are never stored. The results equal
+// skinny_tn_kernel<false>'s bit for bit (the same MFMAs in the same order).
+constexpr int kTnStages = 3;
+constexpr int kTnLRow = SM * 2;                       // bytes per staged L row (128 columns)
+constexpr int kTnSRow = SJ * 2;                       // bytes per staged S row (64 columns)
+constexpr int kTnLBytes = SK * kTnLRow;               // 16 KB
+constexpr int kTnStageBytes = kTnLBytes + SK * kTnSRow;  // 24 KB
+
+__device__ __attribute__((aligned(16))) uint32_t g_tn_zero[4];  // zero-initialised copy source
+
+// 16-byte chunk q of staged row m sits at chunk q ^ swz(m). L rows are 256 B
+// (one row per pass of the 64 banks): the four rows that one transpose read
+// of 32 lanes touches (m0 .. m0 + 3, four chunks each) land on 16 distinct
+// chunk positions. S rows are 128 B (two rows per pass): rows m0 and m0 + 2
+// are moved apart.
+__device__ __forceinline__ int tn_lswz(int m) { return (m & 3) << 2; }
+__device__ __forceinline__ int tn_sswz(int m) { return ((m >> 1) & 1) << 2; }
+
+typedef short tn_v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ tn_v4i16 tn_read_tr(const char* lds_byte) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) tn_v4i16*)(lds_void_t*)lds_byte);
+}
+
+__global__ __launch_bounds__(kSkThreads) void skinny_tn_dma_kernel(TnArgs p) {
+  __shared__ __attribute__((aligned(1024))) char ring[kTnStages * kTnStageBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * SM;
+  const int64_t mz0 = (int64_t)blockIdx.z * p.m_split;
+  const int64_t mz1 = (mz0 + p.m_split < p.M) ? mz0 + p.m_split : p.M;
+  const int ns = mz0 < mz1 ? (int)((mz1 - mz0 + SK - 1) / SK) : 0;
+  const char* zero = reinterpret_cast<const char*>(g_tn_zero);
+
+  // Copy roles. L: instruction i of wave w moves rows 4 (4w + i) .. +3, lane
+  // -> row 4 (4w + i) + lane / 16, chunk position lane % 16. S: instruction i
+  // moves rows 8 (2w + i) .. +7, lane -> row 8 (2w + i) + lane / 8, position
+  // lane % 8. The column parts of the source addresses are fixed per lane.
+  int64_t l_col[4], s_col[2];
+  bool s_in[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * (4 * wave + i) + (lane >> 4);
+    int64_t c = c0 + 8 * ((lane & 15) ^ tn_lswz(row));
+    if (c > p.W - 8) c = p.W - 8;  // W % 8 == 0
+    l_col[i] = c;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 8 * (2 * wave + i) + (lane >> 3);
+    const int j = 8 * ((lane & 7) ^ tn_sswz(row));
+    s_in[i] = j < p.r;
+    s_col[i] = s_in[i] ? j : 0;
+  }
+  auto copy = [&](const char* src, char* lds) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)lds);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "s"(m0) : "memory", "m0");
+  };
+  auto issue = [&](int st) {  // the 6 copy instructions of this wave for stage st
+    const int64_t ms = mz0 + (int64_t)st * SK;
+    char* buf = ring + (st % kTnStages) * kTnStageBytes;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * (4 * wave + i) + (lane >> 4);
+      const int64_t m = ms + row;
+      const char* src = m < mz1 ? reinterpret_cast<const char*>(p.L + m * p.ldl + l_col[i]) : zero;
+      copy(src, buf + (4 * wave + i) * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = 8 * (2 * wave + i) + (lane >> 3);
+      const int64_t m = ms + row;
+      const char* src = (m < mz1 && s_in[i]) ? reinterpret_cast<const char*>(p.S + m * p.lds + s_col[i]) : zero;
+      copy(src, buf + kTnLBytes + (2 * wave + i) * 1024);
+    }
+  };
+
+  f32x16_t acc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[t][v] = 0.0f;
+
+  // Transpose-read addresses, relative to a stage buffer and k-step: lane j
+  // of its group addresses row (lane / 32) * 8 + 4 h + j / 4 (+16 kk),
+  // columns cb + 4 (j % 4) .. +3 with cb = 16 ((lane / 16) % 2) + the wave's
+  // (L) or the tile's (S) first column.
+  const int jl = lane & 15;
+  const int rbase = 8 * (lane >> 5) + (jl >> 2);
+  const int cl = wave * 32 + 16 * ((lane >> 4) & 1) + 4 * (jl & 3);  // L column (within the tile)
+  const int cs = 16 * ((lane >> 4) & 1) + 4 * (jl & 3);              // S column within a 32-wide tile
+  auto loff = [&](int row) { return row * kTnLRow + ((((cl >> 3) ^ tn_lswz(row))) << 4) + ((cl & 7) << 1); };
+  auto soff = [&](int row, int t) {
+    const int c = 32 * t + cs;
+    return kTnLBytes + row * kTnSRow + (((c >> 3) ^ tn_sswz(row)) << 4) + ((c & 7) << 1);
+  };
+
+#pragma unroll
+  for (int st = 0; st < kTnStages - 1; ++st)
+    if (st < ns) issue(st);
+  for (int st = 0; st < ns; ++st) {
+    // this wave's copies of stage st are complete (those of st + 1 may not be)
+    if (st + 1 < ns) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // every wave's copies of stage st are visible; stage st-1's reads are done
+    if (st + kTnStages - 1 < ns) issue(st + kTnStages - 1);  // into stage st-1's buffer
+    const char* buf = ring + (st % kTnStages) * kTnStageBytes;
+#pragma unroll
+    for (int kk = 0; kk < SK / 16; ++kk) {
+      const int r0 = 16 * kk + rbase;
+      const tn_v4i16 a0 = tn_read_tr(buf + loff(r0)), a1 = tn_read_tr(buf + loff(r0 + 4));
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const tn_v4i16 b0 = tn_read_tr(buf + soff(r0, t)), b1 = tn_read_tr(buf + soff(r0 + 4, t));
+        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[t], 0, 0, 0);
+      }
+    }
+  }
+  float* Cz = p.C + (int64_t)blockIdx.z * p.W * SJ;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int j = t * 32 + (lane & 31);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t c = c0 + wave * 32 + (v & 3) + 4 * (lane >> 5) + 8 * (v >> 2);
+      if (c < p.W) Cz[c * SJ + j] = acc[t][v];
+    }
+  }
+}
+
 // out = alpha * sum_z P[z] over a [rows][SJ] slab, columns j < r:
 //   mode 0: out[m][j] (row stride ldo; columns [r, ldo) zero) in bf16, plus
 //           optional out2[m][j] = bf16(alpha2 * sum) with row stride r
@@ -349,12 +492,14 @@ int64_t sk_grid(int64_t total) {
 }  // namespace
 
 // Number of reduction slices for a skinny product with `tiles` output tiles
-// over a reduction of length klen (multiples of 64), so that about 512
-// workgroups stream the large operand.
-SkinnySplit skinny_split(int64_t tiles, int64_t klen) {
+// over a reduction of length klen (multiples of 64): about 512 workgroups
+// stream the large operand, or, with fit > 0, at most max(fit, tiles) of
+// them (the workgroups that fit on the device at once), so that none waits
+// for a second round.
+SkinnySplit skinny_split(int64_t tiles, int64_t klen, int64_t fit) {
   const int64_t steps = sk_cdiv(klen, SK);
   if (steps < 1) return SkinnySplit{1, SK};
-  int64_t z = sk_cdiv(512, tiles < 1 ? 1 : tiles);
+  int64_t z = fit > 0 ? fit / (tiles < 1 ? 1 : tiles) : sk_cdiv(512, tiles < 1 ? 1 : tiles);
   if (z > 32) z = 32;
   if (z > steps) z = steps;
   if (z < 1) z = 1;
@@ -404,7 +549,8 @@ hipError_t skinny_tn(const uint16_t* L, int64_t ldl, int64_t W, const uint16_t* 
                      float* part, float alpha, bool transpose, bool out_bf16, void* out, hipStream_t stream,
                      const DropoutParams* dr) {
   if (dr && (ldl != W || W % 64)) return hipErrorInvalidValue;  // the mask indexes a contiguous [M][W] input
-  const SkinnySplit sp = skinny_split(sk_cdiv(W, SM), M);
+  // the copy-ring kernel (72 KB of LDS) fits two workgroups per CU
+  const SkinnySplit sp = skinny_split(sk_cdiv(W, SM), M, dr ? 0 : 2 * (int64_t)device_cu_count());
   TnArgs a;
   a.L = L; a.S = S; a.C = part; a.ldl = ldl; a.lds = lds; a.M = M; a.W = W; a.r = r; a.m_split = sp.len;
   a.thr = dr ? dr->thr : 0u; a.c = dr ? dr->c : 1.0f; a.seed = dr ? dr->seed : 0u;
@@ -412,7 +558,7 @@ hipError_t skinny_tn(const uint16_t* L, int64_t ldl, int64_t W, const uint16_t* 
   if (dr)
     hipLaunchKernelGGL(skinny_tn_kernel<true>, grid, dim3(kSkThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(skinny_tn_kernel<false>, grid, dim3(kSkThreads), 0, stream, a);
+    hipLaunchKernelGGL(skinny_tn_dma_kernel, grid, dim3(kSkThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (transpose)
