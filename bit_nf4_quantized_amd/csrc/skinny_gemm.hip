@@ -91,18 +91,25 @@ __global__ __launch_bounds__(kSkThreads) void skinny_nt_kernel(NtArgs p) {
     const int rloc = (wave * 2 + j) * 8 + lr;
     offB[j] = (uint32_t)((rloc * p.ldb + (((lane & 7) ^ sk_swz(rloc)) * 8)) * 2);
   }
+  // The copies are issued from inline assembly (uniform base in SGPRs, the
+  // lane's offset in a VGPR): with the compiler builtin for them, the
+  // generated code waited for every copy in flight, the next stages'
+  // included, before the first LDS read of each stage, so no copy overlapped
+  // the MFMAs. The explicit vmcnt before each stage's barrier is the only
+  // wait on them.
+  auto copy = [&](const char* base, uint32_t off, const uint16_t* lds) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)lds);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(off), "s"(base), "s"(m0)
+                 : "memory", "m0");
+  };
   auto issue = [&](int st, int buf) {
     const int64_t k0 = kz0 + (int64_t)st * SK;
     const char* a = reinterpret_cast<const char*>(p.A + k0);
     const char* b = reinterpret_cast<const char*>(p.B + k0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(a + offA[j]), (lds_void_t*)(sA[buf] + (wave * 4 + j) * 8 * SK),
-                                       16, 0, 0);
+    for (int j = 0; j < 4; ++j) copy(a, offA[j], sA[buf] + (wave * 4 + j) * 8 * SK);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(b + offB[j]), (lds_void_t*)(sB[buf] + (wave * 2 + j) * 8 * SK),
-                                       16, 0, 0);
+    for (int j = 0; j < 2; ++j) copy(b, offB[j], sB[buf] + (wave * 2 + j) * 8 * SK);
   };
 
   f32x16_t acc[2];
@@ -528,7 +535,8 @@ hipError_t skinny_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t 
                      float* part, float alpha, uint16_t* out, int64_t ldo, float alpha2, uint16_t* out2,
                      hipStream_t stream, const DropoutParams* dr) {
   if (dr && lda != K) return hipErrorInvalidValue;  // the mask indexes a contiguous [M][K] input
-  const SkinnySplit sp = skinny_split(sk_cdiv(M, SM), K);
+  // 72 KB of LDS: two workgroups per CU
+  const SkinnySplit sp = skinny_split(sk_cdiv(M, SM), K, 2 * (int64_t)device_cu_count());
   NtArgs a;
   a.A = A; a.B = B; a.C = part; a.lda = lda; a.ldb = ldb; a.M = M; a.K = K; a.k_split = sp.len;
   a.thr = dr ? dr->thr : 0u; a.c = dr ? dr->c : 1.0f; a.seed = dr ? dr->seed : 0u;
