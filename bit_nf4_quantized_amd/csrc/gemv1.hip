@@ -105,11 +105,18 @@ __global__ __launch_bounds__(256) void t1_partial_kernel(const uint16_t* __restr
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[ph][cc * 8 + e] = acc[e];
   __syncthreads();
-  if (t < r) {
+  // column j = t / 4: lane t % 4 adds rows 8 (t % 4) .. +7 in order, then
+  // the four lanes' sums are added pairwise by DPP, ((s0 + s1) + (s2 + s3)):
+  // a fixed order (every lane of the four holds the same bits), with a
+  // dependent chain of 10 additions instead of 32
+  {
+    const int j = t >> 2, p4 = t & 3;
     float v = 0.0f;
-#pragma unroll 8
-    for (int q = 0; q < 32; ++q) v += red[q][t];
-    part[(int64_t)blockIdx.x * r + t] = v;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v += red[8 * p4 + q][j];
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+    v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+    if (p4 == 0 && j < r) part[(int64_t)blockIdx.x * r + j] = v;
   }
 }
 
