@@ -21,14 +21,16 @@
 //   dropout (DROP) A is the adapter input X, and every A fragment is
 //   dropped in registers after its LDS read (each A element is read by
 //   exactly one lane), from the Philox words of its element indices.
-// skinny_tn_kernel:  C[z][c][j] = sum_{m in slice z} L[m][c] S[m][j]
-//   the reduction runs down the rows of both operands, so each thread loads
-//   two rows x 8 columns and writes them to LDS transposed as (m, m+1)
-//   pairs; 128 columns c x 64 j per workgroup, M-stages of 64. With LoRA
-//   dropout (DROP) the large operand is the adapter input X and the loaded
-//   values are dropped in registers, from the Philox words of their element
-//   indices m W + c, before they go to LDS: the dropped copy of X is never
-//   written to memory.
+// skinny_tn_dma_kernel:  C[z][c][j] = sum_{m in slice z} L[m][c] S[m][j]
+//   the reduction runs down the rows of both operands; both are copied
+//   global -> LDS in their memory layout into a 3-stage ring, and the MFMA
+//   fragments (consecutive m of one column) are read with the LDS transpose
+//   read; 128 columns c x 64 j per workgroup, M-stages of 64.
+// skinny_tn_kernel<true>:  the same product with LoRA dropout on the large
+//   operand (the adapter input X): each thread loads two rows x 8 columns,
+//   drops them in registers from the Philox words of their element indices
+//   m W + c, and writes them to LDS transposed as (m, m+1) pairs, so the
+//   dropped copy of X is never written to memory.
 #include "common.h"
 #include "launch.h"
 #include "philox.h"
@@ -272,7 +274,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_tn_kernel(TnArgs p) {
   }
 }
 
-// skinny_tn_dma_kernel: the product of skinny_tn_kernel<false> with both
+// skinny_tn_dma_kernel: the product of skinny_tn_kernel without dropout, with both
 // operands copied global -> LDS by global_load_lds_dwordx4 in their memory
 // layout (rows of 128 L columns and of 64 S columns, m running down the rows)
 // into a ring of kTnStages stages, so that the copies of two stages are in
@@ -285,7 +287,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_tn_kernel(TnArgs p) {
 // Rows outside the slice and S columns at or beyond r are copied from a
 // zeroed 16-byte block, L columns at or beyond W from clamped (valid)
 // addresses: their outputs are never stored. The results equal
-// skinny_tn_kernel<false>'s bit for bit (the same MFMAs in the same order).
+// register-staged kernel's bit for bit (the same MFMAs in the same order).
 constexpr int kTnStages = 3;
 constexpr int kTnLRow = SM * 2;                       // bytes per staged L row (128 columns)
 constexpr int kTnSRow = SJ * 2;                       // bytes per staged S row (64 columns)
