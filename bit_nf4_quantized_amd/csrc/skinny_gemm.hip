@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_tn_kernel(TnArgs p) {
 // m0 .. m0 + 3 of column cb + i. Two such reads make one 8-element fragment.
 // Rows outside the slice and S columns at or beyond r are copied from a
 // zeroed 16-byte block, L columns at or beyond W from clamped (valid)
-// addresses: their outputs are never stored. The results equal
+// addresses: their outputs are never stored. The results equal the
 // register-staged kernel's bit for bit (the same MFMAs in the same order).
 constexpr int kTnStages = 3;
 constexpr int kTnLRow = SM * 2;                       // bytes per staged L row (128 columns)
