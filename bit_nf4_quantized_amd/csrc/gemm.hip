@@ -447,6 +447,13 @@ hipError_t launch_small_lora_down(const uint16_t* X, int64_t M, int64_t K, const
                                   uint16_t* sT, int64_t ldst, uint16_t* T_out, float* part, hipStream_t stream);
 hipError_t launch_gemv(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M,
                        const uint16_t* sT, const uint16_t* L2, int r, uint16_t* Y, hipStream_t stream);
+int small_t_slices(int64_t K);
+hipError_t launch_small_t_partial(const uint16_t* X, int64_t M, int64_t K, const uint16_t* L1, int r, float* part,
+                                  hipStream_t stream);
+bool gemv_fuses_t(const NF4View& W, int64_t M, int r);
+hipError_t launch_gemv_fused_t(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M,
+                               const float* part, int Z, float s, uint16_t* T_out, const uint16_t* L2, int r,
+                               uint16_t* Y, hipStream_t stream);
 
 LinearWorkspace linear_workspace_layout(int64_t M, int64_t K, int64_t N, int r, bool dropout) {
   LinearWorkspace L;
@@ -554,6 +561,13 @@ hipError_t linear_forward_small(const NF4View& W, const NF4Table& tab, const uin
                                 int64_t M, const uint16_t* L1, const uint16_t* L2, int r, float s, uint16_t* Y,
                                 uint16_t* T_out, uint16_t* sT, float* part, hipStream_t stream) {
   if (Xa == X && gemv1_applies(W, M, r)) return launch_gemv1(W, tab, X, L1, L2, r, s, Y, T_out, part, stream);
+  if (gemv_fuses_t(W, M, r)) {  // the slice partials of Xa L1 summed inside the GEMV (one launch fewer)
+    hipError_t e = launch_small_t_partial(Xa, M, W.cols, L1, r, part, stream);
+    if (e != hipSuccess) return e;
+    return timed(kTimeGemv, stream, [&] {
+      return launch_gemv_fused_t(W, tab, X, M, part, small_t_slices(W.cols), s, T_out, L2, r, Y, stream);
+    });
+  }
   hipError_t e = launch_small_lora_down(Xa, M, W.cols, L1, r, s, sT, r, T_out, part, stream);
   if (e != hipSuccess) return e;
   return timed(kTimeGemv, stream, [&] { return launch_gemv(W, tab, X, M, sT, L2, r, Y, stream); });

@@ -436,20 +436,33 @@ constexpr int kLutCopies = 32;
 constexpr uint32_t kLutBytes = 256u * kLutCopies * 4u;   // 32 KB
 
 struct GlLayout {
-  uint32_t a_off, lora_off, x_off, xpitch, total;
+  uint32_t a_off, lora_off, x_off, xpitch, q_off, total;
 };
 
-// waves, ring depth, X rows staged in LDS (0 when X rides in registers)
-__host__ __device__ inline GlLayout gl_layout(int64_t K, int waves, int depth, int mx_lds) {
+// waves, ring depth, X rows staged in LDS (0 when X rides in registers),
+// bytes of the per-wave sums of the adapter's slice partials (0 unless fused)
+__host__ __device__ inline GlLayout gl_layout(int64_t K, int waves, int depth, int mx_lds, uint32_t q_bytes) {
   GlLayout L;
   uint32_t off = kLutBytes;                      // the table; partial sums reuse it at the end
   L.a_off = off; off += (uint32_t)(waves * depth) * 128u;  // per wave: a' [slot][block][16 rows] fp32
   L.lora_off = off; off += 2u * 64u * 32u;       // wave 0's packed LoRA fragments, 2 rank chunks x 64 lanes x 32 B
   L.xpitch = (uint32_t)K * 2u;                   // X rows back to back (staged only for M <= 2 in practice)
   L.x_off = off; off += (uint32_t)mx_lds * L.xpitch;
+  L.q_off = off; off += q_bytes;                 // [wave][M r] fp32
   L.total = off;
   return L;
 }
+
+// The adapter's last reduction folded into the GEMV (the slice partials of
+// X L1 summed in the kernel instead of a separate launch): P = [Z][M][r] fp32
+// slice partials, s the LoRA scale, T_out optional bf16(X L1) [M][r].
+struct FuseT {
+  const float* P;
+  int Z;
+  float s;
+  uint16_t* T_out;
+};
+constexpr int kFtSlices = 4;   // slices per wave, one 16-byte load per lane each (M r <= 256)
 
 template <int D, bool XL>
 struct GlSlot {
@@ -457,11 +470,11 @@ struct GlSlot {
   u32x4_t x[XL ? 1 : 2][2];        // X fragments (register path only)
 };
 
-template <int W, int D, bool XL>
+template <int W, int D, bool XL, bool FT>
 __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table tab, const uint16_t* __restrict__ X,
                                                           int M, const uint16_t* __restrict__ sT, int ldst,
                                                           const uint16_t* __restrict__ L2, int r,
-                                                          uint16_t* __restrict__ Y) {
+                                                          uint16_t* __restrict__ Y, FuseT ft) {
   static_assert(D % 4 == 0, "a round of D steps gives each lane D/4 (row, step) block-constant pairs");
   extern __shared__ __attribute__((aligned(16))) unsigned char gl_smem[];
   constexpr int kThreads = 64 * W;
@@ -474,7 +487,8 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
   const int K = (int)Wt.cols, N = (int)Wt.rows;
   const int n0 = (int)blockIdx.x * 16;
   const int nblk = K / kBlock;
-  const GlLayout L = gl_layout(K, W, D, XL ? M : 0);
+  const int mr = M * r;
+  const GlLayout L = gl_layout(K, W, D, XL ? M : 0, FT ? (uint32_t)(W * mr) * 4u : 0u);
   const int nsteps = nblk / 2;                   // K % 128 == 0
   const int mysteps = nsteps > wave ? (nsteps - wave + W - 1) / W : 0;
   const int row = lane & 15, grp = lane >> 4;
@@ -484,6 +498,20 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
   auto ld16 = [](const void* base, uint32_t off) { return *reinterpret_cast<const u32x4_t*>(static_cast<const char*>(base) + off); };
 
   // ---- loads, in the order they are needed: they complete in issue order ----
+  // Fused adapter reduction: the slice partials first (the prologue sums
+  // them before its barrier). Lane l reads the 16-byte chunk l of the [M][r]
+  // slab (M r <= 256) of slices z = wave, wave + W, ...; missing slices and
+  // chunks read offset 0 and are not used.
+  f32x4_t pz[FT ? kFtSlices : 1];
+  if constexpr (FT) {
+#pragma unroll
+    for (int i = 0; i < kFtSlices; ++i) {
+      const int z = wave + W * i;
+      const bool ok = z < ft.Z && 4 * lane < mr;
+      const uint32_t off = ok ? (__umul24((uint32_t)z, (uint32_t)mr) + 4u * (uint32_t)lane) * 4u : 0u;
+      pz[i] = *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const char*>(ft.P) + off);
+    }
+  }
   // LoRA operands for wave 0 (ranks <= 64; the term is added after the K loop):
   // A = L2[j][n0 + row], B = sT[row][j], rank chunks of 32. The prologue loads
   // are unconditional (addresses in bounds): a load under a branch makes the
@@ -500,7 +528,7 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       la[c][e] = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(L2) + o + (uint32_t)(e * N) * 2u);
-    lb[c] = ld16(sT, (__umul24((uint32_t)xm, (uint32_t)ldst) + (uint32_t)jb) * 2u);
+    if constexpr (!FT) lb[c] = ld16(sT, (__umul24((uint32_t)xm, (uint32_t)ldst) + (uint32_t)jb) * 2u);
   }
   // Block constants, one round of D steps ahead: lane l computes a' of row l%16
   // for the wave's steps base + l/16 + 4k (both 64-blocks of the step).
@@ -590,7 +618,7 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
   for (int c = 0; c < kLoraChunks; ++c) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(la[c][e]) :: "memory");
-    asm volatile("" : "+v"(lb[c]) :: "memory");
+    if constexpr (!FT) asm volatile("" : "+v"(lb[c]) :: "memory");
   }
 #pragma unroll
   for (int k = 0; k < kAPairs; ++k) asm volatile("" : "+v"(a16[k]), "+v"(sg0[k]), "+v"(sg1[k]) :: "memory");
@@ -607,7 +635,7 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
       const u32x4_t a = {la[c][0] | (la[c][1] << 16), la[c][2] | (la[c][3] << 16), la[c][4] | (la[c][5] << 16),
                          la[c][6] | (la[c][7] << 16)};
       lp[c * 128] = in ? a : z;
-      lp[c * 128 + 1] = in ? lb[c] : z;
+      if constexpr (!FT) lp[c * 128 + 1] = in ? lb[c] : z;
     }
   }
   if constexpr (XL) {  // the staged X rows (the launcher keeps them within one round of loads)
@@ -627,6 +655,17 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
       aw[(slot * 2 + 1) * 16 + row] = dq ? block_scale((a16[k] >> 8) & 0xFFu, sg1[k], mu) : sg1[k];
     }
   };
+  if constexpr (FT) {  // this wave's slices, summed in ascending order, for wave 0 after the K loop
+    f32x4_t v = pz[0];
+#pragma unroll
+    for (int i = 1; i < kFtSlices; ++i)
+      if (wave + W * i < ft.Z) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += pz[i][e];
+      }
+    if (4 * lane < mr && wave < ft.Z)
+      *reinterpret_cast<f32x4_t*>(gl_smem + L.q_off + (uint32_t)(wave * mr + 4 * lane) * 4u) = v;
+  }
   store_a();
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // table and X visible; code loads stay in flight
 
@@ -690,9 +729,42 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
     const u32x4_t* lp = reinterpret_cast<const u32x4_t*>(gl_smem + L.lora_off) + 2 * lane;
 #pragma unroll
     for (int c = 0; c < kLoraChunks; ++c) {
-      if (32 * c < rp)
+      if (32 * c < rp) {
+        u32x4_t b;
+        if constexpr (FT) {  // T[m][j0 .. j0+8] = the waves' sums added in order; B = bf16(s T)
+          const int j0 = 32 * c + 8 * grp;
+          const bool in = j0 < r;
+          const int nw = ft.Z < W ? ft.Z : W;
+          float v[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+          const unsigned char* qp = gl_smem + L.q_off + (uint32_t)(xm * r + (in ? j0 : 0)) * 4u;
+          for (int w = 0; w < nw; ++w) {
+            const f32x4_t t0 = *reinterpret_cast<const f32x4_t*>(qp + (uint32_t)(w * mr) * 4u);
+            const f32x4_t t1 = *reinterpret_cast<const f32x4_t*>(qp + (uint32_t)(w * mr) * 4u + 16u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[e] += t0[e];
+              v[4 + e] += t1[e];
+            }
+          }
+          uint32_t h[8], t[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            h[e] = f32_to_bf16(ft.s * v[e]);
+            t[e] = f32_to_bf16(v[e]);
+          }
+          const u32x4_t zb = {0u, 0u, 0u, 0u};
+          const u32x4_t hb = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+          b = in ? hb : zb;
+          if (ft.T_out != nullptr && blockIdx.x == 0 && row < M && in) {
+            const u32x4_t tb = {t[0] | (t[1] << 16), t[2] | (t[3] << 16), t[4] | (t[5] << 16), t[6] | (t[7] << 16)};
+            *reinterpret_cast<u32x4_t*>(ft.T_out + row * r + j0) = tb;
+          }
+        } else {
+          b = lp[c * 128 + 1];
+        }
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lp[c * 128]),
-                                                       __builtin_bit_cast(bf16x8_t, lp[c * 128 + 1]), acc, 0, 0, 0);
+                                                       __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+      }
     }
     for (int j0 = 32 * kLoraChunks; j0 < rp; j0 += 32) {  // ranks above 64
       const int jj = j0 + 8 * grp;
@@ -728,19 +800,73 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
   }
 }
 
-template <int W, int D, bool XL>
+template <int W, int D, bool XL, bool FT>
 hipError_t launch_lut(const NF4View& Wt, const NF4Table& tab, const uint16_t* X, int M, const uint16_t* sT,
-                      const uint16_t* L2, int r, uint16_t* Y, int64_t tiles, uint32_t lds, hipStream_t stream) {
+                      const uint16_t* L2, int r, uint16_t* Y, const FuseT& ft, int64_t tiles, uint32_t lds,
+                      hipStream_t stream) {
   static bool attr_set = false;  // raise the dynamic-LDS limit once per instantiation (idempotent)
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_lut_kernel<W, D, XL>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_lut_kernel<W, D, XL, FT>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGvMaxLds);
     (void)hipGetLastError();  // a refusal shows up as a launch error below
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemv_lut_kernel<W, D, XL>), dim3((unsigned)tiles), dim3(64 * W), lds, stream, Wt, tab, X, M, sT,
-                     r, L2, r, Y);
+  hipLaunchKernelGGL((gemv_lut_kernel<W, D, XL, FT>), dim3((unsigned)tiles), dim3(64 * W), lds, stream, Wt, tab, X, M,
+                     sT, r, L2, r, Y, ft);
   return hipGetLastError();
+}
+
+// The byte-table kernel's configuration for a shape: every workgroup of the
+// launch resident at once (LDS budget per workgroup = LDS per CU / workgroups
+// per CU), 4 waves when a CU holds three or more workgroups, else 8; X staged
+// in LDS when it fits. With fusion asked for, the adapter's slice partials
+// are summed in the kernel when M r <= 256, each wave has at most kFtSlices
+// slices and their per-wave sums fit the same budget. waves == 0: the kernel
+// does not apply.
+struct LutPlan {
+  int waves = 0;
+  bool xl = false, fuse = false;
+  uint32_t lds = 0;
+};
+
+// the small-M LoRA down projection's slices (its kernels are below)
+constexpr int kTsWaves = 16;
+constexpr int kTsRows = 32;                  // L1 rows per wave
+constexpr int kTsK = kTsWaves * kTsRows;     // k per slice
+
+LutPlan lut_plan(const NF4View& W, int64_t M, int r, bool want_fuse) {
+  LutPlan p;
+  const int64_t N = W.rows, K = W.cols;
+  const int64_t tiles = (N + kGvRows - 1) / kGvRows;
+  const bool fits32 = N < (1 << 24) && K < (1 << 24) && N * K / 2 < ((int64_t)1 << 32) &&
+                      M * K * 2 < ((int64_t)1 << 32) && (int64_t)r * N * 2 < ((int64_t)1 << 32);
+  if (K % 128 != 0 || !fits32) return p;  // 32-bit byte offsets and 24-bit products in the kernel
+  static int cus = 0;  // compute units of the device (the same on every device this library runs on)
+  if (cus <= 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      cus = n;
+    (void)hipGetLastError();
+    if (cus <= 0) cus = 256;
+  }
+  int64_t per_cu = (tiles + cus - 1) / cus;
+  if (per_cu > 4) per_cu = 4;
+  const uint32_t budget = (uint32_t)(160 * 1024 / per_cu) - 1024u;
+  const int waves = per_cu >= 3 ? 4 : 8;
+  const int m = (int)M;
+  const int64_t xchunks = M * K / 8;   // X staged by one round of kXPer (4) loads per thread
+  const GlLayout xl = gl_layout(K, waves, 4, m, 0u), xr = gl_layout(K, waves, 4, 0, 0u);
+  if (xl.total <= budget && xchunks <= 4 * 64 * waves) p.xl = true;
+  else if (xr.total > budget) return p;
+  p.waves = waves;
+  p.lds = p.xl ? xl.total : xr.total;
+  const int64_t Z = (K + kTsK - 1) / kTsK;
+  const uint32_t qb = (uint32_t)(waves * m * r) * 4u;
+  if (want_fuse && r <= 64 && M * r <= 256 && Z <= (int64_t)kFtSlices * waves && p.lds + qb <= budget) {
+    p.fuse = true;
+    p.lds += qb;
+  }
+  return p;
 }
 
 // ---- small-M LoRA down projection -------------------------------------------
@@ -754,9 +880,6 @@ hipError_t launch_lut(const NF4View& Wt, const NF4Table& tab, const uint16_t* X,
 //   * a fixed-order sum over the (K/512) slices that writes bf16(s T)
 //     for the second adapter product, and bf16(T) when asked.
 
-constexpr int kTsWaves = 16;
-constexpr int kTsRows = 32;                  // L1 rows per wave
-constexpr int kTsK = kTsWaves * kTsRows;     // k per slice
 
 __global__ __launch_bounds__(64 * kTsWaves) void small_t_partial_kernel(const uint16_t* __restrict__ X, int M,
                                                                         int64_t K, const uint16_t* __restrict__ L1,
@@ -833,52 +956,51 @@ size_t small_t_partial_bytes(int64_t M, int64_t K, int r) {
   return (size_t)((K + kTsK - 1) / kTsK) * (size_t)M * (size_t)r * 4;
 }
 
-hipError_t launch_small_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* L1, int r, float s,
-                                  uint16_t* sT, int64_t ldst, uint16_t* T_out, float* part, hipStream_t stream) {
+int small_t_slices(int64_t K) { return (int)((K + kTsK - 1) / kTsK); }
+
+hipError_t launch_small_t_partial(const uint16_t* X, int64_t M, int64_t K, const uint16_t* L1, int r, float* part,
+                                  hipStream_t stream) {
   if (M < 1 || M > 128) return hipErrorInvalidValue;
-  const int Z = (int)((K + kTsK - 1) / kTsK);
-  hipLaunchKernelGGL(small_t_partial_kernel, dim3((unsigned)Z, (unsigned)((r + 63) / 64), (unsigned)((M + 15) / 16)),
+  hipLaunchKernelGGL(small_t_partial_kernel,
+                     dim3((unsigned)small_t_slices(K), (unsigned)((r + 63) / 64), (unsigned)((M + 15) / 16)),
                      dim3(64 * kTsWaves), 0, stream, X, (int)M, K, L1, r, part);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(small_t_reduce_kernel, dim3((unsigned)((M * r + 255) / 256)), dim3(256), 0, stream, part, Z,
-                     (int)M, r, s, sT, ldst, T_out);
   return hipGetLastError();
 }
 
-hipError_t launch_gemv(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M,
-                       const uint16_t* sT, const uint16_t* L2, int r, uint16_t* Y, hipStream_t stream) {
+hipError_t launch_small_lora_down(const uint16_t* X, int64_t M, int64_t K, const uint16_t* L1, int r, float s,
+                                  uint16_t* sT, int64_t ldst, uint16_t* T_out, float* part, hipStream_t stream) {
+  hipError_t e = launch_small_t_partial(X, M, K, L1, r, part, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(small_t_reduce_kernel, dim3((unsigned)((M * r + 255) / 256)), dim3(256), 0, stream, part,
+                     small_t_slices(K), (int)M, r, s, sT, ldst, T_out);
+  return hipGetLastError();
+}
+
+bool gemv_fuses_t(const NF4View& W, int64_t M, int r) {
+  return M >= 1 && M <= 16 && r <= kGvMaxRank && W.cols % kBlock == 0 && lut_plan(W, M, r, true).fuse;
+}
+
+static hipError_t launch_gemv_impl(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M,
+                                   const uint16_t* sT, const uint16_t* L2, int r, uint16_t* Y, const FuseT* ft,
+                                   hipStream_t stream) {
   if (M < 1 || M > 16 || r > kGvMaxRank || (W.cols % kBlock) != 0) return hipErrorInvalidValue;
   const int64_t N = W.rows, K = W.cols;
   const int64_t tiles = (N + kGvRows - 1) / kGvRows;
   const int m = (int)M;
-  // byte-table kernel: every workgroup of the launch resident at once (LDS
-  // budget per workgroup = LDS per CU / workgroups per CU), 4 waves when a CU
-  // holds three or more workgroups, else 8; X staged in LDS when it fits
-  const bool fits32 = N < (1 << 24) && K < (1 << 24) && N * K / 2 < ((int64_t)1 << 32) &&
-                      (int64_t)m * K * 2 < ((int64_t)1 << 32) && (int64_t)r * N * 2 < ((int64_t)1 << 32);
-  if (K % 128 == 0 && fits32) {  // 32-bit byte offsets and 24-bit products in the kernel
-    static int cus = 0;  // compute units of the device (the same on every device this library runs on)
-    if (cus <= 0) {
-      int dev = 0, n = 0;
-      if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
-        cus = n;
-      (void)hipGetLastError();
-      if (cus <= 0) cus = 256;
+  const LutPlan p = lut_plan(W, M, r, ft != nullptr);
+  if (ft != nullptr && !p.fuse) return hipErrorInvalidValue;  // callers ask gemv_fuses_t first
+  if (p.waves > 0) {
+    const FuseT f = ft ? *ft : FuseT{nullptr, 0, 0.0f, nullptr};
+    if (p.waves == 4) {
+      if (p.fuse) return p.xl ? launch_lut<4, 4, true, true>(W, tab, X, m, sT, L2, r, Y, f, tiles, p.lds, stream)
+                              : launch_lut<4, 4, false, true>(W, tab, X, m, sT, L2, r, Y, f, tiles, p.lds, stream);
+      return p.xl ? launch_lut<4, 4, true, false>(W, tab, X, m, sT, L2, r, Y, f, tiles, p.lds, stream)
+                  : launch_lut<4, 4, false, false>(W, tab, X, m, sT, L2, r, Y, f, tiles, p.lds, stream);
     }
-    int64_t per_cu = (tiles + cus - 1) / cus;
-    if (per_cu > 4) per_cu = 4;
-    const uint32_t budget = (uint32_t)(160 * 1024 / per_cu) - 1024u;
-    const int64_t xchunks = M * K / 8;   // X staged by one round of kXPer loads per thread
-    if (per_cu >= 3) {
-      const GlLayout xl = gl_layout(K, 4, 4, m), xr = gl_layout(K, 4, 4, 0);
-      if (xl.total <= budget && xchunks <= 4 * 256) return launch_lut<4, 4, true>(W, tab, X, m, sT, L2, r, Y, tiles, xl.total, stream);
-      if (xr.total <= budget) return launch_lut<4, 4, false>(W, tab, X, m, sT, L2, r, Y, tiles, xr.total, stream);
-    } else {
-      const GlLayout xl = gl_layout(K, 8, 4, m), xr = gl_layout(K, 8, 4, 0);
-      if (xl.total <= budget && xchunks <= 4 * 512) return launch_lut<8, 4, true>(W, tab, X, m, sT, L2, r, Y, tiles, xl.total, stream);
-      if (xr.total <= budget) return launch_lut<8, 4, false>(W, tab, X, m, sT, L2, r, Y, tiles, xr.total, stream);
-    }
+    if (p.fuse) return p.xl ? launch_lut<8, 4, true, true>(W, tab, X, m, sT, L2, r, Y, f, tiles, p.lds, stream)
+                            : launch_lut<8, 4, false, true>(W, tab, X, m, sT, L2, r, Y, f, tiles, p.lds, stream);
+    return p.xl ? launch_lut<8, 4, true, false>(W, tab, X, m, sT, L2, r, Y, f, tiles, p.lds, stream)
+                : launch_lut<8, 4, false, false>(W, tab, X, m, sT, L2, r, Y, f, tiles, p.lds, stream);
   }
   // streamed kernel (double quantisation only): 4 waves when there are
   // enough row tiles for two or more workgroups per CU, else 8
@@ -901,6 +1023,18 @@ hipError_t launch_gemv(const NF4View& W, const NF4Table& tab, const uint16_t* X,
   else
     hipLaunchKernelGGL(gemv_ring_kernel<8>, dim3((unsigned)tiles), dim3(512), 0, stream, W, tab, X, m, sT, r, L2, r, Y);
   return hipGetLastError();
+}
+
+hipError_t launch_gemv(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M,
+                       const uint16_t* sT, const uint16_t* L2, int r, uint16_t* Y, hipStream_t stream) {
+  return launch_gemv_impl(W, tab, X, M, sT, L2, r, Y, nullptr, stream);
+}
+
+hipError_t launch_gemv_fused_t(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M,
+                               const float* part, int Z, float s, uint16_t* T_out, const uint16_t* L2, int r,
+                               uint16_t* Y, hipStream_t stream) {
+  const FuseT ft{part, Z, s, T_out};
+  return launch_gemv_impl(W, tab, X, M, nullptr, L2, r, Y, &ft, stream);
 }
 
 }  // namespace qlora

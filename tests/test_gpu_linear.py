@@ -86,6 +86,12 @@ def test_tiny_512(api):
     # forward (K = 12352) here, and dX (over N = 12352) in the next case
     (300, 64 * 193, 200, 16, 0.5, "normal"),
     (300, 256, 64 * 193, 16, 0.25, "student-t4"),
+    # decode sizes (M r <= 256): the adapter's slice sums inside the GEMV, T
+    # written by it for the backward. 6 slices (the last one partial) over 8
+    # waves with X staged; 19 slices, up to 3 per wave; 4-wave workgroups
+    (4, 64 * 41, 200, 64, 0.5, "normal"),
+    (3, 64 * 151, 40, 64, 0.25, "student-t4"),
+    (4, 64 * 35, 8200, 64, 0.5, "normal"),
 ])
 def test_shapes(api, M, K, N, r, s, kind):
     say(f"linear M={M} K={K} N={N} r={r} s={s} {kind}")
