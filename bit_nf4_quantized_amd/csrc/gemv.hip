@@ -24,6 +24,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace qlora {
 
 namespace {
@@ -431,6 +433,12 @@ bool launch_streamed(const NF4View& Wt, const NF4Table& tab, const uint16_t* X, 
 // the table and the staged X. The LoRA term (operands loaded first) is added
 // by wave 0 after its K loop, and the waves' partial sums are added in a
 // fixed order through LDS.
+// Fused variants (FT > 0) also take over the last step of the adapter's down
+// projection: instead of reading bf16(s T) written by a separate reduction,
+// each wave loads the K-slice partials of T = X L1 of its slices first in the
+// prologue, sums them in slice order and leaves the sums in LDS before the
+// barrier; after the K loop wave 0 adds the waves' sums in wave order, rounds
+// bf16(s T) for its MFMA operand, and workgroup 0 writes bf16(T) when asked.
 
 constexpr int kLutCopies = 32;
 constexpr uint32_t kLutBytes = 256u * kLutCopies * 4u;   // 32 KB
@@ -445,7 +453,9 @@ __host__ __device__ inline GlLayout gl_layout(int64_t K, int waves, int depth, i
   GlLayout L;
   uint32_t off = kLutBytes;                      // the table; partial sums reuse it at the end
   L.a_off = off; off += (uint32_t)(waves * depth) * 128u;  // per wave: a' [slot][block][16 rows] fp32
-  L.lora_off = off; off += 2u * 64u * 32u;       // wave 0's packed LoRA fragments, 2 rank chunks x 64 lanes x 32 B
+  // wave 0's packed LoRA fragments: the L2 operand [2 rank chunks][64 lanes]
+  // x 16 B, then (unless fused) the sT operand in the same layout
+  L.lora_off = off; off += q_bytes ? 2048u : 4096u;
   L.xpitch = (uint32_t)K * 2u;                   // X rows back to back (staged only for M <= 2 in practice)
   L.x_off = off; off += (uint32_t)mx_lds * L.xpitch;
   L.q_off = off; off += q_bytes;                 // [wave][M r] fp32
@@ -462,7 +472,10 @@ struct FuseT {
   float s;
   uint16_t* T_out;
 };
-constexpr int kFtSlices = 4;   // slices per wave, one 16-byte load per lane each (M r <= 256)
+// Fused variants FT = F: lane l loads the 16-byte chunks f 64 + l (f < F)
+// of each of its wave's slices, so M r <= 256 F; a wave takes at most
+// ft_slices(F) slices (the loads stay within 12 registers of 16 bytes).
+constexpr int ft_slices(int F) { return F == 1 ? 4 : 12 / F; }
 
 template <int D, bool XL>
 struct GlSlot {
@@ -470,7 +483,7 @@ struct GlSlot {
   u32x4_t x[XL ? 1 : 2][2];        // X fragments (register path only)
 };
 
-template <int W, int D, bool XL, bool FT>
+template <int W, int D, bool XL, int FT>
 __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table tab, const uint16_t* __restrict__ X,
                                                           int M, const uint16_t* __restrict__ sT, int ldst,
                                                           const uint16_t* __restrict__ L2, int r,
@@ -499,18 +512,21 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
 
   // ---- loads, in the order they are needed: they complete in issue order ----
   // Fused adapter reduction: the slice partials first (the prologue sums
-  // them before its barrier). Lane l reads the 16-byte chunk l of the [M][r]
-  // slab (M r <= 256) of slices z = wave, wave + W, ...; missing slices and
-  // chunks read offset 0 and are not used.
-  f32x4_t pz[FT ? kFtSlices : 1];
-  if constexpr (FT) {
+  // them before its barrier). Lane l reads the 16-byte chunks f 64 + l of the
+  // [M][r] slab of slices z = wave, wave + W, ...; missing slices and chunks
+  // read offset 0 and are not used.
+  constexpr int kSl = FT ? ft_slices(FT) : 1;
+  f32x4_t pz[FT ? kSl * FT : 1];
+  if constexpr (FT > 0) {
 #pragma unroll
-    for (int i = 0; i < kFtSlices; ++i) {
-      const int z = wave + W * i;
-      const bool ok = z < ft.Z && 4 * lane < mr;
-      const uint32_t off = ok ? (__umul24((uint32_t)z, (uint32_t)mr) + 4u * (uint32_t)lane) * 4u : 0u;
-      pz[i] = *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const char*>(ft.P) + off);
-    }
+    for (int i = 0; i < kSl; ++i)
+#pragma unroll
+      for (int f = 0; f < FT; ++f) {
+        const int z = wave + W * i, q = 4 * (64 * f + lane);
+        const bool ok = z < ft.Z && q < mr;
+        const uint32_t off = ok ? (__umul24((uint32_t)z, (uint32_t)mr) + (uint32_t)q) * 4u : 0u;
+        pz[i * FT + f] = *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const char*>(ft.P) + off);
+      }
   }
   // LoRA operands for wave 0 (ranks <= 64; the term is added after the K loop):
   // A = L2[j][n0 + row], B = sT[row][j], rank chunks of 32. The prologue loads
@@ -528,7 +544,7 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       la[c][e] = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(L2) + o + (uint32_t)(e * N) * 2u);
-    if constexpr (!FT) lb[c] = ld16(sT, (__umul24((uint32_t)xm, (uint32_t)ldst) + (uint32_t)jb) * 2u);
+    if constexpr (FT == 0) lb[c] = ld16(sT, (__umul24((uint32_t)xm, (uint32_t)ldst) + (uint32_t)jb) * 2u);
   }
   // Block constants, one round of D steps ahead: lane l computes a' of row l%16
   // for the wave's steps base + l/16 + 4k (both 64-blocks of the step).
@@ -618,7 +634,7 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
   for (int c = 0; c < kLoraChunks; ++c) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(la[c][e]) :: "memory");
-    if constexpr (!FT) asm volatile("" : "+v"(lb[c]) :: "memory");
+    if constexpr (FT == 0) asm volatile("" : "+v"(lb[c]) :: "memory");
   }
 #pragma unroll
   for (int k = 0; k < kAPairs; ++k) asm volatile("" : "+v"(a16[k]), "+v"(sg0[k]), "+v"(sg1[k]) :: "memory");
@@ -627,15 +643,15 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
     for (int u = 0; u < kXPer; ++u) asm volatile("" : "+v"(xv[u]) :: "memory");
   }
   if (wave == 0) {  // packed LoRA fragments, read back by the same lanes after the K loop
-    u32x4_t* lp = reinterpret_cast<u32x4_t*>(gl_smem + L.lora_off) + 2 * lane;
+    u32x4_t* lp = reinterpret_cast<u32x4_t*>(gl_smem + L.lora_off) + lane;
 #pragma unroll
     for (int c = 0; c < kLoraChunks; ++c) {
       const bool in = 32 * c + 8 * grp < r;
       const u32x4_t z = {0u, 0u, 0u, 0u};
       const u32x4_t a = {la[c][0] | (la[c][1] << 16), la[c][2] | (la[c][3] << 16), la[c][4] | (la[c][5] << 16),
                          la[c][6] | (la[c][7] << 16)};
-      lp[c * 128] = in ? a : z;
-      if constexpr (!FT) lp[c * 128 + 1] = in ? lb[c] : z;
+      lp[c * 64] = in ? a : z;
+      if constexpr (FT == 0) lp[128 + c * 64] = in ? lb[c] : z;
     }
   }
   if constexpr (XL) {  // the staged X rows (the launcher keeps them within one round of loads)
@@ -655,16 +671,19 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
       aw[(slot * 2 + 1) * 16 + row] = dq ? block_scale((a16[k] >> 8) & 0xFFu, sg1[k], mu) : sg1[k];
     }
   };
-  if constexpr (FT) {  // this wave's slices, summed in ascending order, for wave 0 after the K loop
-    f32x4_t v = pz[0];
+  if constexpr (FT > 0) {  // this wave's slices, summed in ascending order, for wave 0 after the K loop
 #pragma unroll
-    for (int i = 1; i < kFtSlices; ++i)
-      if (wave + W * i < ft.Z) {
+    for (int f = 0; f < FT; ++f) {
+      f32x4_t v = pz[f];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] += pz[i][e];
-      }
-    if (4 * lane < mr && wave < ft.Z)
-      *reinterpret_cast<f32x4_t*>(gl_smem + L.q_off + (uint32_t)(wave * mr + 4 * lane) * 4u) = v;
+      for (int i = 1; i < kSl; ++i)
+        if (wave + W * i < ft.Z) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] += pz[i * FT + f][e];
+        }
+      const int q = 4 * (64 * f + lane);
+      if (q < mr && wave < ft.Z) *reinterpret_cast<f32x4_t*>(gl_smem + L.q_off + (uint32_t)(wave * mr + q) * 4u) = v;
+    }
   }
   store_a();
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // table and X visible; code loads stay in flight
@@ -726,12 +745,12 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
 
   // ---- LoRA term (wave 0): acc += sum_j L2[j][n] sT[m][j] ----
   if (wave == 0) {
-    const u32x4_t* lp = reinterpret_cast<const u32x4_t*>(gl_smem + L.lora_off) + 2 * lane;
+    const u32x4_t* lp = reinterpret_cast<const u32x4_t*>(gl_smem + L.lora_off) + lane;
 #pragma unroll
     for (int c = 0; c < kLoraChunks; ++c) {
       if (32 * c < rp) {
         u32x4_t b;
-        if constexpr (FT) {  // T[m][j0 .. j0+8] = the waves' sums added in order; B = bf16(s T)
+        if constexpr (FT > 0) {  // T[m][j0 .. j0+8] = the waves' sums added in order; B = bf16(s T)
           const int j0 = 32 * c + 8 * grp;
           const bool in = j0 < r;
           const int nw = ft.Z < W ? ft.Z : W;
@@ -760,9 +779,9 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
             *reinterpret_cast<u32x4_t*>(ft.T_out + row * r + j0) = tb;
           }
         } else {
-          b = lp[c * 128 + 1];
+          b = lp[128 + c * 64];
         }
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lp[c * 128]),
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, lp[c * 64]),
                                                        __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
       }
     }
@@ -800,7 +819,7 @@ __global__ __launch_bounds__(64 * W) void gemv_lut_kernel(NF4View Wt, NF4Table t
   }
 }
 
-template <int W, int D, bool XL, bool FT>
+template <int W, int D, bool XL, int FT>
 hipError_t launch_lut(const NF4View& Wt, const NF4Table& tab, const uint16_t* X, int M, const uint16_t* sT,
                       const uint16_t* L2, int r, uint16_t* Y, const FuseT& ft, int64_t tiles, uint32_t lds,
                       hipStream_t stream) {
@@ -820,12 +839,14 @@ hipError_t launch_lut(const NF4View& Wt, const NF4Table& tab, const uint16_t* X,
 // launch resident at once (LDS budget per workgroup = LDS per CU / workgroups
 // per CU), 4 waves when a CU holds three or more workgroups, else 8; X staged
 // in LDS when it fits. With fusion asked for, the adapter's slice partials
-// are summed in the kernel when M r <= 256, each wave has at most kFtSlices
-// slices and their per-wave sums fit the same budget. waves == 0: the kernel
-// does not apply.
+// are summed in the kernel (fuse = F of the fused variant) when r <= 64,
+// M r <= 256 F (F = 1, or 4 with 8-wave workgroups), each wave has at most
+// ft_slices(F) slices and their per-wave sums fit the same budget. waves == 0: the kernel does not
+// apply.
 struct LutPlan {
   int waves = 0;
-  bool xl = false, fuse = false;
+  bool xl = false;
+  int fuse = 0;
   uint32_t lds = 0;
 };
 
@@ -861,10 +882,17 @@ LutPlan lut_plan(const NF4View& W, int64_t M, int r, bool want_fuse) {
   p.waves = waves;
   p.lds = p.xl ? xl.total : xr.total;
   const int64_t Z = (K + kTsK - 1) / kTsK;
-  const uint32_t qb = (uint32_t)(waves * m * r) * 4u;
-  if (want_fuse && r <= 64 && M * r <= 256 && Z <= (int64_t)kFtSlices * waves && p.lds + qb <= budget) {
-    p.fuse = true;
-    p.lds += qb;
+  // four chunks per lane only with one workgroup per CU: with 4-wave
+  // workgroups (more tiles than two per CU) their longer prologue cost more
+  // than the separate reduction saves (LLaMA-7B 4096 -> 11008, M = 16: 26.0
+  // against 25.6 us per call; 11008 -> 4096: 22.9 against 25.5)
+  const int F = M * r <= 256 ? 1 : (M * r <= 1024 && waves == 8) ? 4 : 0;
+  if (want_fuse && r <= 64 && F > 0 && Z <= (int64_t)ft_slices(F) * waves) {
+    const uint32_t lf = gl_layout(K, waves, 4, p.xl ? m : 0, (uint32_t)(waves * m * r) * 4u).total;
+    if (lf <= budget) {
+      p.fuse = F;
+      p.lds = lf;
+    }
   }
   return p;
 }
@@ -977,7 +1005,7 @@ hipError_t launch_small_lora_down(const uint16_t* X, int64_t M, int64_t K, const
 }
 
 bool gemv_fuses_t(const NF4View& W, int64_t M, int r) {
-  return M >= 1 && M <= 16 && r <= kGvMaxRank && W.cols % kBlock == 0 && lut_plan(W, M, r, true).fuse;
+  return M >= 1 && M <= 16 && r <= kGvMaxRank && W.cols % kBlock == 0 && lut_plan(W, M, r, true).fuse > 0;
 }
 
 static hipError_t launch_gemv_impl(const NF4View& W, const NF4Table& tab, const uint16_t* X, int64_t M,
@@ -988,19 +1016,23 @@ static hipError_t launch_gemv_impl(const NF4View& W, const NF4Table& tab, const 
   const int64_t tiles = (N + kGvRows - 1) / kGvRows;
   const int m = (int)M;
   const LutPlan p = lut_plan(W, M, r, ft != nullptr);
-  if (ft != nullptr && !p.fuse) return hipErrorInvalidValue;  // callers ask gemv_fuses_t first
+  if (ft != nullptr && p.fuse == 0) return hipErrorInvalidValue;  // callers ask gemv_fuses_t first
   if (p.waves > 0) {
     const FuseT f = ft ? *ft : FuseT{nullptr, 0, 0.0f, nullptr};
-    if (p.waves == 4) {
-      if (p.fuse) return p.xl ? launch_lut<4, 4, true, true>(W, tab, X, m, sT, L2, r, Y, f, tiles, p.lds, stream)
-                              : launch_lut<4, 4, false, true>(W, tab, X, m, sT, L2, r, Y, f, tiles, p.lds, stream);
-      return p.xl ? launch_lut<4, 4, true, false>(W, tab, X, m, sT, L2, r, Y, f, tiles, p.lds, stream)
-                  : launch_lut<4, 4, false, false>(W, tab, X, m, sT, L2, r, Y, f, tiles, p.lds, stream);
-    }
-    if (p.fuse) return p.xl ? launch_lut<8, 4, true, true>(W, tab, X, m, sT, L2, r, Y, f, tiles, p.lds, stream)
-                            : launch_lut<8, 4, false, true>(W, tab, X, m, sT, L2, r, Y, f, tiles, p.lds, stream);
-    return p.xl ? launch_lut<8, 4, true, false>(W, tab, X, m, sT, L2, r, Y, f, tiles, p.lds, stream)
-                : launch_lut<8, 4, false, false>(W, tab, X, m, sT, L2, r, Y, f, tiles, p.lds, stream);
+    const int F = ft ? p.fuse : 0;
+    auto go = [&](auto w, auto xl) -> hipError_t {
+      constexpr int kW = decltype(w)::value;
+      constexpr bool kXL = decltype(xl)::value;
+      if (F == 1) return launch_lut<kW, 4, kXL, 1>(W, tab, X, m, sT, L2, r, Y, f, tiles, p.lds, stream);
+      if (F == 4) return launch_lut<kW, 4, kXL, 4>(W, tab, X, m, sT, L2, r, Y, f, tiles, p.lds, stream);
+      return launch_lut<kW, 4, kXL, 0>(W, tab, X, m, sT, L2, r, Y, f, tiles, p.lds, stream);
+    };
+    using I4 = std::integral_constant<int, 4>;
+    using I8 = std::integral_constant<int, 8>;
+    using T = std::true_type;
+    using Fa = std::false_type;
+    if (p.waves == 4) return p.xl ? go(I4{}, T{}) : go(I4{}, Fa{});
+    return p.xl ? go(I8{}, T{}) : go(I8{}, Fa{});
   }
   // streamed kernel (double quantisation only): 4 waves when there are
   // enough row tiles for two or more workgroups per CU, else 8

@@ -217,9 +217,10 @@ hipError_t launch_mfma_probe(int workgroups, int iters, float* sink, unsigned lo
 size_t read_probe_granule();
 hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t never, uint32_t* sink, hipStream_t stream);
 
-// Decode-path forward (M <= 16): bf16(s Xa L1) into sT ([M][r]) from the
-// K-slice partials in part, then the dequant-GEMV with the LoRA term. Xa is
-// the adapter branch's input (X, or its dropped copy).
+// Decode-path forward (M <= 16): the K-slice partials of Xa L1 into part,
+// then the dequant-GEMV with the LoRA term; bf16(s Xa L1) goes through sT
+// ([M][r]) from a separate reduction unless the GEMV sums the partials
+// itself. Xa is the adapter branch's input (X, or its dropped copy).
 hipError_t linear_forward_small(const NF4View& W, const NF4Table& tab, const uint16_t* X, const uint16_t* Xa,
                                 int64_t M, const uint16_t* L1, const uint16_t* L2, int r, float s, uint16_t* Y,
                                 uint16_t* T_out, uint16_t* sT, float* part, hipStream_t stream);

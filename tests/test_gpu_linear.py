@@ -92,6 +92,12 @@ def test_tiny_512(api):
     (4, 64 * 41, 200, 64, 0.5, "normal"),
     (3, 64 * 151, 40, 64, 0.25, "student-t4"),
     (4, 64 * 35, 8200, 64, 0.5, "normal"),
+    # M r <= 1024: four 16-byte chunks of each slice per lane. 6 slices;
+    # 24 slices, 3 per wave (the most a wave takes); 25 slices (one more than
+    # 8 waves take: the separate reduction)
+    (16, 64 * 45, 136, 64, 0.25, "normal"),
+    (12, 64 * 192, 64, 32, 0.5, "student-t4"),
+    (12, 64 * 194, 64, 32, 0.5, "normal"),
 ])
 def test_shapes(api, M, K, N, r, s, kind):
     say(f"linear M={M} K={K} N={N} r={r} s={s} {kind}")
