@@ -733,7 +733,9 @@ def bench_quantize_pass(api, workloads, layers=80, pool=2, oracle_layer=True):
     + DQ from fp32 and from bf16. The inputs are a pool of ``pool`` distinct
     layers (host-drawn, N(0, 0.015)), cycled so that every layer writes its
     own output set (codes, absmax8, scale2, mean); the whole pass is timed
-    with HIP events. GB/s = (input + output bytes) / time. The oracle
+    with HIP events, once with one qlora_quantize_batch call per layer (the
+    reported figure) and once with one qlora_quantize call per tensor.
+    GB/s = (input + output bytes) / time. The oracle
     quantises one layer (fp32 input) on the host cores; the pass estimate is
     that time x 80."""
     import torch
@@ -754,27 +756,43 @@ def bench_quantize_pass(api, workloads, layers=80, pool=2, oracle_layer=True):
         pool32.append([torch.from_numpy(workloads.quantize_weight(sh, 4, 7 * li + i)).cuda()
                        for i, sh in enumerate(shapes)])
         log(f"65B pass: pool layer {li} drawn")
-    for dt in ("f32", "bf16"):
-        src = pool32 if dt == "f32" else [[w.to(torch.bfloat16) for w in lay] for lay in pool32]
-        for i, w in enumerate(src[0]):      # warm-up of every shape
-            api.qlora_quantize(w, out=outs[0][i], workspace=ws)
+    ws_b = torch.empty(api.qlora_quant_batch_workspace([(sh.N, sh.K) for sh in shapes]), dtype=torch.uint8,
+                       device="cuda")
+
+    def timed_pass(src, batched):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
         for layer in range(layers):
-            for i, w in enumerate(src[layer % pool]):
-                api.qlora_quantize(w, out=outs[layer][i], workspace=ws)
+            if batched:     # one call per layer: its 7 tensors share the launches
+                api.qlora_quantize_batch(src[layer % pool], outs=outs[layer], workspace=ws_b)
+            else:
+                for i, w in enumerate(src[layer % pool]):
+                    api.qlora_quantize(w, out=outs[layer][i], workspace=ws)
         e1.record()
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
+        return e0.elapsed_time(e1)
+
+    for dt in ("f32", "bf16"):
+        src = pool32 if dt == "f32" else [[w.to(torch.bfloat16) for w in lay] for lay in pool32]
+        for i, w in enumerate(src[0]):      # warm-up of every shape, both call forms
+            api.qlora_quantize(w, out=outs[0][i], workspace=ws)
+        api.qlora_quantize_batch(src[0], outs=outs[0], workspace=ws_b)
+        ms_single = timed_pass(src, False)
+        ms = timed_pass(src, True)
         in_bytes = numel * (4 if dt == "f32" else 2)
         gbps = (in_bytes + out_bytes) / (ms * 1e-3) / 1e9
+        gbps_single = (in_bytes + out_bytes) / (ms_single * 1e-3) / 1e9
         res[dt] = {"ms": ms, "input_bytes": in_bytes, "GBps": gbps, "frac_of_hbm_peak": gbps / PEAK_HBM_GBPS,
-                   "roofline_ms": (in_bytes + out_bytes) / (PEAK_HBM_GBPS * 1e9) * 1e3}
-        log(f"65B pass from {dt}: {ms:.1f} ms for {layers * len(shapes)} tensors, {gbps:.0f} GB/s")
+                   "roofline_ms": (in_bytes + out_bytes) / (PEAK_HBM_GBPS * 1e9) * 1e3,
+                   "calls": "qlora_quantize_batch, one per layer (7 tensors)",
+                   "per_tensor_calls": {"ms": ms_single, "GBps": gbps_single,
+                                        "frac_of_hbm_peak": gbps_single / PEAK_HBM_GBPS}}
+        log(f"65B pass from {dt}: {ms:.1f} ms for {layers * len(shapes)} tensors, {gbps:.0f} GB/s "
+            f"(one call per layer; one call per tensor: {ms_single:.1f} ms, {gbps_single:.0f} GB/s)")
         if dt == "bf16":
             del src
-    del outs, ws
+    del outs, ws, ws_b
     if oracle_layer:
         from oracle import nf4
 
@@ -802,7 +820,7 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=["llama7b-layer", "llama33b-layer"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="only the headline step")
-    ap.add_argument("--only", choices=["gemv", "mid_m", "merge", "quantize", "attainable"],
+    ap.add_argument("--only", choices=["gemv", "mid_m", "merge", "quantize", "quantize_pass", "attainable"],
                     help="run one extra section alone and print its JSON (for profiling)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (calibration of the HBM byte counters)")
@@ -827,6 +845,7 @@ def main():
     if args.only:
         fn = {"gemv": lambda: bench_gemv(api, workloads), "mid_m": lambda: bench_mid_m(api, workloads),
               "merge": lambda: bench_merge(api, workloads), "quantize": lambda: bench_quantize(api, workloads),
+              "quantize_pass": lambda: bench_quantize_pass(api, workloads, oracle_layer=False),
               "attainable": lambda: attainable_peaks(api)}[args.only]
         print(json.dumps({args.only: fn()}), flush=True)
         return

@@ -40,8 +40,10 @@ EXPORTS = (
     "qlora_merge_adapters", "qlora_linear_workspace_dropout", "qlora_linear_fwd_dropout",
     "qlora_linear_bwd_dropout", "qlora_lora_dropout", "qlora_clip_grad_norm", "qlora_adam_step",
     "qlora_linear_fwd_noalloc", "qlora_check_conversions", "qlora_probe_mfma", "qlora_probe_read",
+    "qlora_quantize_batch", "qlora_quant_batch_workspace",
 )
 QLORA_NOALLOC_SCRATCH_BYTES = (2 << 20) + (64 << 10)
+QLORA_QUANT_BATCH_MAX = 16
 QLORA_CLIP_WORKSPACE_BYTES = 8192
 
 
@@ -121,6 +123,10 @@ def _load():
     lib.qlora_linear_fwd_noalloc.restype = ctypes.c_int
     lib.qlora_set_timing.argtypes = [ctypes.c_int, vp, vp, ctypes.c_int, P(ctypes.c_int)]
     lib.qlora_set_timing.restype = ctypes.c_int
+    lib.qlora_quantize_batch.argtypes = [ctypes.c_int, P(vp), ctypes.c_int, P(P(QNF4)), vp, sz, vp]
+    lib.qlora_quantize_batch.restype = ctypes.c_int
+    lib.qlora_quant_batch_workspace.argtypes = [ctypes.c_int, P(i64), P(i64), P(sz)]
+    lib.qlora_quant_batch_workspace.restype = ctypes.c_int
     u64 = ctypes.c_uint64
     lib.qlora_clip_grad_norm.argtypes = [vp, i64, ctypes.c_float, vp, vp, vp, sz, vp]
     lib.qlora_clip_grad_norm.restype = ctypes.c_int
@@ -240,6 +246,16 @@ def qlora_quant_sizes(rows: int, cols: int) -> dict:
     _check(_load().qlora_quant_sizes(rows, cols, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c),
                                      ctypes.byref(d)), "qlora_quant_sizes")
     return {"codes": a.value, "absmax8": b.value, "scale2": c.value, "workspace": d.value}
+
+
+def qlora_quant_batch_workspace(shapes) -> int:
+    """Scratch bytes of qlora_quantize_batch for a list of (rows, cols)."""
+    n = len(shapes)
+    rows = (ctypes.c_int64 * max(n, 1))(*[int(a) for a, _ in shapes])
+    cols = (ctypes.c_int64 * max(n, 1))(*[int(b) for _, b in shapes])
+    out = ctypes.c_size_t()
+    _check(_load().qlora_quant_batch_workspace(n, rows, cols, ctypes.byref(out)), "qlora_quant_batch_workspace")
+    return out.value
 
 
 def qlora_linear_workspace(M: int, K: int, N: int, r: int) -> int:
@@ -478,6 +494,38 @@ def qlora_quantize(W, out: NF4Tensor | None = None, workspace=None, stream=None,
     _check(_load().qlora_quantize(_ptr(W), dt, ctypes.byref(st), _ptr(ws), ws.numel() * ws.element_size(),
                                   _stream(stream)), "qlora_quantize")
     return q
+
+
+@_on_stream
+def qlora_quantize_batch(Ws, outs=None, workspace=None, stream=None, qtype: str | int = "nf4",
+                         double_quant: bool = True) -> list:
+    """qlora_quantize of several [rows][cols] device tensors (all fp32 or all
+    bf16) in one pass; returns their NF4Tensors (``outs`` keep their own
+    settings)."""
+    import torch
+
+    Ws = list(Ws)
+    n = len(Ws)
+    if not 1 <= n <= QLORA_QUANT_BATCH_MAX:
+        raise ValueError(f"1 to {QLORA_QUANT_BATCH_MAX} tensors per call")
+    dt = {torch.float32: QLORA_F32, torch.bfloat16: QLORA_BF16}.get(Ws[0].dtype)
+    if dt is None or any(W.dtype != Ws[0].dtype for W in Ws):
+        raise TypeError("all tensors float32 or all bfloat16")
+    for W in Ws:
+        if W.dim() != 2:
+            raise ValueError("each W must be 2-D [rows][cols]")
+        _need(W, W.dtype, tuple(W.shape), "W")
+    qs = list(outs) if outs is not None else [NF4Tensor.empty(W.shape[0], W.shape[1], W.device, qtype, double_quant)
+                                              for W in Ws]
+    if len(qs) != n:
+        raise ValueError("one output per tensor")
+    ws = _workspace(qlora_quant_batch_workspace([tuple(W.shape) for W in Ws]), Ws[0].device, workspace)
+    structs = [q.struct() for q in qs]
+    sp = (ctypes.POINTER(QNF4) * n)(*[ctypes.pointer(st) for st in structs])
+    wp = (ctypes.c_void_p * n)(*[W.data_ptr() for W in Ws])
+    _check(_load().qlora_quantize_batch(n, wp, dt, sp, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "qlora_quantize_batch")
+    return qs
 
 
 @_on_stream

@@ -219,6 +219,67 @@ int qlora_quantize(const void* W, qlora_dtype in_dtype, const qlora_nf4* q, void
   return e == hipSuccess ? QLORA_OK : hip_fail(e);
 }
 
+// Byte offset of tensor k's scratch in a batch workspace (each part rounded
+// up to 256); k = n gives the total.
+static size_t batch_ws_offset(int k, const int64_t* numel) {
+  size_t off = 0;
+  for (int j = 0; j < k; ++j) off += qlora::align_up(qlora::quant_workspace_layout(numel[j]).total, 256);
+  return off;
+}
+
+// rows/cols -> numel with the single-tensor shape rules; QLORA_OK or an error.
+static int batch_numel(int64_t rows, int64_t cols, int64_t* numel) {
+  if (rows < 0 || cols < 0) return QLORA_ERR_SHAPE;
+  if (cols > 0 && rows > INT64_MAX / 2 / cols) return QLORA_ERR_SHAPE;
+  *numel = rows * cols;
+  if ((*numel + QLORA_BLOCK * QLORA_DQ_BLOCK - 1) / (QLORA_BLOCK * QLORA_DQ_BLOCK) > 0x7FFFFFFF)
+    return QLORA_ERR_SHAPE;
+  return QLORA_OK;
+}
+
+int qlora_quant_batch_workspace(int n, const int64_t* rows, const int64_t* cols, size_t* bytes) {
+  if (n < 1 || n > QLORA_QUANT_BATCH_MAX || !rows || !cols || !bytes) return QLORA_ERR_ARG;
+  int64_t numel[QLORA_QUANT_BATCH_MAX];
+  for (int k = 0; k < n; ++k) {
+    const int st = batch_numel(rows[k], cols[k], &numel[k]);
+    if (st != QLORA_OK) return st;
+  }
+  *bytes = batch_ws_offset(n, numel);
+  return QLORA_OK;
+}
+
+int qlora_quantize_batch(int n, const void* const* W, qlora_dtype in_dtype, const qlora_nf4* const* q, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  if (n < 1 || n > QLORA_QUANT_BATCH_MAX || !W || !q) return QLORA_ERR_ARG;
+  if (in_dtype != QLORA_F32 && in_dtype != QLORA_BF16) return QLORA_ERR_ARG;
+  int64_t numel[QLORA_QUANT_BATCH_MAX];
+  int first = -1;                                // the first non-empty tensor
+  for (int k = 0; k < n; ++k) {
+    if (!q[k]) return QLORA_ERR_ARG;
+    const int st = batch_numel(q[k]->rows, q[k]->cols, &numel[k]);
+    if (st != QLORA_OK) return st;
+    if (numel[k] == 0) continue;
+    if (!W[k] || !valid_nf4(q[k])) return QLORA_ERR_ARG;
+    if (first < 0) first = k;
+    if (q[k]->qtype != q[first]->qtype) return QLORA_ERR_ARG;     // one threshold table per launch
+    if (!aligned16(W[k]) || !aligned16(q[k]->codes)) return QLORA_ERR_ALIGN;
+  }
+  if (first < 0) return QLORA_OK;                // nothing to quantise
+  if (!ws) return QLORA_ERR_ARG;
+  if (!aligned16(ws)) return QLORA_ERR_ALIGN;
+  if (ws_bytes < batch_ws_offset(n, numel)) return QLORA_ERR_WORKSPACE;
+  qlora::QuantItem items[QLORA_QUANT_BATCH_MAX];
+  for (int k = 0; k < n; ++k) {
+    const qlora_nf4* t = q[k];
+    items[k] = qlora::QuantItem{W[k], numel[k], t->codes, t->absmax8, t->scale2, t->mean,
+                                t->no_dq ? t->absmax32 : nullptr, static_cast<char*>(ws) + batch_ws_offset(k, numel)};
+  }
+  (void)hipGetLastError();  // drop an error left by an earlier, unrelated runtime call
+  const hipError_t e =
+      qlora::launch_quantize_batch(items, n, in_dtype == QLORA_BF16, tables(q[first]->qtype).th, stream);
+  return e == hipSuccess ? QLORA_OK : hip_fail(e);
+}
+
 int qlora_dequantize(const qlora_nf4* q, uint16_t* out, hipStream_t stream) {
   if (!q) return QLORA_ERR_ARG;
   if (q->rows < 0 || q->cols < 0) return QLORA_ERR_SHAPE;

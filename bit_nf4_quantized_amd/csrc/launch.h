@@ -68,6 +68,25 @@ hipError_t launch_quantize(const void* w, bool bf16_in, int64_t numel, const NF4
                            uint8_t* codes, uint8_t* absmax8, float* scale2, float* mean, float* absmax32,
                            void* ws, hipStream_t stream);
 
+// Several tensors in one pass: one launch of the block kernel over all their
+// DQ groups, one fold launch (a workgroup per tensor), one E4M3 launch.
+// Every tensor's arithmetic is that of launch_quantize on it alone.
+// absmax32 != null: that tensor keeps fp32 block constants (no DQ passes).
+// ws: the tensor's own scratch, quant_workspace_layout(numel).total bytes.
+constexpr int kQuantBatchMax = 16;
+struct QuantItem {
+  const void* w;
+  int64_t numel;
+  uint8_t* codes;
+  uint8_t* absmax8;
+  float* scale2;
+  float* mean;
+  float* absmax32;
+  void* ws;
+};
+hipError_t launch_quantize_batch(const QuantItem* items, int n, bool bf16_in, const NF4Thresholds& th,
+                                 hipStream_t stream);
+
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* absmax8, const float* scale2,
                              const float* mean, const float* absmax32, const NF4Table& tab, int64_t numel,
                              uint16_t* out, hipStream_t stream);

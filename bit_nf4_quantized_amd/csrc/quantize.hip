@@ -106,11 +106,11 @@ __device__ __forceinline__ int lut_bucket(float x) {
 // checks around the loads made the compiler wait for them where the
 // branches join, one memory round trip per load).
 template <typename InT, bool FULL>
-__device__ __forceinline__ void quant_group(const InT* __restrict__ w, int64_t numel, int64_t nb,
+__device__ __forceinline__ void quant_group(const InT* __restrict__ w, int64_t numel, int64_t nb, int64_t g,
                                             const NF4Thresholds& th, uint8_t* __restrict__ codes,
                                             float* __restrict__ absmax, float* s_a, u32x2_t* s_lut) {
   const int t = threadIdx.x;
-  const int64_t gbase = (int64_t)blockIdx.x * kGroupWeights;
+  const int64_t gbase = g * kGroupWeights;
   float tt[15];
 #pragma unroll
   for (int j = 0; j < 15; ++j) tt[j] = th.t[j];
@@ -188,19 +188,57 @@ __device__ __forceinline__ void quant_group(const InT* __restrict__ w, int64_t n
   }
 }
 
+// The tensors of one launch: workgroup x quantises group x - gb[i] of
+// tensor i, where gb[i] <= x < gb[i + 1] (gb = prefix sums of the group
+// counts). Passed by value; indexed only with workgroup-uniform values.
+struct QuantBatchArgs {
+  int n;
+  int64_t gb[kQuantBatchMax + 1];
+  const void* w[kQuantBatchMax];
+  int64_t numel[kQuantBatchMax];
+  uint8_t* codes[kQuantBatchMax];
+  float* absmax[kQuantBatchMax];
+  double* gsum[kQuantBatchMax];
+};
+
+// DQ passes of the tensors that have them: sums of tensor i in sum_a[i]
+// (sum_b[i] the fold's second buffer), its block absmax values in absmax[i].
+struct DqBatchArgs {
+  int n;
+  int64_t gb[kQuantBatchMax + 1];
+  const float* absmax[kQuantBatchMax];
+  int64_t nb[kQuantBatchMax];
+  double* sum_a[kQuantBatchMax];
+  double* sum_b[kQuantBatchMax];
+  float* mean[kQuantBatchMax];
+  uint8_t* absmax8[kQuantBatchMax];
+  float* scale2[kQuantBatchMax];
+};
+
+// The tensor that holds workgroup x (uniform: a scan over the prefix sums).
+__device__ __forceinline__ int batch_item(const int64_t* gb, int n, int64_t x) {
+  int i = 0;
+  while (i + 1 < n && gb[i + 1] <= x) ++i;
+  return __builtin_amdgcn_readfirstlane(i);
+}
+
 template <typename InT>
-__global__ __launch_bounds__(kQuantThreads) void quant_blocks_kernel(
-    const InT* __restrict__ w, int64_t numel, int64_t nb, NF4Thresholds th,
-    uint8_t* __restrict__ codes, float* __restrict__ absmax, double* __restrict__ gsum) {
+__global__ __launch_bounds__(kQuantThreads) void quant_blocks_kernel(QuantBatchArgs B, NF4Thresholds th) {
   __shared__ float s_a[kDqBlock];
   __shared__ double s_t[2][kDqBlock];
   __shared__ u32x2_t s_lut[kLutBuckets];  // (count of thresholds in lower buckets, the bucket's threshold bits)
   const int t = threadIdx.x;
-  const int64_t g = blockIdx.x;
+  const int i = batch_item(B.gb, B.n, blockIdx.x);
+  const int64_t g = (int64_t)blockIdx.x - B.gb[i];
+  const InT* __restrict__ w = static_cast<const InT*>(B.w[i]);
+  const int64_t numel = B.numel[i];
+  const int64_t nb = (numel + kBlock - 1) / kBlock;
+  uint8_t* __restrict__ codes = B.codes[i];
+  float* __restrict__ absmax = B.absmax[i];
   if ((g + 1) * kGroupWeights <= numel)   // uniform per workgroup
-    quant_group<InT, true>(w, numel, nb, th, codes, absmax, s_a, s_lut);
+    quant_group<InT, true>(w, numel, nb, g, th, codes, absmax, s_a, s_lut);
   else
-    quant_group<InT, false>(w, numel, nb, th, codes, absmax, s_a, s_lut);
+    quant_group<InT, false>(w, numel, nb, g, th, codes, absmax, s_a, s_lut);
   __syncthreads();
   // float64 adjacent-pair tree over the group's valid block constants
   int n = (int)((nb - g * kDqBlock) < kDqBlock ? (nb - g * kDqBlock) : kDqBlock);
@@ -215,7 +253,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_blocks_kernel(
     src ^= 1;
     n = (n + 1) >> 1;
   }
-  if (t == 0) gsum[g] = s_t[src][0];
+  if (t == 0) B.gsum[i][g] = s_t[src][0];
 }
 
 // Folds buf[0..n) with the adjacent-pair rule, level by level, in place
@@ -227,11 +265,16 @@ __global__ __launch_bounds__(kQuantThreads) void quant_blocks_kernel(
 // tree, and the last, partial run ends the array at every level, so its
 // carries are the tree's own), the remaining levels in LDS. Larger n fold
 // level by level in the two global buffers.
-__global__ __launch_bounds__(1024) void tree_fold_kernel(double* __restrict__ a, double* __restrict__ b,
-                                                         int64_t n, int64_t nb, float* __restrict__ mean) {
+__global__ __launch_bounds__(1024) void tree_fold_kernel(DqBatchArgs D) {
   constexpr int kRun = 32;
   __shared__ double s_fold[2][1024];
   const int t = threadIdx.x;
+  const int item = __builtin_amdgcn_readfirstlane((int)blockIdx.x);
+  double* __restrict__ a = D.sum_a[item];
+  double* __restrict__ b = D.sum_b[item];
+  const int64_t nb = D.nb[item];
+  int64_t n = D.gb[item + 1] - D.gb[item];       // the tensor's group count
+  float* __restrict__ mean = D.mean[item];
   if (n <= (int64_t)kRun * 1024) {
     const int nruns = (int)((n + kRun - 1) / kRun);
     if (t < nruns) {
@@ -279,14 +322,17 @@ __global__ __launch_bounds__(1024) void tree_fold_kernel(double* __restrict__ a,
   }
 }
 
-__global__ __launch_bounds__(kDqBlock) void dq_encode_kernel(const float* __restrict__ absmax, int64_t nb,
-                                                             const float* __restrict__ mean,
-                                                             uint8_t* __restrict__ absmax8,
-                                                             float* __restrict__ scale2) {
+__global__ __launch_bounds__(kDqBlock) void dq_encode_kernel(DqBatchArgs D) {
   __shared__ float s_max[kDqBlock / 64];
   const int t = threadIdx.x;
-  const int64_t b = (int64_t)blockIdx.x * kDqBlock + t;
-  const float mu = mean[0];
+  const int item = batch_item(D.gb, D.n, blockIdx.x);
+  const int64_t grp = (int64_t)blockIdx.x - D.gb[item];
+  const float* __restrict__ absmax = D.absmax[item];
+  const int64_t nb = D.nb[item];
+  uint8_t* __restrict__ absmax8 = D.absmax8[item];
+  float* __restrict__ scale2 = D.scale2[item];
+  const int64_t b = grp * kDqBlock + t;
+  const float mu = D.mean[item][0];
   const float d = (b < nb) ? absmax[b] - mu : 0.0f;  // RN32(a - mu)
   float m = wave_max(__builtin_fabsf(d), 64);
   if ((t & 63) == 0) s_max[t >> 6] = m;
@@ -301,7 +347,7 @@ __global__ __launch_bounds__(kDqBlock) void dq_encode_kernel(const float* __rest
     if (sigma != 0.0f) c = f32_to_e4m3(d / sigma);     // RN32(d / sigma), then E4M3
     absmax8[b] = (uint8_t)c;
   }
-  if (t == 0) scale2[blockIdx.x] = sigma;
+  if (t == 0) scale2[grp] = sigma;
 }
 
 // Units of 8 weights (one code dword in, one 16-byte bf16 store out). A
@@ -359,31 +405,63 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 
 }  // namespace
 
+hipError_t launch_quantize_batch(const QuantItem* items, int n, bool bf16_in, const NF4Thresholds& th,
+                                 hipStream_t stream) {
+  if (n < 1 || n > kQuantBatchMax) return hipErrorInvalidValue;
+  QuantBatchArgs B{};
+  DqBatchArgs D{};
+  int64_t groups = 0, dq_groups = 0;
+  for (int k = 0; k < n; ++k) {
+    const QuantItem& it = items[k];
+    if (it.numel == 0) continue;
+    const int64_t nb = (it.numel + kBlock - 1) / kBlock;
+    const int64_t ng = (nb + kDqBlock - 1) / kDqBlock;
+    const QuantWorkspace L = quant_workspace_layout(it.numel);
+    char* base = static_cast<char*>(it.ws);
+    float* absmax = it.absmax32 ? it.absmax32 : reinterpret_cast<float*>(base + L.absmax_off);
+    double* sum_a = reinterpret_cast<double*>(base + L.sum_a_off);
+    B.gb[B.n] = groups;
+    B.w[B.n] = it.w;
+    B.numel[B.n] = it.numel;
+    B.codes[B.n] = it.codes;
+    B.absmax[B.n] = absmax;
+    B.gsum[B.n] = sum_a;
+    ++B.n;
+    groups += ng;
+    if (!it.absmax32) {   // double quantisation: the fold and the E4M3 pass
+      D.gb[D.n] = dq_groups;
+      D.absmax[D.n] = absmax;
+      D.nb[D.n] = nb;
+      D.sum_a[D.n] = sum_a;
+      D.sum_b[D.n] = reinterpret_cast<double*>(base + L.sum_b_off);
+      D.mean[D.n] = it.mean;
+      D.absmax8[D.n] = it.absmax8;
+      D.scale2[D.n] = it.scale2;
+      ++D.n;
+      dq_groups += ng;
+    }
+  }
+  B.gb[B.n] = groups;
+  D.gb[D.n] = dq_groups;
+  if (groups == 0) return hipSuccess;
+  hipError_t e = timed(kTimeQuant, stream, [&] {
+    if (bf16_in)
+      hipLaunchKernelGGL(quant_blocks_kernel<uint16_t>, dim3((unsigned)groups), dim3(kQuantThreads), 0, stream, B, th);
+    else
+      hipLaunchKernelGGL(quant_blocks_kernel<float>, dim3((unsigned)groups), dim3(kQuantThreads), 0, stream, B, th);
+    return hipGetLastError();
+  });
+  if (e != hipSuccess || D.n == 0) return e;
+  hipLaunchKernelGGL(tree_fold_kernel, dim3((unsigned)D.n), dim3(1024), 0, stream, D);
+  hipLaunchKernelGGL(dq_encode_kernel, dim3((unsigned)dq_groups), dim3(kDqBlock), 0, stream, D);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize(const void* w, bool bf16_in, int64_t numel, const NF4Thresholds& th,
                            uint8_t* codes, uint8_t* absmax8, float* scale2, float* mean, float* absmax32,
                            void* ws, hipStream_t stream) {
-  const int64_t nb = (numel + kBlock - 1) / kBlock;
-  const int64_t ng = (nb + kDqBlock - 1) / kDqBlock;
-  QuantWorkspace L = quant_workspace_layout(numel);
-  char* base = static_cast<char*>(ws);
-  float* absmax = absmax32 ? absmax32 : reinterpret_cast<float*>(base + L.absmax_off);
-  double* sum_a = reinterpret_cast<double*>(base + L.sum_a_off);
-  double* sum_b = reinterpret_cast<double*>(base + L.sum_b_off);
-  hipError_t e = timed(kTimeQuant, stream, [&] {
-    if (bf16_in)
-      hipLaunchKernelGGL(quant_blocks_kernel<uint16_t>, dim3((unsigned)ng), dim3(kQuantThreads), 0, stream,
-                         static_cast<const uint16_t*>(w), numel, nb, th, codes, absmax, sum_a);
-    else
-      hipLaunchKernelGGL(quant_blocks_kernel<float>, dim3((unsigned)ng), dim3(kQuantThreads), 0, stream,
-                         static_cast<const float*>(w), numel, nb, th, codes, absmax, sum_a);
-    return hipGetLastError();
-  });
-  if (e != hipSuccess) return e;
-  if (absmax32) return hipSuccess;  // no double quantisation: the fp32 absmax is the stored constant
-  hipLaunchKernelGGL(tree_fold_kernel, dim3(1), dim3(1024), 0, stream, sum_a, sum_b, ng, nb, mean);
-  hipLaunchKernelGGL(dq_encode_kernel, dim3((unsigned)ng), dim3(kDqBlock), 0, stream, absmax, nb, mean,
-                     absmax8, scale2);
-  return hipGetLastError();
+  const QuantItem it{w, numel, codes, absmax8, scale2, mean, absmax32, ws};
+  return launch_quantize_batch(&it, 1, bf16_in, th, stream);
 }
 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* absmax8, const float* scale2,

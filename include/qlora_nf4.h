@@ -183,6 +183,35 @@ int qlora_quantize(const void *W, qlora_dtype in_dtype, const qlora_nf4 *q, void
                    size_t ws_bytes, hipStream_t stream);
 
 /*
+ * qlora_quantize_batch: qlora_quantize applied to n tensors (1 <= n <=
+ * QLORA_QUANT_BATCH_MAX) in one pass, e.g. the seven linears of a
+ * transformer layer (gptget.net abstract and diycv.top, section 方法总览
+ * items 1-3: every frozen linear of the model is stored in NF4 + DQ). Each
+ * tensor is quantised exactly as by qlora_quantize on it alone (the same
+ * codes and constants, bit for bit); the tensors share the launches: one
+ * over all their 64-blocks, one fold of the per-tensor means, one 8-bit
+ * float pass.
+ *   W       host array of n device pointers, all fp32 or all bf16 (in_dtype).
+ *   q       host array of n structs, as for qlora_quantize (each with its
+ *           own rows, cols, output buffers and no_dq flag); all non-empty
+ *           ones with the same qtype. Empty tensors are skipped.
+ *   ws      device scratch of at least qlora_quant_batch_workspace bytes.
+ * Errors: QLORA_ERR_ARG (n out of range, null pointers, mixed qtypes, bad
+ * dtype), QLORA_ERR_SHAPE, QLORA_ERR_ALIGN, QLORA_ERR_WORKSPACE, all before
+ * anything is enqueued; QLORA_ERR_HIP.
+ */
+#define QLORA_QUANT_BATCH_MAX 16
+int qlora_quantize_batch(int n, const void *const *W, qlora_dtype in_dtype, const qlora_nf4 *const *q,
+                         void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * qlora_quant_batch_workspace: scratch bytes of qlora_quantize_batch for n
+ * tensors of rows[k] x cols[k] (host only; the sum of the single-tensor
+ * scratch sizes, each rounded up to 256 bytes).
+ */
+int qlora_quant_batch_workspace(int n, const int64_t *rows, const int64_t *cols, size_t *bytes);
+
+/*
  * qlora_dequantize: doubleDequant to bf16 (diycv.top, section 关键公式):
  *   a'_b = RN32(RN32(e4m3(absmax8_b) * scale2_g) + mean)   (absmax32_b when no_dq)
  *   out_e = bf16_RNE(RN32(q[code_e] * a'_b)), q = the table of q->qtype

@@ -38,7 +38,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 24, names
+    assert len(names) == 26, names
     assert sorted(api.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -143,6 +143,42 @@ def test_quantize_validation(lib):
     nodq.absmax32 = 0x10400000
     assert lib.qlora_quantize(ok_ptr, 0, ctypes.byref(nodq), ws, big, None) == api.QLORA_ERR_ARG
     assert lib.qlora_dequantize(ctypes.byref(nodq), ctypes.c_void_p(0x20000000), None) == api.QLORA_ERR_ARG
+
+
+def test_quantize_batch_validation(lib):
+    """qlora_quantize_batch checks every tensor as qlora_quantize does, and
+    the batch rules, before anything is enqueued (no GPU needed)."""
+    P = ctypes.POINTER(api.QNF4)
+    a, b = fake_nf4(64, 64), fake_nf4(128, 64, base=0x11000000)
+    W = (ctypes.c_void_p * 2)(0x20000000, 0x21000000)
+    qs = (P * 2)(ctypes.pointer(a), ctypes.pointer(b))
+    ws = ctypes.c_void_p(0x30000000)
+    big = 1 << 30
+    need = api.qlora_quant_batch_workspace([(64, 64), (128, 64)])
+    assert need >= api.qlora_quant_sizes(64, 64)["workspace"] + api.qlora_quant_sizes(128, 64)["workspace"]
+    assert lib.qlora_quantize_batch(0, W, 0, qs, ws, big, None) == api.QLORA_ERR_ARG        # n < 1
+    assert lib.qlora_quantize_batch(17, W, 0, qs, ws, big, None) == api.QLORA_ERR_ARG       # n > 16
+    assert lib.qlora_quantize_batch(2, None, 0, qs, ws, big, None) == api.QLORA_ERR_ARG
+    assert lib.qlora_quantize_batch(2, W, 2, qs, ws, big, None) == api.QLORA_ERR_ARG        # dtype
+    assert lib.qlora_quantize_batch(2, W, 0, qs, None, big, None) == api.QLORA_ERR_ARG
+    assert lib.qlora_quantize_batch(2, W, 0, qs, ws, need - 1, None) == api.QLORA_ERR_WORKSPACE
+    mixed = fake_nf4(128, 64, base=0x11000000)
+    mixed.qtype = 1                                   # another threshold table in the same pass
+    assert lib.qlora_quantize_batch(2, W, 0, (P * 2)(ctypes.pointer(a), ctypes.pointer(mixed)), ws, big,
+                                    None) == api.QLORA_ERR_ARG
+    Wmis = (ctypes.c_void_p * 2)(0x20000000, 0x21000004)
+    assert lib.qlora_quantize_batch(2, Wmis, 0, qs, ws, big, None) == api.QLORA_ERR_ALIGN
+    neg = fake_nf4(-1, 4)
+    assert lib.qlora_quantize_batch(2, W, 0, (P * 2)(ctypes.pointer(a), ctypes.pointer(neg)), ws, big,
+                                    None) == api.QLORA_ERR_SHAPE
+    e0, e1 = fake_nf4(0, 17), fake_nf4(5, 0)
+    assert lib.qlora_quantize_batch(2, (ctypes.c_void_p * 2)(None, None), 0,
+                                    (P * 2)(ctypes.pointer(e0), ctypes.pointer(e1)), None, 0, None) == api.QLORA_OK
+    rows = (ctypes.c_int64 * 1)(-1)
+    cols = (ctypes.c_int64 * 1)(4)
+    out = ctypes.c_size_t()
+    assert lib.qlora_quant_batch_workspace(1, rows, cols, ctypes.byref(out)) == api.QLORA_ERR_SHAPE
+    assert lib.qlora_quant_batch_workspace(0, rows, cols, ctypes.byref(out)) == api.QLORA_ERR_ARG
 
 
 def test_dequantize_validation(lib):

@@ -122,3 +122,71 @@ def test_llama65b_22016_wide(api, index, bf16):
     say(f"quantize llama65b {shp.name} {shp.N}x{shp.K} ({'bf16' if bf16 else 'fp32'})")
     W = workloads.quantize_weight(shp, 4, index)
     check_roundtrip(api, workloads.to_bf16_bits(W) if bf16 else W, bf16=bf16)
+
+
+def batch_host(q):
+    """Host copies of one batch output (codes and block constants)."""
+    from gpu_util import nf4_host
+
+    return nf4_host(q)
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["fp32", "bf16"])
+def test_batch_mixed_shapes(api, bf16):
+    """qlora_quantize_batch over ragged, tiny, empty and group-spanning
+    tensors in one pass (one with fp32 block constants, no DQ): every tensor
+    bit-exact with the oracle, as if quantised alone."""
+    import torch
+
+    shapes = [(1, 63), (5, 64 * 256 // 5 + 7), (0, 17), (257, 64), (33, 4097), (100, 100), (64, 16384 + 9),
+              (3, 21)]
+    say(f"quantize batch of {len(shapes)} ({'bf16' if bf16 else 'fp32'})")
+    rng = np.random.default_rng(4242 + bf16)
+    hostW, devW = [], []
+    for rows, cols in shapes:
+        W = workloads.random_weight(rng, rows * cols, "student-t4").reshape(rows, cols)
+        if bf16:
+            W = workloads.to_bf16_bits(W)
+            devW.append(api.to_device_bf16(W))
+        else:
+            devW.append(torch.from_numpy(np.ascontiguousarray(W)).cuda())
+        hostW.append(nf4.bf16_bits_to_f32(W) if bf16 else W)
+    nodq = 5                                           # the 100 x 100 tensor keeps fp32 constants
+    outs = [api.NF4Tensor.empty(r, c, "cuda", "nf4", k != nodq) for k, (r, c) in enumerate(shapes)]
+    api.qlora_quantize_batch(devW, outs=outs)
+    torch.cuda.synchronize()
+    for k, (W, q) in enumerate(zip(hostW, outs)):
+        if W.size == 0:
+            continue
+        got = batch_host(q)
+        if k == nodq:
+            ref = nf4.quantize(W, double_quant=False)
+            np.testing.assert_array_equal(got["codes"], ref["codes"])
+            np.testing.assert_array_equal(got["absmax32"].view(np.uint32), ref["absmax32"].view(np.uint32))
+        else:
+            assert_quant_equal(got, nf4.quantize(W))
+
+
+def test_batch_llama65b_layer_equals_single_calls(api):
+    """The seven LLaMA-65B linears of one layer (809.5M weights) in one batch,
+    from fp32 and from bf16: every output equal, byte for byte, to the
+    single-tensor call (itself bit-exact with the oracle on these shapes,
+    test_llama65b_22016_wide and test_llama65b_shape_bf16)."""
+    import torch
+
+    Ws = [torch.from_numpy(workloads.quantize_weight(shp, 4, i)).cuda() for i, shp in enumerate(workloads.LLAMA65B)]
+    for bf16 in (False, True):
+        say(f"quantize batch llama65b layer ({'bf16' if bf16 else 'fp32'})")
+        src = [W.to(torch.bfloat16) for W in Ws] if bf16 else Ws
+        outs = api.qlora_quantize_batch(src)
+        for W, qb in zip(src, outs):
+            qs = api.qlora_quantize(W)
+            torch.cuda.synchronize()
+            numel = W.numel()
+            nb = -(-numel // 64)
+            ng = -(-nb // 256)
+            assert torch.equal(qb.codes[: numel // 2], qs.codes[: numel // 2])
+            assert torch.equal(qb.absmax8[:nb], qs.absmax8[:nb])
+            assert torch.equal(qb.scale2[:ng].view(torch.int32), qs.scale2[:ng].view(torch.int32))
+            assert torch.equal(qb.mean.view(torch.int32), qs.mean.view(torch.int32))
+        del outs
