@@ -18,7 +18,7 @@
 //                         same adjacent-pair rule (first levels in
 //                         registers, the rest in LDS) and writes the fp32
 //                         mean.
-//   dq_encode_kernel      one workgroup per group: a - mean, group absmax,
+//   dq_encode_kernel      one wave per group: a - mean, group absmax,
 //                         fp32 scale, E4M3 codes.
 //   dequant_kernel        4 units of 8 weights per thread: a code dword + the
 //                         E4M3 constant -> bf16, one 16-byte store per unit.
@@ -322,32 +322,66 @@ __global__ __launch_bounds__(1024) void tree_fold_kernel(DqBatchArgs D) {
   }
 }
 
-__global__ __launch_bounds__(kDqBlock) void dq_encode_kernel(DqBatchArgs D) {
-  __shared__ float s_max[kDqBlock / 64];
-  const int t = threadIdx.x;
-  const int item = batch_item(D.gb, D.n, blockIdx.x);
-  const int64_t grp = (int64_t)blockIdx.x - D.gb[item];
-  const float* __restrict__ absmax = D.absmax[item];
-  const int64_t nb = D.nb[item];
-  uint8_t* __restrict__ absmax8 = D.absmax8[item];
-  float* __restrict__ scale2 = D.scale2[item];
-  const int64_t b = grp * kDqBlock + t;
-  const float mu = D.mean[item][0];
-  const float d = (b < nb) ? absmax[b] - mu : 0.0f;  // RN32(a - mu)
-  float m = wave_max(__builtin_fabsf(d), 64);
-  if ((t & 63) == 0) s_max[t >> 6] = m;
-  __syncthreads();
-  float A = s_max[0];
+// The E4M3 pass: one wave per DQ group of 256 block constants. Lane l holds
+// blocks 4l .. 4l+3 of its group (one 16-byte load, one 4-byte store of the
+// codes), so the group absmax is one cross-lane max: no LDS, no barrier.
+// Each wave takes kDqGroupsPerWave consecutive groups of the batch's group
+// space, all their loads issued first. Per block: d = RN32(a - mean); per
+// group: sigma = RN32(max|d| / 448) (0 below 2^-126); code = E4M3 of
+// RN32(d / sigma).
+constexpr int kDqWaves = 4;
+constexpr int kDqGroupsPerWave = 2;
+__global__ __launch_bounds__(64 * kDqWaves) void dq_encode_kernel(DqBatchArgs D, int64_t total_groups) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t g0 = ((int64_t)blockIdx.x * kDqWaves + wave) * kDqGroupsPerWave;
+  f32x4_t v[kDqGroupsPerWave];
+  int item[kDqGroupsPerWave];
+  int64_t grp[kDqGroupsPerWave];
 #pragma unroll
-  for (int i = 1; i < kDqBlock / 64; ++i) A = __builtin_fmaxf(A, s_max[i]);
-  float sigma = A / 448.0f;                            // RN32(A / 448)
-  if (!(sigma >= 0x1p-126f)) sigma = 0.0f;
-  if (b < nb) {
-    uint32_t c = 0;
-    if (sigma != 0.0f) c = f32_to_e4m3(d / sigma);     // RN32(d / sigma), then E4M3
-    absmax8[b] = (uint8_t)c;
+  for (int q = 0; q < kDqGroupsPerWave; ++q) {
+    const int64_t gg = g0 + q < total_groups ? g0 + q : total_groups - 1;   // clamped: loads stay unconditional
+    item[q] = batch_item(D.gb, D.n, gg);
+    grp[q] = gg - D.gb[item[q]];
+    const int64_t nb = D.nb[item[q]];
+    const int64_t b0 = grp[q] * kDqBlock + 4 * lane;
+    const int64_t bl = b0 < nb ? b0 : ((nb - 1) & ~(int64_t)3);   // an aligned quad inside the padded array
+    v[q] = *reinterpret_cast<const f32x4_t*>(D.absmax[item[q]] + bl);
   }
-  if (t == 0) scale2[grp] = sigma;
+#pragma unroll
+  for (int q = 0; q < kDqGroupsPerWave; ++q) {
+    const int it = item[q];
+    const int64_t nb = D.nb[it];
+    const int64_t b0 = grp[q] * kDqBlock + 4 * lane;
+    const float mu = D.mean[it][0];
+    const float a[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+    float d[4];
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      d[e] = (b0 + e < nb) ? a[e] - mu : 0.0f;         // RN32(a - mu)
+      m = __builtin_fmaxf(m, __builtin_fabsf(d[e]));
+    }
+    const float A = wave_max(m, 64);
+    float sigma = A / 448.0f;                            // RN32(A / 448)
+    if (!(sigma >= 0x1p-126f)) sigma = 0.0f;
+    uint32_t packed = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t c = sigma != 0.0f ? f32_to_e4m3(d[e] / sigma) : 0u;   // RN32(d / sigma), then E4M3
+      packed |= c << (8 * e);
+    }
+    if (g0 + q >= total_groups) continue;                // a clamped duplicate: nothing stored
+    uint8_t* a8 = D.absmax8[it] + b0;
+    if (b0 + 3 < nb && ((uintptr_t)D.absmax8[it] & 3u) == 0) {
+      *reinterpret_cast<uint32_t*>(a8) = packed;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (b0 + e < nb) a8[e] = (uint8_t)(packed >> (8 * e));
+    }
+    if (lane == 0) D.scale2[it][grp[q]] = sigma;
+  }
 }
 
 // Units of 8 weights (one code dword in, one 16-byte bf16 store out). A
@@ -453,7 +487,9 @@ hipError_t launch_quantize_batch(const QuantItem* items, int n, bool bf16_in, co
   });
   if (e != hipSuccess || D.n == 0) return e;
   hipLaunchKernelGGL(tree_fold_kernel, dim3((unsigned)D.n), dim3(1024), 0, stream, D);
-  hipLaunchKernelGGL(dq_encode_kernel, dim3((unsigned)dq_groups), dim3(kDqBlock), 0, stream, D);
+  const int64_t per_wg = (int64_t)kDqWaves * kDqGroupsPerWave;
+  hipLaunchKernelGGL(dq_encode_kernel, dim3((unsigned)((dq_groups + per_wg - 1) / per_wg)), dim3(64 * kDqWaves), 0,
+                     stream, D, dq_groups);
   return hipGetLastError();
 }
 
