@@ -190,3 +190,31 @@ def test_batch_llama65b_layer_equals_single_calls(api):
             assert torch.equal(qb.scale2[:ng].view(torch.int32), qs.scale2[:ng].view(torch.int32))
             assert torch.equal(qb.mean.view(torch.int32), qs.mean.view(torch.int32))
         del outs
+
+
+@pytest.mark.parametrize("qtype", ["int4", "fp4_e2m1", "fp4_e3m0"])
+def test_batch_other_types_equal_single_calls(api, qtype):
+    """A batch of another 4-bit type (one threshold table per launch), with
+    and without DQ: byte-equal to qlora_quantize on each tensor alone (which
+    test_gpu_qtypes.py pins to the oracle bit for bit)."""
+    import torch
+
+    say(f"quantize batch {qtype}")
+    rng = np.random.default_rng(5151)
+    shapes = [(300, 700), (64, 16384 + 64), (7, 64 * 256 + 3)]
+    Ws = [torch.from_numpy(workloads.random_weight(rng, r * c, "student-t4").reshape(r, c)).cuda() for r, c in shapes]
+    for dq in (True, False):
+        outs = api.qlora_quantize_batch(Ws, qtype=qtype, double_quant=dq)
+        for W, qb in zip(Ws, outs):
+            qs = api.qlora_quantize(W, qtype=qtype, double_quant=dq)
+            torch.cuda.synchronize()
+            numel = W.numel()
+            nb = -(-numel // 64)
+            assert torch.equal(qb.codes[: (numel + 1) // 2], qs.codes[: (numel + 1) // 2])
+            if dq:
+                ng = -(-nb // 256)
+                assert torch.equal(qb.absmax8[:nb], qs.absmax8[:nb])
+                assert torch.equal(qb.scale2[:ng].view(torch.int32), qs.scale2[:ng].view(torch.int32))
+                assert torch.equal(qb.mean.view(torch.int32), qs.mean.view(torch.int32))
+            else:
+                assert torch.equal(qb.absmax32[:nb].view(torch.int32), qs.absmax32[:nb].view(torch.int32))
