@@ -265,6 +265,9 @@ int qlora_quantize_batch(int n, const void* const* W, qlora_dtype in_dtype, cons
     if (!aligned16(W[k]) || !aligned16(q[k]->codes)) return QLORA_ERR_ALIGN;
   }
   if (first < 0) return QLORA_OK;                // nothing to quantise
+  int64_t groups = 0;                            // one workgroup per DQ group of the whole batch
+  for (int k = 0; k < n; ++k) groups += (numel[k] + QLORA_BLOCK * QLORA_DQ_BLOCK - 1) / (QLORA_BLOCK * QLORA_DQ_BLOCK);
+  if (groups > 0x7FFFFFFF) return QLORA_ERR_SHAPE;
   if (!ws) return QLORA_ERR_ARG;
   if (!aligned16(ws)) return QLORA_ERR_ALIGN;
   if (ws_bytes < batch_ws_offset(n, numel)) return QLORA_ERR_WORKSPACE;

@@ -197,8 +197,9 @@ int qlora_quantize(const void *W, qlora_dtype in_dtype, const qlora_nf4 *q, void
  *           ones with the same qtype. Empty tensors are skipped.
  *   ws      device scratch of at least qlora_quant_batch_workspace bytes.
  * Errors: QLORA_ERR_ARG (n out of range, null pointers, mixed qtypes, bad
- * dtype), QLORA_ERR_SHAPE, QLORA_ERR_ALIGN, QLORA_ERR_WORKSPACE, all before
- * anything is enqueued; QLORA_ERR_HIP.
+ * dtype), QLORA_ERR_SHAPE (a tensor as for qlora_quantize, or more than
+ * 2^31 - 1 groups of 16384 weights in the batch), QLORA_ERR_ALIGN,
+ * QLORA_ERR_WORKSPACE, all before anything is enqueued; QLORA_ERR_HIP.
  */
 #define QLORA_QUANT_BATCH_MAX 16
 int qlora_quantize_batch(int n, const void *const *W, qlora_dtype in_dtype, const qlora_nf4 *const *q,

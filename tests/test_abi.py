@@ -171,6 +171,9 @@ def test_quantize_batch_validation(lib):
     neg = fake_nf4(-1, 4)
     assert lib.qlora_quantize_batch(2, W, 0, (P * 2)(ctypes.pointer(a), ctypes.pointer(neg)), ws, big,
                                     None) == api.QLORA_ERR_SHAPE
+    huge = [fake_nf4(1 << 30, 1 << 14, base=0x10000000 + (k << 24)) for k in range(2)]   # 2^30 groups each, 2^31 together
+    assert lib.qlora_quantize_batch(2, W, 0, (P * 2)(*[ctypes.pointer(h) for h in huge]), ws, 1 << 62,
+                                    None) == api.QLORA_ERR_SHAPE
     e0, e1 = fake_nf4(0, 17), fake_nf4(5, 0)
     assert lib.qlora_quantize_batch(2, (ctypes.c_void_p * 2)(None, None), 0,
                                     (P * 2)(ctypes.pointer(e0), ctypes.pointer(e1)), None, 0, None) == api.QLORA_OK

@@ -218,3 +218,18 @@ def test_batch_other_types_equal_single_calls(api, qtype):
                 assert torch.equal(qb.mean.view(torch.int32), qs.mean.view(torch.int32))
             else:
                 assert torch.equal(qb.absmax32[:nb].view(torch.int32), qs.absmax32[:nb].view(torch.int32))
+
+
+def test_batch_of_sixteen(api):
+    """The largest batch, 16 tensors of assorted small shapes (one of them
+    one weight long), each bit-exact with the oracle."""
+    import torch
+
+    say("quantize batch of 16")
+    rng = np.random.default_rng(1616)
+    shapes = [(1 + int(rng.integers(0, 40)), 1 + int(rng.integers(0, 3000))) for _ in range(15)] + [(1, 1)]
+    hostW = [workloads.random_weight(rng, r * c).reshape(r, c) for r, c in shapes]
+    outs = api.qlora_quantize_batch([torch.from_numpy(W).cuda() for W in hostW])
+    torch.cuda.synchronize()
+    for W, q in zip(hostW, outs):
+        assert_quant_equal(batch_host(q), nf4.quantize(W))
