@@ -514,11 +514,15 @@ def qlora_quantize_batch(Ws, outs=None, workspace=None, stream=None, qtype: str 
     for W in Ws:
         if W.dim() != 2:
             raise ValueError("each W must be 2-D [rows][cols]")
+        if W.device != Ws[0].device:
+            raise ValueError("all tensors of a batch on one device")
         _need(W, W.dtype, tuple(W.shape), "W")
     qs = list(outs) if outs is not None else [NF4Tensor.empty(W.shape[0], W.shape[1], W.device, qtype, double_quant)
                                               for W in Ws]
     if len(qs) != n:
         raise ValueError("one output per tensor")
+    if any(q.codes.device != Ws[0].device for q in qs):
+        raise ValueError("outputs on the inputs' device")
     ws = _workspace(qlora_quant_batch_workspace([tuple(W.shape) for W in Ws]), Ws[0].device, workspace)
     structs = [q.struct() for q in qs]
     sp = (ctypes.POINTER(QNF4) * n)(*[ctypes.pointer(st) for st in structs])
