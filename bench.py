@@ -252,8 +252,10 @@ def kernel_summary(durs_ms, flops):
             "tflops": tot_f / (tot_ms * 1e-3) / 1e12 if tot_ms > 0 else None, "total_ms": tot_ms}
 
 
-def bench_gemv(api, workloads, reps=4):
-    """Decode-style forward, M in {1, 4, 16}, weights cycled over distinct copies."""
+def bench_gemv(api, workloads, reps=4, oracle=False):
+    """Decode-style forward, M in {1, 4, 16}, weights cycled over distinct copies.
+    With ``oracle``, the float64 oracle's dequant + forward of the same call
+    is timed on the host beside each GPU figure."""
     import torch
 
     out = []
@@ -315,6 +317,17 @@ def bench_gemv(api, workloads, reps=4):
                         "graph_call_us": graph_ms * 1e3, "graph_call_GBps": cbytes / (graph_ms * 1e-3) / 1e9,
                         "graph_call_frac_of_hbm_peak": cbytes / (graph_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                         "graph_result_equal": same, "weight_copies": copies})
+            if oracle:
+                from oracle import linear, nf4
+
+                qt = nf4.quantize(inp.W)                 # the frozen base: outside the timed call
+                t0 = time.perf_counter()
+                Wd = nf4.dequantize(qt, inp.W.shape)
+                linear.linear_fwd(inp.X[:M], Wd, inp.L1, inp.L2, inp.s)
+                dt = time.perf_counter() - t0
+                out[-1]["cpu_oracle"] = {"call_us": dt * 1e6, "GBps": cbytes / dt / 1e9, "kind": "oracle",
+                                         "sample": "one call: float64 NumPy dequant (single-threaded) + forward"}
+                log(f"gemv K={K} N={N} M={M}: oracle call {dt*1e3:.1f} ms")
             log(f"gemv K={K} N={N} M={M}: kernel {avg*1e3:.2f} us "
                 f"{out[-1]['kernel_GBps']:.0f} GB/s, call {call_ms*1e3:.2f} us, "
                 f"graph-replayed call {graph_ms*1e3:.2f} us ({out[-1]['graph_call_GBps']:.0f} GB/s, "
@@ -883,12 +896,16 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_extras:
         other = "llama7b-layer" if name == "llama33b-layer" else "llama33b-layer"
-        sec, l2, _, ws2 = setup_and_time(api, workloads, other, max(args.steps // 2, 5), 3, 1)
+        sec, l2, host2, ws2 = setup_and_time(api, workloads, other, max(args.steps // 2, 5), 3, 1)
         del l2, ws2
         torch.cuda.empty_cache()
         result[other.replace("-", "_") + "_step"] = {k: sec[k] for k in ("value", "ms_per_step", "roofline",
                                                                           "kernels", "config")}
-        result["gemv"] = bench_gemv(api, workloads)
+        if not args.no_cpu_baseline:   # the oracle on this step too (a context figure, like cpu_baseline)
+            result[other.replace("-", "_") + "_step"]["cpu_oracle"] = cpu_baseline(host2)
+            log(f"{other}: oracle step {result[other.replace('-', '_') + '_step']['cpu_oracle']['seconds']:.1f} s")
+        del host2
+        result["gemv"] = bench_gemv(api, workloads, oracle=not args.no_cpu_baseline)
         for g in result["gemv"]:
             g["graph_call_frac_of_attainable_read"] = g["graph_call_GBps"] / peaks["hbm_read_GBps"]
         result["quantize"] = bench_quantize(api, workloads)
